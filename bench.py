@@ -1,0 +1,249 @@
+"""Decode-step benchmark of the Locks path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rank R]
+
+One step = locks_score_select (page scoring, share-average combine, top-k
+selection) + locks_sparse_decode (split-K sparse attention + merge) over one
+batch of synthetic inputs already resident in HBM. The summary build of the
+pages that complete in a step is timed in the same run and reported beside it
+(it runs when a page completes, off the decode critical path), together with
+the one-off build of every page after prefill.
+
+Prints one JSON line. `roofline` describes the dominant kernel (the page
+scorer) with algorithmic bytes = summary records streamed per launch;
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "decode-step score+select+sparse-attn µs and % HBM roofline, 128K ctx, batch 8"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b_128k_b8")
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by (sequence, KV head) with no exchange, so N GPUs would run N "
+              "independent copies).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_kv_page_amd import locks as L
+    from sparse_kv_page_amd import synth
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    wl = synth.WORKLOADS[args.workload]
+    if args.rank is not None:
+        wl = wl.with_(rank=args.rank)
+    cfg = L.config_for(wl)
+    B, Hkv, Hq, d, P, r, k = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim,
+                              wl.page_size, wl.rank, wl.budget_pages)
+    print(f"[bench] generating {wl.name} (batch {B}, ctx {wl.seq_lens[0]}, r {r}) on the GPU",
+          file=sys.stderr, flush=True)
+    data = synth.generate(wl, args.seed, dev)
+    q, kp, vp, bt, sl = (data[x] for x in ("q", "k_pool", "v_pool", "block_table", "seq_lens"))
+    maxp = wl.max_pages
+    pool = L.summary_pool_for(cfg, wl.num_blocks, dev)
+    rec_bytes = L.locks_summary_record_bytes(cfg)
+
+    # ---- prefill build of every complete page (one-off) ----
+    full_ids = []
+    for b in range(B):
+        Jc = int(wl.seq_lens[b]) // P
+        full_ids.append(bt[b, :Jc])
+    full_ids = torch.cat(full_ids).contiguous()
+    n_full = full_ids.numel()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L.locks_build_summaries(cfg, kp, wl.num_blocks, full_ids, n_full, pool)  # warm
+    torch.cuda.synchronize()
+    e0.record()
+    L.locks_build_summaries(cfg, kp, wl.num_blocks, full_ids, n_full, pool)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_build_ms = e0.elapsed_time(e1)
+    print(f"[bench] prefill build of {n_full * Hkv} page tiles: {prefill_build_ms:.2f} ms",
+          file=sys.stderr, flush=True)
+
+    # pages completing in a decode step: the current page of every sequence whose
+    # length is a multiple of the page size
+    step_ids = torch.stack([bt[b, int(wl.seq_lens[b]) // P - 1] for b in range(B)
+                            if int(wl.seq_lens[b]) % P == 0]).to(torch.int32).contiguous()
+    n_step = step_ids.numel()
+
+    sel = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, d), dtype=synth.torch_dtype(wl.kv_dtype), device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws_bytes = L.locks_workspace_size(cfg, B, maxp)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    scores = torch.empty((B, Hq, maxp), dtype=torch.float32, device=dev)
+    sigma = torch.empty((B, Hkv, maxp), dtype=torch.float32, device=dev)
+
+    def step():
+        L.locks_score_select(cfg, q, pool, wl.num_blocks, bt, sl, B, maxp, sel, ws, ws_bytes)
+        L.locks_sparse_decode(cfg, q, kp, vp, wl.num_blocks, bt, sl, sel, B, maxp, out, lse, ws,
+                              ws_bytes)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ----
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    step_ms = t0.elapsed_time(t1) / args.steps
+
+    # ---- per-stage timing with events on the launch stream ----
+    names = ("build_step", "page_score", "select", "sparse_decode")
+    acc = {n: 0.0 for n in names}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for it in range(args.steps):
+        ev[0].record()
+        if n_step:
+            L.locks_build_summaries(cfg, kp, wl.num_blocks, step_ids, n_step, pool)
+        ev[1].record()
+        L.locks_page_score(cfg, q, pool, wl.num_blocks, bt, sl, B, maxp, scores)
+        ev[2].record()
+        L.locks_select_pages(cfg, scores, sl, B, maxp, sel, sigma)
+        ev[3].record()
+        L.locks_sparse_decode(cfg, q, kp, vp, wl.num_blocks, bt, sl, sel, B, maxp, out, lse, ws,
+                              ws_bytes)
+        ev[4].record()
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    stage_us = {n: 1e3 * acc[n] / args.steps for n in names}
+
+    # ---- algorithmic bytes (what the method must move per step) ----
+    summary_bytes = 0
+    kv_bytes = 0
+    ekv = 2 if wl.kv_dtype == "bf16" else 4
+    for b in range(B):
+        T = int(wl.seq_lens[b])
+        J, Jc = -(-T // P), T // P
+        summary_bytes += Hkv * Jc * rec_bytes
+        if J <= k:
+            A = T
+        else:
+            A = (k - 1) * P + (T - (J - 1) * P)
+        kv_bytes += Hkv * A * 2 * d * ekv
+    step_bytes = summary_bytes + kv_bytes
+    score_gbs = summary_bytes / (stage_us["page_score"] * 1e-6) / 1e9
+    step_gbs = step_bytes / (step_ms * 1e-3) / 1e9
+    gram_flops = 2.0 * P * d * d * n_full * Hkv
+    build_tflops = gram_flops / (prefill_build_ms * 1e-3) / 1e12
+
+    # ---- CPU oracle on a bounded sample of the same step ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, cfg, data, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(step_ms * 1e3, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "context_tokens": int(wl.seq_lens[0]),
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "page_size": P, "rank": r,
+                   "budget_tokens": k * P, "summary_dtype": wl.summary_dtype,
+                   "parallelism": "single-gpu"},
+        "hbm_roofline_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes": step_bytes,
+        "step_achieved_GBps": round(step_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": "page_score", "achieved": round(score_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": summary_bytes,
+                     "avg_launch_us": round(stage_us["page_score"], 3)},
+        "stages_us": {n: round(v, 3) for n, v in stage_us.items()},
+        "step_with_build_us": round(step_ms * 1e3 + stage_us["build_step"], 3),
+        "build": {"pages_per_step": int(n_step) * Hkv, "step_build_us": round(stage_us["build_step"], 3),
+                  "prefill_page_tiles": int(n_full) * Hkv, "prefill_ms": round(prefill_build_ms, 3),
+                  "gram_TFLOPs": round(build_tflops, 3),
+                  "gram_mfma_frac": round(build_tflops / BF16_MFMA_PEAK_TFLOPS, 5)},
+        "wall_s_timed": round(wall1 - wall0, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(wl, cfg, data, seconds):
+    """Oracle score -> combine -> select -> attend on the first sequences of the batch,
+    with synthetic summary records of the same shape; scaled to one full step."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_kv_page_amd import synth
+
+    nseq = min(2, wl.batch)
+    sub = wl.with_(batch=nseq, seq_lens=wl.seq_lens[:nseq])
+    bt = data["block_table"][:nseq].cpu()
+    used = torch.unique(bt.reshape(-1)).long()
+    remap = torch.full((wl.num_blocks,), -1, dtype=torch.long)
+    remap[used] = torch.arange(used.numel())
+    bt_local = remap[bt.long()].numpy()
+    to32 = lambda t: t.to("cpu", torch.float32).numpy()
+    kp = to32(data["k_pool"][used.to(data["k_pool"].device)])
+    vp = to32(data["v_pool"][used.to(data["v_pool"].device)])
+    # records indexed by the local block ids (one per (page, KV head) of the sample)
+    mu, vt, cf = synth.random_summaries(sub.with_(extra_blocks=0), seed=1, device="cpu")
+    assert mu.shape[0] == used.numel()
+    mu, vt, cf = (x.double().numpy() for x in (mu, vt, cf))
+    q = data["q"][:nseq].to("cpu", torch.float64).numpy()
+    threads = oracle.default_threads()
+    oracle.decode_step(q, mu, vt, cf, kp, vp, bt_local, list(sub.seq_lens), wl.page_size,
+                       wl.budget_pages, wl.softmax_scale, threads=threads)  # warm (loads lib)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_step(q, mu, vt, cf, kp, vp, bt_local, list(sub.seq_lens), wl.page_size,
+                           wl.budget_pages, wl.softmax_scale, threads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    per_rep = (time.perf_counter() - t0) / reps
+    per_step_us = per_rep * (wl.batch / nseq) * 1e6
+    return {"value": round(per_step_us, 1), "unit": "us", "cores": threads, "kind": "oracle",
+            "sample": f"{nseq} of {wl.batch} sequences x {wl.num_kv_heads} KV heads "
+                      f"(score+combine+select+attend, fp64), {reps} repeats, scaled x{wl.batch // nseq}"}
+
+
+if __name__ == "__main__":
+    main()

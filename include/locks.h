@@ -1,0 +1,165 @@
+/*
+ * locks.h - C ABI of the Locks decode-step library for AMD Instinct MI355X
+ * (gfx950): page-local rank-r key summaries, query-aware page selection and
+ * sparse paged decode attention.
+ *
+ * Method: "Locks: Page-Local Compact Key Summaries for Efficient Long-Context
+ * Decoding" (J. Hwang, arXiv 2607.24555), cited as [Locks].
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All array arguments are DEVICE pointers into memory the caller allocated
+ *   and owns (the library never allocates, frees or keeps device memory, and
+ *   holds no mutable global state). Arrays are dense, row-major, and must be
+ *   16-byte aligned; element types are given per argument.
+ * - Every call only validates its arguments on the host and enqueues kernels
+ *   on `stream` (a hipStream_t; NULL = the default stream). It never
+ *   synchronises and never reads device memory on the host, so it may be
+ *   captured into a HIP graph.
+ * - Return value: LOCKS_OK (0) or a negative status (see below). A non-OK
+ *   status means nothing was enqueued, except LOCKS_E_HIP, which reports a
+ *   launch failure from the HIP runtime.
+ * - Data-dependent checks are done on the device: a block id outside
+ *   [0, num_blocks) is skipped (its page scores -inf and is never selected;
+ *   in decode the slot contributes nothing), a negative sequence length counts
+ *   as 0 and a length above max_pages * page_size is clamped to it.
+ *
+ * Paged layouts (P = page_size, d = head_dim, r = rank, e = element bytes)
+ *   K pool, V pool   [num_blocks][num_kv_heads][P][d]     kv_dtype
+ *   block_table      [batch][max_pages] int32: physical block of logical page j
+ *   seq_lens         [batch] int32: tokens T in the cache (current token included)
+ *   summary pool     [num_blocks][num_kv_heads][record], one record per
+ *                    (block, KV head), summary_dtype elements:
+ *                        mu[d] | V^T[r][d] | C[P][r]
+ *                    record bytes = e * (d + r*d + P*r)
+ *   q                [batch][num_q_heads][d] kv_dtype; query head g belongs
+ *                    to KV head g / G, G = num_q_heads / num_kv_heads
+ *   selected         [batch][num_kv_heads][budget_pages] int32 logical page ids,
+ *                    ascending, padded with -1
+ * A sequence with T tokens has J = ceil(T/P) pages; the first floor(T/P) are
+ * complete. Page J-1 is the current page (partial when P does not divide T).
+ */
+#ifndef LOCKS_H
+#define LOCKS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  LOCKS_OK = 0,
+  LOCKS_E_INVALID_ARG = -1,  /* null pointer, negative size, k < 2, bad scale ... */
+  LOCKS_E_UNSUPPORTED = -2,  /* a shape or dtype this build has no kernel for   */
+  LOCKS_E_WORKSPACE = -3,    /* workspace pointer NULL or smaller than required */
+  LOCKS_E_HIP = -4           /* the HIP runtime reported a launch error          */
+};
+
+typedef enum { LOCKS_BF16 = 0, LOCKS_F32 = 1 } locks_dtype_t;
+
+typedef struct locks_config {
+  int32_t head_dim;      /* d: 64 or 128                                          */
+  int32_t page_size;     /* P: 16, 32 or 64 tokens per page                       */
+  int32_t rank;          /* r: 1 .. min(15, P - 1)                                */
+  int32_t num_q_heads;   /* H_q                                                   */
+  int32_t num_kv_heads;  /* H_kv >= 1; G = H_q / H_kv must be 1, 2, 4 or 8        */
+  int32_t budget_pages;  /* k = ceil(b / P) page slots per (sequence, KV head), >= 2 */
+  int32_t kv_dtype;      /* locks_dtype_t of q, K, V and the attention output     */
+  int32_t summary_dtype; /* locks_dtype_t of the summary records; must equal kv_dtype */
+  float softmax_scale;   /* logit scale, normally 1/sqrt(d); finite and > 0       */
+} locks_config_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* locks_status_string(int status);
+
+/* Library ABI version (this header: 1). */
+int locks_version(void);
+
+/* Bytes of one summary record, e*(d + r*d + P*r); 0 when cfg is invalid or
+ * unsupported. [Locks] §4: a page stores its centroid mu_j, its basis V_j and
+ * its per-token coefficients C_j. */
+size_t locks_summary_record_bytes(const locks_config_t* cfg);
+
+/* Workspace bytes needed by locks_score_select and locks_sparse_decode for a
+ * batch of `batch` sequences of at most `max_pages` pages (one buffer of
+ * this size serves both calls). Writes *bytes; returns a status. */
+int locks_workspace_size(const locks_config_t* cfg, int32_t batch, int32_t max_pages,
+                         size_t* bytes);
+
+/* (a1) Summary build, [Locks] §3-§4: for each physical block id in
+ * block_ids[n_ids] (device int32) and each KV head h, fit to the P keys
+ * k_i of that (block, head) tile
+ *     mu = (1/P) sum_i k_i,   D = [k_i - mu]_i  (P x d),
+ *     V  = top-r eigenvectors of H = D^T D (orthonormal, d x r),
+ *     C  = D V  (P x r),
+ * and store (mu, V^T, C) rounded to summary_dtype (round-to-nearest-even)
+ * into the record of (block, h) in summary_pool. Keys are read as stored;
+ * the fit is computed in fp32 (Gram matrix on the matrix cores, subspace
+ * iteration with a Rayleigh-Ritz step). Within an eigenvalue cluster any
+ * orthonormal basis of the subspace is an equally valid result; each basis
+ * vector is sign-fixed so its largest-magnitude entry is positive.
+ * Only summarise complete pages. Ids outside [0, num_blocks) are skipped;
+ * duplicate ids race. n_ids == 0 enqueues nothing. */
+int locks_build_summaries(const locks_config_t* cfg, const void* k_pool, int64_t num_blocks,
+                          const int32_t* block_ids, int32_t n_ids, void* summary_pool,
+                          hipStream_t stream);
+
+/* (a2) Page scoring, [Locks] §4 Eq. (2): for every sequence b, query head g
+ * and complete page j < floor(T_b / P), with mu, V, C the summary of
+ * block_table[b][j] for KV head g / G,
+ *     head_scores[b][g][j] = (q.mu) * scale + log sum_i exp(((V^T q).c_i) * scale)
+ * computed from the stored summary values in fp32. Entries j >= floor(T_b/P)
+ * are left untouched. head_scores: [batch][H_q][max_pages] fp32. */
+int locks_page_score(const locks_config_t* cfg, const void* q, const void* summary_pool,
+                     int64_t num_blocks, const int32_t* block_table, const int32_t* seq_lens,
+                     int32_t batch, int32_t max_pages, float* head_scores, hipStream_t stream);
+
+/* (a3 + a4) Share-average combine and selection, [Locks] §2 and §4. Per
+ * (sequence, KV head) with J pages and Jc complete pages:
+ *   log Z_g  = log sum_{j<Jc} exp(s_g(j))                 (per query head)
+ *   sigma_j  = log( (1/G) sum_g exp(s_g(j) - log Z_g) )   (log of the share average)
+ * If J <= k every page 0..J-1 is selected. Otherwise the sink page 0 and the
+ * current page J-1 are always selected and the other k-2 slots take the
+ * complete pages outside {0, J-1} with the largest sigma (ties: lower page
+ * id), by radix selection on the fp32 keys. selected receives the ids in
+ * ascending order, padded with -1. page_sigma ([batch][H_kv][max_pages]
+ * fp32) receives sigma_j for j < Jc when J > k and is left untouched
+ * otherwise; it is also the selector's scratch. head_scores as written by
+ * locks_page_score. */
+int locks_select_pages(const locks_config_t* cfg, const float* head_scores,
+                       const int32_t* seq_lens, int32_t batch, int32_t max_pages,
+                       int32_t* selected, float* page_sigma, hipStream_t stream);
+
+/* locks_page_score followed by locks_select_pages, with the head scores and
+ * page keys kept in the caller's workspace (ws, ws_bytes >=
+ * locks_workspace_size). Reads no candidate key or value ([Locks] §4). */
+int locks_score_select(const locks_config_t* cfg, const void* q, const void* summary_pool,
+                       int64_t num_blocks, const int32_t* block_table, const int32_t* seq_lens,
+                       int32_t batch, int32_t max_pages, int32_t* selected, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* (a5) Sparse decode attention over the selected pages, [Locks] §2: for
+ * query head g of sequence b, over every valid token i of the pages listed
+ * in selected[b][g / G] (the current page contributes its T - (J-1)*P valid
+ * tokens; -1 slots are skipped) with the original K and V,
+ *     out[b][g] = sum_i softmax_i(q_g . k_i * scale) v_i,
+ *     lse[b][g] = log sum_i exp(q_g . k_i * scale)
+ * Split-K over page slots with an LSE merge, fp32 accumulation; out is
+ * [batch][H_q][d] in kv_dtype (round-to-nearest-even), lse (may be NULL)
+ * [batch][H_q] fp32. A (sequence, KV head) with no valid slot gives out = 0,
+ * lse = -inf. ws as for locks_score_select. */
+int locks_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_pool,
+                        const void* v_pool, int64_t num_blocks, const int32_t* block_table,
+                        const int32_t* seq_lens, const int32_t* selected, int32_t batch,
+                        int32_t max_pages, void* out, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOCKS_H */

@@ -1,0 +1,438 @@
+// (a1) Summary build, [Locks] §3-§4: for one (physical block, KV head) tile of
+// P keys, fit
+//   mu = (1/P) sum_i k_i,  D = K - 1 mu^T,  H = D^T D (d x d),
+//   V  = top-r eigenvectors of H,  C = D V,
+// and store (mu, V^T, C) in the summary record.
+//
+// One workgroup (4 waves) per tile, everything in LDS and registers:
+//  1. K is staged transposed in LDS; mu is a plain fp32 mean.
+//  2. Gram on the matrix cores. bf16 keys: H = K^T K - P mu mu^T with
+//     v_mfma_f32_16x16x16_bf16 (exact bf16 products, fp32 accumulation);
+//     fp32 keys are centred first and use v_mfma_f32_16x16x4_f32. Wave w
+//     computes the 16-row tiles it owns against every column tile; because H
+//     is symmetric the MFMA output registers already are the A operand of
+//     H X for those rows, with the k index permuted as
+//     k(step = 4*tile + i, lane group lg) = 16*tile + 4*lg + i.
+//     H therefore never leaves registers.
+//  3. Subspace iteration on a 16-column block X: Y = H X (fp32 MFMA), then
+//     X = Y R^-1 from a Cholesky factor of the column-scaled Gram Y^T Y
+//     (columns that collapse are replaced by fresh pseudo-random vectors).
+//  4. A second Cholesky-QR pass, then Rayleigh-Ritz: T = X^T H X (16 x 16)
+//     diagonalised by parallel cyclic Jacobi; the r largest Ritz pairs give
+//     V = X W_r, each column sign-fixed so its largest-magnitude entry is
+//     positive (lowest index on ties).
+//  5. C = D V in fp32 from the unrounded V; mu, V, C are rounded to the
+//     summary dtype independently.
+#include "common.h"
+#include "kernels.h"
+
+namespace locks {
+
+constexpr int kBuildIters = 10;   // subspace iterations
+constexpr int kJacobiSweeps = 8;  // sweeps of the 16 x 16 Rayleigh-Ritz problem
+constexpr int kBlk = 16;          // block size of the subspace iteration
+
+namespace {
+
+__device__ __forceinline__ float hash_unit(uint32_t a, uint32_t b, uint32_t salt) {
+  uint32_t x = a * 0x9E3779B1u ^ (b + 97u * salt) * 0x85EBCA77u;
+  x ^= x >> 15; x *= 0x2C1B3C6Du;
+  x ^= x >> 12; x *= 0x297A2D39u;
+  x ^= x >> 15;
+  return (float)(x >> 8) * (1.0f / 8388608.0f) - 1.0f;  // [-1, 1)
+}
+
+template <typename T>
+struct GramOp;
+
+template <>
+struct GramOp<bf16_t> {
+  static constexpr int kStep = 16;  // tokens per MFMA
+  // kt row r holds the keys of dimension r over tokens (stride in elements)
+  static __device__ __forceinline__ f32x4_t mfma(const bf16_t* kt, int stride, int ra, int rb, int tok0,
+                                                 int lane, f32x4_t c) {
+    const int t = tok0 + 4 * (lane >> 4);
+    const bf16x4_t av = *reinterpret_cast<const bf16x4_t*>(kt + (ra + (lane & 15)) * stride + t);
+    const bf16x4_t bv = *reinterpret_cast<const bf16x4_t*>(kt + (rb + (lane & 15)) * stride + t);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct GramOp<float> {
+  static constexpr int kStep = 4;
+  static __device__ __forceinline__ f32x4_t mfma(const float* kt, int stride, int ra, int rb, int tok0,
+                                                 int lane, f32x4_t c) {
+    const int t = tok0 + (lane >> 4);
+    const float av = kt[(ra + (lane & 15)) * stride + t];
+    const float bv = kt[(rb + (lane & 15)) * stride + t];
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c, 0, 0, 0);
+  }
+};
+
+}  // namespace
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
+  constexpr int NT = D / 16;          // row tiles of H
+  constexpr int RTW = NT / 4;         // row tiles per wave
+  constexpr int KT_STRIDE = 64 + 4;   // LDS row stride of the transposed keys
+  __shared__ __attribute__((aligned(16))) T kt[D * KT_STRIDE];
+  __shared__ float mu[D];
+  __shared__ __attribute__((aligned(16))) float X[D][kBlk];
+  __shared__ __attribute__((aligned(16))) float Y[D][kBlk];
+  __shared__ float Mp[4][kBlk][kBlk];
+  __shared__ float Ms[kBlk][kBlk + 1];
+  __shared__ float Lm[kBlk][kBlk + 1];
+  __shared__ float Li[kBlk][kBlk + 1];
+  __shared__ float Ri[kBlk][kBlk];
+  __shared__ float Wm[kBlk][kBlk + 1];
+  __shared__ float sdiag[kBlk];
+  __shared__ int dead[kBlk];
+  __shared__ float rot[8][2];
+  __shared__ int rpq[8][2];
+  __shared__ int order[kBlk];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = blockIdx.y;
+  const int P = a.P, r = a.r;
+  const int blk = a.block_ids[blockIdx.x];
+  if (blk < 0 || (int64_t)blk >= a.num_blocks) return;  // uniform for the workgroup
+  const T* tile = reinterpret_cast<const T*>(a.k_pool) + ((int64_t)blk * a.Hkv + h) * (int64_t)P * D;
+
+  // ---- 1. keys -> LDS (transposed), centroid ----
+  {
+    constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+    const int chunks = P * D / EPC;
+    for (int c = tid; c < chunks; c += 256) {
+      const int e0 = c * EPC;
+      const int i = e0 / D;
+      const int a0 = e0 - i * D;
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(tile + e0);
+      const T* v = reinterpret_cast<const T*>(&w);
+#pragma unroll
+      for (int x = 0; x < EPC; ++x) kt[(a0 + x) * KT_STRIDE + i] = v[x];
+    }
+  }
+  __syncthreads();
+  for (int d0 = tid; d0 < D; d0 += 256) {
+    float s = 0.f;
+    for (int i = 0; i < P; ++i) s += Elem<T>::load(&kt[d0 * KT_STRIDE + i]);
+    mu[d0] = s / (float)P;
+  }
+  __syncthreads();
+  if constexpr (sizeof(T) == 4) {  // fp32 keys: centre in place
+    for (int e = tid; e < D * P; e += 256) {
+      const int d0 = e / P, i = e - d0 * P;
+      kt[d0 * KT_STRIDE + i] -= mu[d0];
+    }
+    __syncthreads();
+  }
+
+  // ---- 2. Gram matrix: hreg[t][c][i] = H[16*tc + lane%16][16*c + 4*(lane/16) + i], tc = wave*RTW + t ----
+  f32x4_t hreg[RTW][NT];
+#pragma unroll
+  for (int t = 0; t < RTW; ++t) {
+    const int tc = wave * RTW + t;
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < P; k0 += GramOp<T>::kStep)
+        acc = GramOp<T>::mfma(kt, KT_STRIDE, 16 * c, 16 * tc, k0, lane, acc);
+      if constexpr (sizeof(T) == 2) {
+        const float mrow = mu[16 * tc + (lane & 15)] * (float)P;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] -= mrow * mu[16 * c + 4 * (lane >> 4) + i];
+      }
+      hreg[t][c] = acc;
+    }
+  }
+
+  // helpers ---------------------------------------------------------------
+  // Y = H X for this wave's rows; ytile[t][i] = Y[16*tc + 4*(lane/16) + i][lane%16]
+  auto matmul_hx = [&](f32x4_t* ytile) {
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) ytile[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float bx = X[16 * c + 4 * (lane >> 4) + i][lane & 15];
+#pragma unroll
+        for (int t = 0; t < RTW; ++t)
+          ytile[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(hreg[t][c][i], bx, ytile[t], 0, 0, 0);
+      }
+    }
+  };
+  // partial Gram of the rows in `rows` (same layout as ytile) against `cols`
+  auto partial_gram = [&](const f32x4_t* rows, const f32x4_t* cols) {
+    f32x4_t m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < RTW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = __builtin_amdgcn_mfma_f32_16x16x4f32(rows[t][i], cols[t][i], m, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Mp[wave][4 * (lane >> 4) + i][lane & 15] = m[i];
+  };
+  auto load_x_tiles = [&](f32x4_t* xt) {
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      const int tc = wave * RTW + t;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xt[t][i] = X[16 * tc + 4 * (lane >> 4) + i][lane & 15];
+    }
+  };
+  auto store_y_tiles = [&](const f32x4_t* yt) {
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      const int tc = wave * RTW + t;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Y[16 * tc + 4 * (lane >> 4) + i][lane & 15] = yt[t][i];
+    }
+  };
+  // Sum Mp into Ms (wave 0), symmetrised.
+  auto reduce_gram = [&]() {
+    if (wave == 0) {
+      for (int e = lane; e < kBlk * kBlk; e += 64) {
+        const int i = e / kBlk, j = e % kBlk;
+        const float v = Mp[0][i][j] + Mp[1][i][j] + Mp[2][i][j] + Mp[3][i][j];
+        const float vt = Mp[0][j][i] + Mp[1][j][i] + Mp[2][j][i] + Mp[3][j][i];
+        Ms[i][j] = 0.5f * (v + vt);
+      }
+    }
+  };
+  // Wave 0: Ri = S L^-T from the Cholesky factor of the column-scaled Ms.
+  auto cholesky_inverse = [&]() {
+    if (wave != 0) return;
+    float dmax = 0.f;
+    for (int j = 0; j < kBlk; ++j) dmax = fmaxf(dmax, Ms[j][j]);
+    if (lane < kBlk) {
+      const float dj = Ms[lane][lane];
+      const bool dd = !(dj > 1e-30f * fmaxf(dmax, 1e-30f));
+      dead[lane] = dd ? 1 : 0;
+      sdiag[lane] = dd ? 0.f : 1.0f / sqrtf(dj);
+    }
+    wave_lds_sync();
+    // scaled matrix into Lm (lower triangle becomes L)
+    for (int e = lane; e < kBlk * kBlk; e += 64) {
+      const int i = e / kBlk, j = e % kBlk;
+      Lm[i][j] = Ms[i][j] * sdiag[i] * sdiag[j];
+    }
+    wave_lds_sync();
+    for (int j = 0; j < kBlk; ++j) {
+      // column j: v_i = Lm[i][j] - sum_{k<j} L[i][k] L[j][k] for i >= j
+      float v = 0.f;
+      if (lane >= j && lane < kBlk) {
+        v = Lm[lane][j];
+        for (int k = 0; k < j; ++k) v -= Lm[lane][k] * Lm[j][k];
+      }
+      const float vjj = __shfl(v, j, 64);
+      const bool ok = vjj > 1e-12f && !dead[j];
+      const float ljj = ok ? sqrtf(vjj) : 1.0f;
+      if (lane == j) Lm[j][j] = ljj;
+      if (lane > j && lane < kBlk) Lm[lane][j] = ok ? v / ljj : 0.f;
+      if (lane == j && !ok) dead[j] = 1;
+      wave_lds_sync();
+    }
+    // Li = L^-1 (lower), column c by forward substitution in lane c
+    if (lane < kBlk) {
+      const int c = lane;
+      for (int i = 0; i < kBlk; ++i) Li[i][c] = 0.f;
+      Li[c][c] = 1.0f / Lm[c][c];
+      for (int i = c + 1; i < kBlk; ++i) {
+        float s = 0.f;
+        for (int k = c; k < i; ++k) s += Lm[i][k] * Li[k][c];
+        Li[i][c] = -s / Lm[i][i];
+      }
+    }
+    wave_lds_sync();
+    for (int e = lane; e < kBlk * kBlk; e += 64) {
+      const int i = e / kBlk, j = e % kBlk;  // Ri[i][j] = s_i * Li[j][i]
+      Ri[i][j] = (j >= i && !dead[j]) ? sdiag[i] * Li[j][i] : 0.f;
+    }
+  };
+  // X = Y Ri (all threads), collapsed columns replaced by pseudo-random vectors
+  auto apply_rinv = [&](uint32_t salt) {
+    for (int e = tid; e < D * kBlk; e += 256) {
+      const int row = e / kBlk, c = e % kBlk;
+      float s;
+      if (dead[c]) {
+        s = hash_unit((uint32_t)row, (uint32_t)c, salt);
+      } else {
+        s = 0.f;
+        for (int j = 0; j <= c; ++j) s += Y[row][j] * Ri[j][c];
+      }
+      X[row][c] = s;
+    }
+  };
+  // One Cholesky-QR pass of the block currently in Y (rows also in `yt`).
+  auto cholqr = [&](const f32x4_t* yt, uint32_t salt) {
+    partial_gram(yt, yt);
+    __syncthreads();
+    reduce_gram();
+    __syncthreads();
+    cholesky_inverse();
+    __syncthreads();
+    apply_rinv(salt);
+    __syncthreads();
+  };
+
+  // ---- 3. subspace iteration ----
+  f32x4_t yt[RTW];
+  for (int e = tid; e < D * kBlk; e += 256) Y[e / kBlk][e % kBlk] = hash_unit((uint32_t)(e / kBlk), (uint32_t)(e % kBlk), 1u);
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < RTW; ++t) {
+    const int tc = wave * RTW + t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yt[t][i] = Y[16 * tc + 4 * (lane >> 4) + i][lane & 15];
+  }
+  cholqr(yt, 2u);
+  for (int it = 0; it < kBuildIters; ++it) {
+    matmul_hx(yt);
+    store_y_tiles(yt);
+    cholqr(yt, 3u + (uint32_t)it);
+  }
+  // second pass for orthonormality
+  load_x_tiles(yt);
+  __syncthreads();
+  store_y_tiles(yt);
+  cholqr(yt, 101u);
+
+  // ---- 4. Rayleigh-Ritz: T = X^T H X ----
+  {
+    f32x4_t xt[RTW];
+    load_x_tiles(xt);
+    matmul_hx(yt);
+    partial_gram(xt, yt);
+    __syncthreads();
+    reduce_gram();  // Ms = T (symmetrised)
+    if (wave == 0) {
+      for (int e = lane; e < kBlk * kBlk; e += 64) Wm[e / kBlk][e % kBlk] = (e / kBlk == e % kBlk) ? 1.f : 0.f;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
+        for (int rnd = 0; rnd < kBlk - 1; ++rnd) {
+          if (lane < 8) {
+            int p, q;
+            if (lane == 0) { p = kBlk - 1; q = rnd; }
+            else { p = (rnd + lane) % (kBlk - 1); q = (rnd - lane + (kBlk - 1)) % (kBlk - 1); }
+            const float apq = Ms[p][q];
+            const float app = Ms[p][p], aqq = Ms[q][q];
+            float c = 1.f, s = 0.f;
+            if (apq != 0.f && fabsf(apq) > 1e-10f * sqrtf(fabsf(app * aqq))) {
+              const float theta = (aqq - app) / (2.f * apq);
+              const float tt = (theta >= 0.f ? 1.f : -1.f) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
+              c = 1.f / sqrtf(tt * tt + 1.f);
+              s = tt * c;
+            }
+            rot[lane][0] = c; rot[lane][1] = s;
+            rpq[lane][0] = p; rpq[lane][1] = q;
+          }
+          wave_lds_sync();
+          // rows p, q of Ms
+          for (int e = lane; e < 8 * kBlk; e += 64) {
+            const int pi = e / kBlk, x = e % kBlk;
+            const int p = rpq[pi][0], q = rpq[pi][1];
+            const float c = rot[pi][0], s = rot[pi][1];
+            const float vp = Ms[p][x], vq = Ms[q][x];
+            Ms[p][x] = c * vp - s * vq;
+            Ms[q][x] = s * vp + c * vq;
+          }
+          wave_lds_sync();
+          // columns p, q of Ms and of Wm
+          for (int e = lane; e < 8 * kBlk; e += 64) {
+            const int pi = e / kBlk, x = e % kBlk;
+            const int p = rpq[pi][0], q = rpq[pi][1];
+            const float c = rot[pi][0], s = rot[pi][1];
+            const float vp = Ms[x][p], vq = Ms[x][q];
+            Ms[x][p] = c * vp - s * vq;
+            Ms[x][q] = s * vp + c * vq;
+            const float wp = Wm[x][p], wq = Wm[x][q];
+            Wm[x][p] = c * wp - s * wq;
+            Wm[x][q] = s * wp + c * wq;
+          }
+          wave_lds_sync();
+        }
+      }
+      // descending order of the Ritz values, ties by index
+      if (lane < kBlk) {
+        const float v = Ms[lane][lane];
+        int rank = 0;
+        for (int j = 0; j < kBlk; ++j) {
+          const float u = Ms[j][j];
+          rank += (u > v || (u == v && j < lane)) ? 1 : 0;
+        }
+        order[rank] = lane;
+      }
+    }
+    __syncthreads();
+  }
+  // V = X W[:, order[0..r-1]] into Y[:, 0..r-1]
+  for (int e = tid; e < D * kBlk; e += 256) {
+    const int row = e / kBlk, rho = e % kBlk;
+    if (rho < r) {
+      const int col = order[rho];
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < kBlk; ++j) s += X[row][j] * Wm[j][col];
+      Y[row][rho] = s;
+    }
+  }
+  __syncthreads();
+  // sign: largest-magnitude entry positive (lowest index on ties)
+  for (int rho = wave; rho < r; rho += 4) {
+    float best = -1.f;
+    int arg = D;
+    for (int row = lane; row < D; row += 64) {
+      const float m = fabsf(Y[row][rho]);
+      if (m > best) { best = m; arg = row; }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ob = __shfl_xor(best, o, 64);
+      const int oa = __shfl_xor(arg, o, 64);
+      if (ob > best || (ob == best && oa < arg)) { best = ob; arg = oa; }
+    }
+    if (arg >= D) arg = 0;  // only when every entry is NaN
+    const float sg = Y[arg][rho] < 0.f ? -1.f : 1.f;
+    wave_lds_sync();
+    for (int row = lane; row < D; row += 64) Y[row][rho] *= sg;
+  }
+  __syncthreads();
+
+  // ---- 5. C = D V and the record ----
+  T* rec = reinterpret_cast<T*>(a.sum_pool) + ((int64_t)blk * a.Hkv + h) * a.rec_elems;
+  for (int d0 = tid; d0 < D; d0 += 256) rec[d0] = Elem<T>::from_f32(mu[d0]);
+  for (int e = tid; e < r * D; e += 256) {
+    const int rho = e / D, d0 = e - rho * D;
+    rec[D + e] = Elem<T>::from_f32(Y[d0][rho]);
+  }
+  T* crec = rec + (int64_t)D * (1 + r);
+  for (int e = tid; e < P * r; e += 256) {
+    const int i = e / r, rho = e - i * r;
+    float s = 0.f;
+    for (int d0 = 0; d0 < D; ++d0) {
+      float kv = Elem<T>::load(&kt[d0 * KT_STRIDE + i]);
+      if constexpr (sizeof(T) == 2) kv -= mu[d0];
+      s = fmaf(kv, Y[d0][rho], s);
+    }
+    crec[e] = Elem<T>::from_f32(s);
+  }
+}
+
+hipError_t launch_build(const BuildArgs& a, int dtype, int D, hipStream_t stream) {
+  dim3 grid(a.n, a.Hkv);
+  if (dtype == 0) {
+    if (D == 64) hipLaunchKernelGGL((build_kernel<bf16_t, 64>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((build_kernel<bf16_t, 128>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((build_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((build_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace locks

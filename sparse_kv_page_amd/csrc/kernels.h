@@ -1,0 +1,61 @@
+// Kernel argument blocks and launchers of the Locks library (host + device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace locks {
+
+struct ScoreArgs {
+  const void* q;              // [B][Hq][D] kv dtype
+  const uint8_t* sum_pool;    // [blocks][Hkv][record]
+  const int32_t* block_table; // [B][max_pages]
+  const int32_t* seq_lens;    // [B]
+  float* scores;              // [B][Hq][max_pages]
+  int64_t num_blocks;
+  int64_t rec_elems;          // elements per record
+  int Hkv, G, P, r, max_pages;
+  int ppw;                    // pages per wave (<= 64)
+  float scale;
+};
+
+struct SelectArgs {
+  const float* scores;        // [B][Hq][max_pages]
+  const int32_t* seq_lens;    // [B]
+  int32_t* selected;          // [B][Hkv][k]
+  float* sigma;               // [B][Hkv][max_pages]
+  int Hkv, G, P, k, max_pages;
+};
+
+struct DecodeArgs {
+  const void* q;              // [B][Hq][D]
+  const void* k_pool;         // [blocks][Hkv][P][D]
+  const void* v_pool;
+  const int32_t* block_table; // [B][max_pages]
+  const int32_t* seq_lens;    // [B]
+  const int32_t* selected;    // [B][Hkv][k]
+  float* part_o;              // [B][Hq][splits][D]
+  float* part_lse;            // [B][Hq][splits]
+  void* out;                  // [B][Hq][D] kv dtype
+  float* lse;                 // [B][Hq] or null
+  int64_t num_blocks;
+  int Hkv, G, P, k, max_pages;
+  int pages_per_split, splits;
+  float scale;
+};
+
+struct BuildArgs {
+  const void* k_pool;         // [blocks][Hkv][P][D]
+  const int32_t* block_ids;   // [n]
+  uint8_t* sum_pool;          // [blocks][Hkv][record]
+  int64_t num_blocks;
+  int64_t rec_elems;
+  int Hkv, P, r, n;
+};
+
+hipError_t launch_page_score(const ScoreArgs& a, int dtype, int D, int batch, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s);
+hipError_t launch_sparse_decode(const DecodeArgs& a, int dtype, int D, int batch, hipStream_t s);
+hipError_t launch_build(const BuildArgs& a, int dtype, int D, hipStream_t s);
+
+}  // namespace locks

@@ -1,0 +1,245 @@
+// Host side of the Locks C ABI: argument validation, workspace layout and
+// kernel dispatch. Every entry point decides OK/error from its arguments
+// alone, then only enqueues work on the caller's stream.
+#include "../../include/locks.h"
+
+#include <cmath>
+#include <cstddef>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxK = 1024;
+constexpr int kDecodePagesPerSplit = 4;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int dtype) { return dtype == LOCKS_BF16 ? 2 : 4; }
+
+int check_config(const locks_config_t* c) {
+  if (!c) return LOCKS_E_INVALID_ARG;
+  if (c->head_dim <= 0 || c->page_size <= 0 || c->rank <= 0 || c->num_q_heads <= 0 ||
+      c->num_kv_heads <= 0 || c->budget_pages < 2)
+    return LOCKS_E_INVALID_ARG;
+  if (!std::isfinite(c->softmax_scale) || !(c->softmax_scale > 0.f)) return LOCKS_E_INVALID_ARG;
+  if (c->kv_dtype != LOCKS_BF16 && c->kv_dtype != LOCKS_F32) return LOCKS_E_INVALID_ARG;
+  if (c->summary_dtype != LOCKS_BF16 && c->summary_dtype != LOCKS_F32) return LOCKS_E_INVALID_ARG;
+  if (c->num_q_heads % c->num_kv_heads != 0) return LOCKS_E_INVALID_ARG;
+  const int G = c->num_q_heads / c->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return LOCKS_E_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return LOCKS_E_UNSUPPORTED;
+  if (c->page_size != 16 && c->page_size != 32 && c->page_size != 64) return LOCKS_E_UNSUPPORTED;
+  if (c->rank > 15 || c->rank > c->page_size - 1) return LOCKS_E_UNSUPPORTED;
+  if (c->budget_pages > kMaxK) return LOCKS_E_UNSUPPORTED;
+  if (c->summary_dtype != c->kv_dtype) return LOCKS_E_UNSUPPORTED;
+  return LOCKS_OK;
+}
+
+int check_batch(int32_t batch, int32_t max_pages) {
+  if (batch < 0 || max_pages < 0) return LOCKS_E_INVALID_ARG;
+  if (batch > 0 && max_pages < 1) return LOCKS_E_INVALID_ARG;
+  if (batch > 65535) return LOCKS_E_UNSUPPORTED;  // grid dimension
+  // page offsets and token counts stay inside int32
+  if ((int64_t)max_pages * 64 > (int64_t)0x7fffffff) return LOCKS_E_UNSUPPORTED;
+  return LOCKS_OK;
+}
+
+int64_t rec_elems(const locks_config_t* c) {
+  return (int64_t)c->head_dim * (1 + c->rank) + (int64_t)c->page_size * c->rank;
+}
+
+size_t score_ws_bytes(const locks_config_t* c, int32_t batch, int32_t max_pages) {
+  const size_t scores = (size_t)batch * c->num_q_heads * max_pages * sizeof(float);
+  const size_t sigma = (size_t)batch * c->num_kv_heads * max_pages * sizeof(float);
+  return align_up(scores) + align_up(sigma);
+}
+
+int decode_splits(const locks_config_t* c) {
+  return (c->budget_pages + kDecodePagesPerSplit - 1) / kDecodePagesPerSplit;
+}
+
+size_t decode_ws_bytes(const locks_config_t* c, int32_t batch) {
+  const size_t rows = (size_t)batch * c->num_q_heads * decode_splits(c);
+  return align_up(rows * c->head_dim * sizeof(float)) + align_up(rows * sizeof(float));
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LOCKS_OK : LOCKS_E_HIP; }
+
+int pages_per_wave(int32_t batch, int hkv, int32_t max_pages) {
+  const int64_t total = (int64_t)batch * hkv * max_pages;
+  int64_t ppw = (total + 2048 * 4 - 1) / (2048 * 4);
+  if (ppw < 1) ppw = 1;
+  if (ppw > 64) ppw = 64;
+  return (int)ppw;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* locks_status_string(int status) {
+  switch (status) {
+    case LOCKS_OK: return "ok";
+    case LOCKS_E_INVALID_ARG: return "invalid argument";
+    case LOCKS_E_UNSUPPORTED: return "unsupported shape or dtype";
+    case LOCKS_E_WORKSPACE: return "workspace missing or too small";
+    case LOCKS_E_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int locks_version(void) { return 1; }
+
+size_t locks_summary_record_bytes(const locks_config_t* cfg) {
+  if (check_config(cfg) != LOCKS_OK) return 0;
+  return (size_t)rec_elems(cfg) * elem_bytes(cfg->summary_dtype);
+}
+
+int locks_workspace_size(const locks_config_t* cfg, int32_t batch, int32_t max_pages, size_t* bytes) {
+  int st = check_config(cfg);
+  if (st != LOCKS_OK) return st;
+  if (!bytes) return LOCKS_E_INVALID_ARG;
+  st = check_batch(batch, max_pages);
+  if (st != LOCKS_OK) return st;
+  const size_t a = score_ws_bytes(cfg, batch, max_pages);
+  const size_t b = decode_ws_bytes(cfg, batch);
+  *bytes = a > b ? a : b;
+  return LOCKS_OK;
+}
+
+int locks_build_summaries(const locks_config_t* cfg, const void* k_pool, int64_t num_blocks,
+                          const int32_t* block_ids, int32_t n_ids, void* summary_pool,
+                          hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != LOCKS_OK) return st;
+  if (n_ids < 0 || num_blocks < 0) return LOCKS_E_INVALID_ARG;
+  if (n_ids == 0) return LOCKS_OK;
+  if (!k_pool || !block_ids || !summary_pool) return LOCKS_E_INVALID_ARG;
+  if (cfg->num_kv_heads > 65535) return LOCKS_E_UNSUPPORTED;
+  locks::BuildArgs a{};
+  a.k_pool = k_pool;
+  a.block_ids = block_ids;
+  a.sum_pool = static_cast<uint8_t*>(summary_pool);
+  a.num_blocks = num_blocks;
+  a.rec_elems = rec_elems(cfg);
+  a.Hkv = cfg->num_kv_heads;
+  a.P = cfg->page_size;
+  a.r = cfg->rank;
+  a.n = n_ids;
+  return hip_status(locks::launch_build(a, cfg->kv_dtype, cfg->head_dim, stream));
+}
+
+int locks_page_score(const locks_config_t* cfg, const void* q, const void* summary_pool,
+                     int64_t num_blocks, const int32_t* block_table, const int32_t* seq_lens,
+                     int32_t batch, int32_t max_pages, float* head_scores, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != LOCKS_OK) return st;
+  st = check_batch(batch, max_pages);
+  if (st != LOCKS_OK) return st;
+  if (num_blocks < 0) return LOCKS_E_INVALID_ARG;
+  if (batch == 0) return LOCKS_OK;
+  if (!q || !summary_pool || !block_table || !seq_lens || !head_scores) return LOCKS_E_INVALID_ARG;
+  locks::ScoreArgs a{};
+  a.q = q;
+  a.sum_pool = static_cast<const uint8_t*>(summary_pool);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.scores = head_scores;
+  a.num_blocks = num_blocks;
+  a.rec_elems = rec_elems(cfg);
+  a.Hkv = cfg->num_kv_heads;
+  a.G = cfg->num_q_heads / cfg->num_kv_heads;
+  a.P = cfg->page_size;
+  a.r = cfg->rank;
+  a.max_pages = max_pages;
+  a.ppw = pages_per_wave(batch, a.Hkv, max_pages);
+  a.scale = cfg->softmax_scale;
+  return hip_status(locks::launch_page_score(a, cfg->kv_dtype, cfg->head_dim, batch, stream));
+}
+
+int locks_select_pages(const locks_config_t* cfg, const float* head_scores, const int32_t* seq_lens,
+                       int32_t batch, int32_t max_pages, int32_t* selected, float* page_sigma,
+                       hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != LOCKS_OK) return st;
+  st = check_batch(batch, max_pages);
+  if (st != LOCKS_OK) return st;
+  if (batch == 0) return LOCKS_OK;
+  if (!head_scores || !seq_lens || !selected || !page_sigma) return LOCKS_E_INVALID_ARG;
+  locks::SelectArgs a{};
+  a.scores = head_scores;
+  a.seq_lens = seq_lens;
+  a.selected = selected;
+  a.sigma = page_sigma;
+  a.Hkv = cfg->num_kv_heads;
+  a.G = cfg->num_q_heads / cfg->num_kv_heads;
+  a.P = cfg->page_size;
+  a.k = cfg->budget_pages;
+  a.max_pages = max_pages;
+  return hip_status(locks::launch_select(a, batch, stream));
+}
+
+int locks_score_select(const locks_config_t* cfg, const void* q, const void* summary_pool,
+                       int64_t num_blocks, const int32_t* block_table, const int32_t* seq_lens,
+                       int32_t batch, int32_t max_pages, int32_t* selected, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != LOCKS_OK) return st;
+  st = check_batch(batch, max_pages);
+  if (st != LOCKS_OK) return st;
+  if (num_blocks < 0) return LOCKS_E_INVALID_ARG;
+  if (batch == 0) return LOCKS_OK;
+  if (!q || !summary_pool || !block_table || !seq_lens || !selected) return LOCKS_E_INVALID_ARG;
+  if (!ws || ws_bytes < score_ws_bytes(cfg, batch, max_pages)) return LOCKS_E_WORKSPACE;
+  float* scores = static_cast<float*>(ws);
+  float* sigma = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+                                          align_up((size_t)batch * cfg->num_q_heads * max_pages * sizeof(float)));
+  st = locks_page_score(cfg, q, summary_pool, num_blocks, block_table, seq_lens, batch, max_pages,
+                        scores, stream);
+  if (st != LOCKS_OK) return st;
+  return locks_select_pages(cfg, scores, seq_lens, batch, max_pages, selected, sigma, stream);
+}
+
+int locks_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_pool,
+                        const void* v_pool, int64_t num_blocks, const int32_t* block_table,
+                        const int32_t* seq_lens, const int32_t* selected, int32_t batch,
+                        int32_t max_pages, void* out, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != LOCKS_OK) return st;
+  st = check_batch(batch, max_pages);
+  if (st != LOCKS_OK) return st;
+  if (num_blocks < 0) return LOCKS_E_INVALID_ARG;
+  if (batch == 0) return LOCKS_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !selected || !out)
+    return LOCKS_E_INVALID_ARG;
+  if (!ws || ws_bytes < decode_ws_bytes(cfg, batch)) return LOCKS_E_WORKSPACE;
+  const int splits = decode_splits(cfg);
+  const size_t rows = (size_t)batch * cfg->num_q_heads * splits;
+  locks::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.selected = selected;
+  a.part_o = static_cast<float*>(ws);
+  a.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+                                        align_up(rows * cfg->head_dim * sizeof(float)));
+  a.out = out;
+  a.lse = lse;
+  a.num_blocks = num_blocks;
+  a.Hkv = cfg->num_kv_heads;
+  a.G = cfg->num_q_heads / cfg->num_kv_heads;
+  a.P = cfg->page_size;
+  a.k = cfg->budget_pages;
+  a.max_pages = max_pages;
+  a.pages_per_split = kDecodePagesPerSplit;
+  a.splits = splits;
+  a.scale = cfg->softmax_scale;
+  return hip_status(locks::launch_sparse_decode(a, cfg->kv_dtype, cfg->head_dim, batch, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,466 @@
+"""GPU parity of the HIP path against the fp64 oracle, stage by stage and end to
+end, through the C ABI (liblocks.so). Inputs come from the seeded generator;
+stage inputs of the GPU (summaries, page scores, selections) come from the
+oracle or the generator, never from an earlier GPU stage.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_kv_page_amd import locks as L
+from sparse_kv_page_amd import synth
+from tests import gpu_glue as gg
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+TINY = W["tiny_f32"]
+W32K = W["llama8b_32k"]
+# small bf16 workload for end-to-end checks: ragged batch, partial pages, J > k
+E2E = synth.Workload("e2e_bf16", 3, 2, 4, 128, 64, (64 * 40 + 37, 64 * 24, 64 * 9 + 1), 4, 8,
+                     "bf16", "bf16", n_needles=3, extra_blocks=5)
+
+
+def _cfg(wl):
+    return L.config_for(wl)
+
+
+# --------------------------------------------------------------------------
+# (a2) scorer on identical summary bytes
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("wl,source", [(TINY, "oracle"), (E2E, "oracle"), (W32K, "synthetic")],
+                         ids=["tiny_f32", "e2e_bf16", "llama8b_32k"])
+def test_page_score_parity(wl, source):
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=0)
+    if source == "oracle":
+        summ, _, _ = gg.oracle_summaries(wl, data)
+        pool = gg.pool_from_summaries(wl, cfg, summ)
+    else:
+        pool = gg.synthetic_pool(wl, cfg, seed=0)
+    hs = gg.gpu_scores(wl, cfg, g, pool)
+    torch.cuda.synchronize()
+    hs_c = hs.cpu()
+    pool_c = pool.cpu()
+    worst = 0.0
+    for b in range(wl.batch):
+        _, J, Jc = gg.lens(wl, b)
+        for h in range(wl.num_kv_heads):
+            mu, vt, cf = gg.unit_records(wl, cfg, pool_c, data["block_table"], b, h, Jc)
+            ref = gg.oracle_unit_scores(wl, data, b, h, mu, vt, cf)
+            got = gg.f64(hs_c[b, h * wl.group:(h + 1) * wl.group, :Jc])
+            worst = max(worst, gg.mixed_violation(got, ref))
+            # entries past the complete pages are left untouched
+            assert torch.isnan(hs_c[b, h * wl.group:(h + 1) * wl.group, Jc:]).all()
+    assert worst <= 1.0, f"score violation {worst:.3f} x tolerance"
+
+
+# --------------------------------------------------------------------------
+# (a3+a4) selector on identical page scores
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("wl", [TINY, E2E, W32K], ids=["tiny_f32", "e2e_bf16", "llama8b_32k"])
+def test_select_parity(wl):
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=1)
+    pool = gg.synthetic_pool(wl, cfg, seed=1, device="cpu")
+    hs = torch.full((wl.batch, wl.num_q_heads, wl.max_pages), float("nan"), dtype=torch.float32)
+    refs = {}
+    for b in range(wl.batch):
+        _, J, Jc = gg.lens(wl, b)
+        for h in range(wl.num_kv_heads):
+            mu, vt, cf = gg.unit_records(wl, cfg, pool, data["block_table"], b, h, Jc)
+            s = gg.oracle_unit_scores(wl, data, b, h, mu, vt, cf)
+            hs[b, h * wl.group:(h + 1) * wl.group, :Jc] = torch.from_numpy(s).float()
+            s32 = hs[b, h * wl.group:(h + 1) * wl.group, :Jc].double().numpy()
+            refs[(b, h)] = gg.oracle_unit_select(wl, b, s32)
+    sel, sig = gg.gpu_select(wl, cfg, g, hs.to(gg.DEV))
+    torch.cuda.synchronize()
+    sel, sig = sel.cpu(), sig.cpu()
+    ndiff = 0
+    for (b, h), (sel_o, sigma_o) in refs.items():
+        ndiff += gg.check_selection(wl, b, sel[b, h].tolist(), sel_o.tolist(), sigma_o)
+        if sigma_o is not None:
+            _, J, Jc = gg.lens(wl, b)
+            assert gg.mixed_violation(gg.f64(sig[b, h, :Jc]), sigma_o) <= 1.0
+    assert ndiff <= 2 * len(refs)
+
+
+def test_select_ties_go_to_lower_page():
+    """Equal keys: the lower page id wins (radix select resolves full 64-bit keys)."""
+    wl = E2E.with_(batch=1, seq_lens=(64 * 40,), budget_pages=6)
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=2)
+    hs = torch.zeros((1, wl.num_q_heads, wl.max_pages), dtype=torch.float32)
+    hs[0, :, [3, 7, 11, 20, 30]] = 1.0    # 5 tied winners for 4 free slots
+    hs[0, :, 38] = 5.0                    # page J-1 = 39 is mandatory; 38 wins outright
+    sel, _ = gg.gpu_select(wl, cfg, g, hs.to(gg.DEV))
+    for h in range(wl.num_kv_heads):
+        assert sel[0, h].tolist() == [0, 3, 7, 11, 38, 39]
+    # all-equal scores: lowest ids
+    hs2 = torch.full((1, wl.num_q_heads, wl.max_pages), -3.25)
+    sel2, _ = gg.gpu_select(wl, cfg, g, hs2.to(gg.DEV))
+    assert sel2[0, 0].tolist() == [0, 1, 2, 3, 4, 39]
+
+
+# --------------------------------------------------------------------------
+# (a5) sparse decode on the oracle's page selection
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("wl", [TINY, E2E, W32K], ids=["tiny_f32", "e2e_bf16", "llama8b_32k"])
+def test_sparse_decode_parity(wl):
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=3)
+    rng = np.random.default_rng(3)
+    k = wl.budget_pages
+    sel = np.full((wl.batch, wl.num_kv_heads, k), -1, dtype=np.int32)
+    for b in range(wl.batch):
+        _, J, Jc = gg.lens(wl, b)
+        for h in range(wl.num_kv_heads):
+            if J <= k:
+                sel[b, h, :J] = np.arange(J)
+            else:   # a valid selection: sink, current page, k-2 random others
+                others = rng.choice(np.arange(1, J - 1), size=k - 2, replace=False)
+                sel[b, h] = np.sort(np.concatenate([[0, J - 1], others]))
+    out, lse = gg.gpu_decode(wl, cfg, g, torch.from_numpy(sel).to(gg.DEV))
+    torch.cuda.synchronize()
+    out, lse = gg.f64(out.cpu()), gg.f64(lse.cpu())
+    worst_o, worst_l = 0.0, 0.0
+    for b in range(wl.batch):
+        for h in range(wl.num_kv_heads):
+            o_ref, l_ref = gg.oracle_unit_attend(wl, data, b, h, sel[b, h])
+            sl = slice(h * wl.group, (h + 1) * wl.group)
+            worst_o = max(worst_o, float(np.max(np.abs(out[b, sl] - o_ref))))
+            worst_l = max(worst_l, gg.mixed_violation(lse[b, sl], l_ref))
+    assert worst_o <= gg.out_tol(wl), worst_o
+    assert worst_l <= 1.0, worst_l
+
+
+def test_full_budget_decode_is_dense():
+    """k >= J: every page is selected and the result is dense decode attention."""
+    wl = E2E.with_(budget_pages=64)
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=4)
+    pool = gg.synthetic_pool(wl, cfg, seed=4)
+    sel = gg.gpu_score_select(wl, cfg, g, pool)
+    out, _ = gg.gpu_decode(wl, cfg, g, sel)
+    torch.cuda.synchronize()
+    out = gg.f64(out.cpu())
+    for b in range(wl.batch):
+        T, J, _ = gg.lens(wl, b)
+        assert sel[b, 0].tolist() == list(range(J)) + [-1] * (64 - J)
+        for h in range(wl.num_kv_heads):
+            G = wl.group
+            bt = data["block_table"][b, :J].long()
+            keys = gg.f64(data["k_pool"][bt, h].reshape(-1, wl.head_dim)[:T])
+            vals = gg.f64(data["v_pool"][bt, h].reshape(-1, wl.head_dim)[:T])
+            o_ref, _ = oracle.attend(gg.f64(data["q"][b, h * G:(h + 1) * G]), keys, vals,
+                                     wl.softmax_scale)
+            assert np.max(np.abs(out[b, h * G:(h + 1) * G] - o_ref)) <= gg.out_tol(wl)
+
+
+# --------------------------------------------------------------------------
+# (a1) summary build
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("wl,npages", [(TINY, None), (E2E, 48), (W32K, 48)],
+                         ids=["tiny_f32", "e2e_bf16", "llama8b_32k"])
+def test_build_parity(wl, npages):
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=5)
+    pool = gg.gpu_build(wl, cfg, g)
+    torch.cuda.synchronize()
+    pool_c = pool.cpu()
+    mu_g, vt_g, cf_g = L.split_records(cfg, pool_c)
+    pages = []
+    for b in range(wl.batch):
+        _, _, Jc = gg.lens(wl, b)
+        for h in range(wl.num_kv_heads):
+            pages += [(int(data["block_table"][b, j]), h) for j in range(Jc)]
+    if npages is not None:
+        rng = np.random.default_rng(5)
+        pages = [pages[i] for i in sorted(rng.choice(len(pages), npages, replace=False))]
+    summ, raw, keys = gg.oracle_summaries(wl, data, pages)
+    bf = wl.summary_dtype == "bf16"
+    r = wl.rank
+    checked = 0
+    for i, (blk, h) in enumerate(pages):
+        mu_o, vt_o, cf_o, ev = raw[(blk, h)]
+        K = keys[i]
+        D = K - mu_o
+        mu = gg.f64(mu_g[blk, h]); vt = gg.f64(vt_g[blk, h]); cf = gg.f64(cf_g[blk, h])
+        # centroid: the rounded mean (one storage ulp)
+        ulp = 2.0 ** -7 if bf else 1e-6
+        assert np.all(np.abs(mu - mu_o) <= ulp * np.maximum(np.abs(mu_o), 1e-3) + 1e-7)
+        # orthonormal basis (up to storage rounding)
+        assert np.max(np.abs(vt @ vt.T - np.eye(r))) <= (2e-2 if bf else 1e-5)
+        # C = D V for the stored V (up to storage rounding)
+        scale_c = max(1.0, np.max(np.abs(cf_o)))
+        assert np.max(np.abs(cf - D @ vt.T)) <= (3e-2 if bf else 1e-4) * scale_c
+        # Eckart-Young: residual of the GPU basis matches the optimum
+        tau_opt = float(np.sum(np.clip(ev[r:], 0, None)))
+        resid = float(np.linalg.norm(D - D @ vt.T @ vt) ** 2)
+        total = float(np.sum(np.clip(ev, 0, None)))
+        assert resid <= tau_opt + (2e-2 if bf else 1e-5) * total + 1e-9, (resid, tau_opt)
+        # same subspace where the eigen-gap makes it well defined
+        gap = (ev[r - 1] - ev[r]) / max(ev[r - 1], 1e-30)
+        if gap > 0.2:
+            dist = np.linalg.norm(vt.T @ vt - vt_o.T @ vt_o)
+            assert dist <= (5e-2 if bf else 1e-4), (dist, gap)
+            checked += 1
+    assert checked >= max(1, len(pages) // 4)
+
+
+def test_full_rank_reconstruction_equals_exact_lse():
+    """r = P - 1 >= rank(D): the GPU-built summaries reproduce the exact page LSE
+    ([Locks] Thm. 1(i), eta = 0) and the selection equals the exact-LSE set."""
+    wl = TINY.with_(rank=15, noise=0.2)
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=6)
+    pool = gg.gpu_build(wl, cfg, g)
+    hs = gg.gpu_scores(wl, cfg, g, pool)
+    sel, _ = gg.gpu_select(wl, cfg, g, hs)
+    torch.cuda.synchronize()
+    T, J, Jc = gg.lens(wl, 0)
+    bt = data["block_table"][0, :Jc].long()
+    keys = gg.f64(data["k_pool"][bt, 0])
+    q = gg.f64(data["q"][0])
+    s_exact = oracle.exact_page_lse(q, keys, wl.softmax_scale)
+    assert gg.mixed_violation(gg.f64(hs[0, :, :Jc].cpu()), s_exact) <= 1.0
+    sel_o, sigma_o = gg.oracle_unit_select(wl, 0, s_exact)
+    gg.check_selection(wl, 0, sel[0, 0].tolist(), sel_o.tolist(), sigma_o)
+
+
+# --------------------------------------------------------------------------
+# end to end: build -> score -> select -> decode on the GPU vs the oracle
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("wl", [TINY, E2E], ids=["tiny_f32", "e2e_bf16"])
+def test_end_to_end(wl):
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=7)
+    pool = gg.gpu_build(wl, cfg, g)
+    hs = gg.gpu_scores(wl, cfg, g, pool)
+    sel, _ = gg.gpu_select(wl, cfg, g, hs)
+    sel_c = gg.gpu_score_select(wl, cfg, g, pool)
+    out, _ = gg.gpu_decode(wl, cfg, g, sel)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel_c)  # the fused entry point matches the two stages
+    summ, _, _ = gg.oracle_summaries(wl, data)
+    hs, sel, out = hs.cpu(), sel.cpu(), gg.f64(out.cpu())
+    same = 0
+    units = 0
+    for b in range(wl.batch):
+        _, J, Jc = gg.lens(wl, b)
+        for h in range(wl.num_kv_heads):
+            units += 1
+            blocks = [int(x) for x in data["block_table"][b, :Jc]]
+            mu = np.stack([summ[(x, h)][0] for x in blocks])
+            vt = np.stack([summ[(x, h)][1] for x in blocks])
+            cf = np.stack([summ[(x, h)][2] for x in blocks])
+            s_o = gg.oracle_unit_scores(wl, data, b, h, mu, vt, cf)
+            assert gg.mixed_violation(gg.f64(hs[b, h * wl.group:(h + 1) * wl.group, :Jc]), s_o) <= 1.0
+            sel_o, sigma_o = gg.oracle_unit_select(wl, b, s_o)
+            nd = gg.check_selection(wl, b, sel[b, h].tolist(), sel_o.tolist(), sigma_o)
+            if nd == 0:
+                same += 1
+                o_ref, _ = gg.oracle_unit_attend(wl, data, b, h, sel_o)
+                sl = slice(h * wl.group, (h + 1) * wl.group)
+                assert np.max(np.abs(out[b, sl] - o_ref)) <= gg.out_tol(wl)
+    assert same >= units - 1
+
+
+# --------------------------------------------------------------------------
+# shapes: group sizes, head dims, page sizes, ranks (generic-rank kernels too)
+# --------------------------------------------------------------------------
+VARIANTS = [
+    dict(group=1, head_dim=128, page_size=64, rank=8),
+    dict(group=2, head_dim=64, page_size=32, rank=3),
+    dict(group=8, head_dim=128, page_size=16, rank=5),
+    dict(group=4, head_dim=64, page_size=16, rank=1),
+    dict(group=4, head_dim=128, page_size=32, rank=2, kv_dtype="f32", summary_dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("kw", VARIANTS, ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
+def test_shape_variants(kw):
+    P = kw["page_size"]
+    wl = synth.Workload("variant", 2, 2, kw["group"], kw["head_dim"], P, (P * 21 + 3, P * 12),
+                        kw["rank"], 6, kw.get("kv_dtype", "bf16"), kw.get("summary_dtype", "bf16"),
+                        n_needles=2)
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=8)
+    summ, _, _ = gg.oracle_summaries(wl, data)
+    pool = gg.pool_from_summaries(wl, cfg, summ)
+    hs = gg.gpu_scores(wl, cfg, g, pool)
+    # selector on the oracle's scores rounded to fp32; decode on the oracle's selection
+    hs_o = torch.full_like(hs.cpu(), float("nan"))
+    sel_o_all = torch.full((wl.batch, wl.num_kv_heads, wl.budget_pages), -1, dtype=torch.int32)
+    refs = {}
+    for b in range(wl.batch):
+        _, J, Jc = gg.lens(wl, b)
+        for h in range(wl.num_kv_heads):
+            blocks = [int(x) for x in data["block_table"][b, :Jc]]
+            mu = np.stack([summ[(x, h)][0] for x in blocks])
+            vt = np.stack([summ[(x, h)][1] for x in blocks])
+            cf = np.stack([summ[(x, h)][2] for x in blocks])
+            s_o = gg.oracle_unit_scores(wl, data, b, h, mu, vt, cf)
+            sl = slice(h * wl.group, (h + 1) * wl.group)
+            assert gg.mixed_violation(gg.f64(hs[b, sl, :Jc].cpu()), s_o) <= 1.0
+            hs_o[b, sl, :Jc] = torch.from_numpy(s_o).float()
+            s32 = hs_o[b, sl, :Jc].double().numpy()
+            sel_o, sigma_o = gg.oracle_unit_select(wl, b, s32)
+            refs[(b, h)] = (sel_o, sigma_o)
+            sel_o_all[b, h] = torch.from_numpy(sel_o)
+    sel, _ = gg.gpu_select(wl, cfg, g, hs_o.to(gg.DEV))
+    out, _ = gg.gpu_decode(wl, cfg, g, sel_o_all.to(gg.DEV))
+    torch.cuda.synchronize()
+    sel, out = sel.cpu(), gg.f64(out.cpu())
+    for (b, h), (sel_o, sigma_o) in refs.items():
+        gg.check_selection(wl, b, sel[b, h].tolist(), sel_o.tolist(), sigma_o)
+        o_ref, _ = gg.oracle_unit_attend(wl, data, b, h, sel_o)
+        sl = slice(h * wl.group, (h + 1) * wl.group)
+        assert np.max(np.abs(out[b, sl] - o_ref)) <= gg.out_tol(wl)
+
+
+# --------------------------------------------------------------------------
+# edge cases and robustness
+# --------------------------------------------------------------------------
+def test_edge_lengths():
+    """Empty, one-token, exactly-k, k+1 pages, partial pages; max_pages > needed."""
+    P, k = 64, 4
+    lens_ = (0, 1, 63, 64, 65, P * k, P * k + 1, P * (k + 1), P * 9 + 17)
+    wl = synth.Workload("edges", len(lens_), 2, 4, 128, P, lens_, 4, k, "bf16", "bf16",
+                        extra_blocks=3)
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=9)
+    pool = gg.synthetic_pool(wl, cfg, seed=9)
+    sel = gg.gpu_score_select(wl, cfg, g, pool)
+    out, lse = gg.gpu_decode(wl, cfg, g, sel)
+    torch.cuda.synchronize()
+    sel, out, lse = sel.cpu(), gg.f64(out.cpu()), gg.f64(lse.cpu())
+    pool_c = pool.cpu()
+    for b, T in enumerate(lens_):
+        _, J, Jc = gg.lens(wl, b)
+        for h in range(wl.num_kv_heads):
+            if J > k:
+                mu, vt, cf = gg.unit_records(wl, cfg, pool_c, data["block_table"], b, h, Jc)
+                s_o = gg.oracle_unit_scores(wl, data, b, h, mu, vt, cf)
+            else:
+                s_o = None
+            sel_o, sigma_o = gg.oracle_unit_select(wl, b, s_o)
+            gg.check_selection(wl, b, sel[b, h].tolist(), sel_o.tolist(), sigma_o)
+            sl = slice(h * wl.group, (h + 1) * wl.group)
+            if T == 0:
+                assert np.all(out[b, sl] == 0) and np.all(np.isneginf(lse[b, sl]))
+                continue
+            if sel[b, h].tolist() == sel_o.tolist():
+                o_ref, _ = gg.oracle_unit_attend(wl, data, b, h, sel_o)
+                assert np.max(np.abs(out[b, sl] - o_ref)) <= gg.out_tol(wl)
+
+
+def test_invalid_block_ids_are_skipped():
+    """A block id outside the pool scores -inf and is never chosen; decode skips it."""
+    wl = E2E.with_(batch=1, seq_lens=(64 * 30,))
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=10)
+    g["block_table"][0, 5] = -1
+    g["block_table"][0, 6] = wl.num_blocks + 100
+    pool = gg.synthetic_pool(wl, cfg, seed=10)
+    hs = gg.gpu_scores(wl, cfg, g, pool)
+    sel, _ = gg.gpu_select(wl, cfg, g, hs)
+    torch.cuda.synchronize()
+    assert torch.isneginf(hs[0, :, 5]).all() and torch.isneginf(hs[0, :, 6]).all()
+    assert torch.isfinite(hs[0, :, :30][:, [j for j in range(30) if j not in (5, 6)]]).all()
+    for h in range(wl.num_kv_heads):
+        assert 5 not in sel[0, h].tolist() and 6 not in sel[0, h].tolist()
+    # a selection naming the bad pages attends the remaining ones only
+    bad = torch.tensor([[[0, 5, 6, 9, 12, 15, 20, 29]] * wl.num_kv_heads], dtype=torch.int32)
+    good = torch.tensor([[[0, -1, -1, 9, 12, 15, 20, 29]] * wl.num_kv_heads], dtype=torch.int32)
+    o1, _ = gg.gpu_decode(wl, cfg, g, bad.to(gg.DEV))
+    o2, _ = gg.gpu_decode(wl, cfg, g, good.to(gg.DEV))
+    assert torch.equal(o1, o2)
+
+
+def test_deterministic_repeats():
+    wl = E2E
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=11)
+    res = []
+    for _ in range(3):
+        pool = gg.gpu_build(wl, cfg, g)
+        hs = gg.gpu_scores(wl, cfg, g, pool)
+        sel, sig = gg.gpu_select(wl, cfg, g, hs)
+        out, lse = gg.gpu_decode(wl, cfg, g, sel)
+        torch.cuda.synchronize()
+        res.append([t.cpu() for t in (pool, hs, sel, out, lse)])
+    for other in res[1:]:
+        for a, b in zip(res[0], other):
+            assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+# --------------------------------------------------------------------------
+# headline shape (128K context, batch 8, r = 8): sampled parity at full size
+# --------------------------------------------------------------------------
+def test_headline_sampled():
+    wl = W["llama8b_128k_b8"]
+    cfg = _cfg(wl)
+    d = synth.generate(wl, 0, gg.DEV)
+    # scorer + selector on synthetic records, all units on the GPU
+    pool = gg.synthetic_pool(wl, cfg, seed=0)
+    hs = gg.gpu_scores(wl, cfg, d, pool)
+    sel = gg.gpu_score_select(wl, cfg, d, pool)
+    torch.cuda.synchronize()
+    units = [(0, 0), (3, 5), (7, 7)]
+    pool_c = {}
+    q_c = d["q"].cpu()
+    bt_c = d["block_table"].cpu()
+    sel_o_all = sel.clone()
+    refs = {}
+    for (b, h) in units:
+        _, J, Jc = gg.lens(wl, b)
+        idx = bt_c[b, :Jc].long().to(gg.DEV)
+        rec = pool[idx, h].cpu()
+        mu, vt, cf = (gg.f64(x) for x in L.split_records(cfg, rec))
+        s_o = oracle.page_scores(gg.f64(q_c[b, h * 4:(h + 1) * 4]), mu, vt, cf, wl.softmax_scale)
+        got = gg.f64(hs[b, h * 4:(h + 1) * 4, :Jc].cpu())
+        assert gg.mixed_violation(got, s_o) <= 1.0
+        sel_o, sigma_o = gg.oracle_unit_select(wl, b, s_o)
+        gg.check_selection(wl, b, sel[b, h].tolist(), sel_o.tolist(), sigma_o)
+        sel_o_all[b, h] = torch.from_numpy(sel_o).to(gg.DEV)
+        refs[(b, h)] = sel_o
+    out, _ = gg.gpu_decode(wl, cfg, d, sel_o_all)
+    torch.cuda.synchronize()
+    out = gg.f64(out.cpu())
+    for (b, h), sel_o in refs.items():
+        T, _, _ = gg.lens(wl, b)
+        ks, vs = [], []
+        for j in sel_o:
+            blk = int(bt_c[b, j])
+            ks.append(gg.f64(d["k_pool"][blk, h].cpu()))
+            vs.append(gg.f64(d["v_pool"][blk, h].cpu()))
+        o_ref, _ = oracle.attend(gg.f64(q_c[b, h * 4:(h + 1) * 4]), np.concatenate(ks),
+                                 np.concatenate(vs), wl.softmax_scale)
+        assert np.max(np.abs(out[b, h * 4:(h + 1) * 4] - o_ref)) <= gg.out_tol(wl)
+    # build at full size: every page of every unit, a sample checked against the oracle
+    ids = d["block_table"].reshape(-1).contiguous()
+    pool2 = L.summary_pool_for(cfg, wl.num_blocks, gg.DEV)
+    L.locks_build_summaries(cfg, d["k_pool"], wl.num_blocks, ids, ids.numel(), pool2)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    sample = [(int(bt_c[b, j]), int(h)) for b, j, h in zip(rng.integers(0, 8, 12),
+                                                            rng.integers(0, 2048, 12),
+                                                            rng.integers(0, 8, 12))]
+    keys = np.stack([gg.f64(d["k_pool"][blk, h].cpu()) for blk, h in sample])
+    mu_o, vt_o, cf_o, ev, _ = oracle.build_pages(keys, wl.rank)
+    rec = pool2.cpu()
+    mu_g, vt_g, cf_g = L.split_records(cfg, rec)
+    for i, (blk, h) in enumerate(sample):
+        D = keys[i] - mu_o[i]
+        vt = gg.f64(vt_g[blk, h])
+        tau = float(np.sum(np.clip(ev[i, wl.rank:], 0, None)))
+        resid = float(np.linalg.norm(D - D @ vt.T @ vt) ** 2)
+        assert resid <= tau + 2e-2 * float(np.sum(np.clip(ev[i], 0, None)))
+        # the signal subspace (well separated) matches
+        gap = (ev[i, 5] - ev[i, 6]) / ev[i, 5]
+        if gap > 0.2:
+            p6g = vt.T @ vt
+            p6o = vt_o[i, :6].T @ vt_o[i, :6]
+            assert np.linalg.norm(p6o @ p6g @ p6o - p6o) <= 5e-2
