@@ -31,10 +31,16 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-fno-gpu-rdc",
          "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include")]
 
 
+# Kernel sources only (not the host validation in locks_api.cpp): no NaN
+# operands reach the reductions, which lets max fuse with DPP lane moves.
+# Infinities stay honoured (-inf marks masked logits and empty pages).
+KERNEL_FLAGS = ["-fno-honor-nans"]
+
+
 def _compile(src: str) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + KERNEL_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

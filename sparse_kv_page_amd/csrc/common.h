@@ -56,6 +56,74 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// ---- cross-lane helpers (DPP inside a 16-lane row, LDS permute across rows) ----
+// DPP controls: quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// All-reduce (max or sum) over aligned groups of N lanes, N in {1,2,4,8,16,32,64}.
+// Every lane of a group ends with the group's result.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (N >= 2) v = fmaxf(v, dpp_f<kDppXor1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp_f<kDppXor2>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp_f<kDppMirror>(v));
+  if constexpr (N >= 32) v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  if constexpr (N >= 64) v = fmaxf(v, __shfl_xor(v, 32, kWave));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp_f<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f<kDppMirror>(v);
+  if constexpr (N >= 32) v += __shfl_xor(v, 16, kWave);
+  if constexpr (N >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// Streaming (non-temporal) loads: data read once per step bypasses cache reuse.
+__device__ __forceinline__ u32x4_t ld_nt4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ u32x2_t ld_nt2(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
+__device__ __forceinline__ uint32_t ld_nt1(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+// NW 32-bit words from a 4*NW-byte block aligned to min(16, 4*NW) bytes.
+template <int NW>
+__device__ __forceinline__ void ld_nt_words(const void* p, uint32_t* w) {
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(p);
+  if constexpr (NW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const u32x4_t v = ld_nt4(b + 16 * i);
+      w[4 * i] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
+    }
+  } else if constexpr (NW % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < NW / 2; ++i) {
+      const u32x2_t v = ld_nt2(b + 8 * i);
+      w[2 * i] = v[0]; w[2 * i + 1] = v[1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = ld_nt1(b + 4 * i);
+  }
+}
+
 // Order-preserving map of a float onto uint32 (larger float -> larger key);
 // NaN maps below -inf so it is never preferred.
 __device__ __forceinline__ uint32_t float_key(float f) {
