@@ -98,7 +98,7 @@ def main():
     out = torch.empty((B, Hq, d), dtype=synth.torch_dtype(wl.kv_dtype), device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     ws_bytes = L.locks_workspace_size(cfg, B, maxp)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     scores = torch.empty((B, Hq, maxp), dtype=torch.float32, device=dev)
     sigma = torch.empty((B, Hkv, maxp), dtype=torch.float32, device=dev)
 

@@ -86,7 +86,11 @@ size_t locks_summary_record_bytes(const locks_config_t* cfg);
 
 /* Workspace bytes needed by locks_score_select and locks_sparse_decode for a
  * batch of `batch` sequences of at most `max_pages` pages (one buffer of
- * this size serves both calls). Writes *bytes; returns a status. */
+ * this size serves both calls). Writes *bytes; returns a status.
+ * The workspace must be zero-filled once before its first use: its first
+ * bytes hold per-(sequence, KV head) arrival counters of the decode split
+ * merge, which every locks_sparse_decode call returns to zero. Calls that
+ * share a workspace must not overlap in time (same stream, or synchronised). */
 int locks_workspace_size(const locks_config_t* cfg, int32_t batch, int32_t max_pages,
                          size_t* bytes);
 

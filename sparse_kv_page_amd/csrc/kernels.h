@@ -25,6 +25,7 @@ struct SelectArgs {
   int32_t* selected;          // [B][Hkv][k]
   float* sigma;               // [B][Hkv][max_pages]
   int Hkv, G, P, k, max_pages;
+  int idbits;                 // bits that hold any page id < max_pages (>= 1)
 };
 
 struct DecodeArgs {
@@ -34,8 +35,9 @@ struct DecodeArgs {
   const int32_t* block_table; // [B][max_pages]
   const int32_t* seq_lens;    // [B]
   const int32_t* selected;    // [B][Hkv][k]
-  float* part_o;              // [B][Hq][splits][D]
-  float* part_lse;            // [B][Hq][splits]
+  float* part_o;              // [B][Hkv][splits][G][D]
+  float* part_lse;            // [B][Hkv][splits][G]
+  int32_t* counters;          // [B][Hkv] arrival counters, zero between calls
   void* out;                  // [B][Hq][D] kv dtype
   float* lse;                 // [B][Hq] or null
   int64_t num_blocks;
@@ -56,6 +58,7 @@ struct BuildArgs {
 hipError_t launch_page_score(const ScoreArgs& a, int dtype, int D, int batch, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s);
 hipError_t launch_sparse_decode(const DecodeArgs& a, int dtype, int D, int batch, hipStream_t s);
+int decode_pages_per_split(int page_size);
 hipError_t launch_build(const BuildArgs& a, int dtype, int D, hipStream_t s);
 
 }  // namespace locks

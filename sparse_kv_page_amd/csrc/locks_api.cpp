@@ -11,7 +11,6 @@
 namespace {
 
 constexpr int kMaxK = 1024;
-constexpr int kDecodePagesPerSplit = 4;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -50,30 +49,34 @@ int64_t rec_elems(const locks_config_t* c) {
   return (int64_t)c->head_dim * (1 + c->rank) + (int64_t)c->page_size * c->rank;
 }
 
+// Workspace layout: [decode arrival counters, one int32 per (sequence, KV
+// head), zero between calls] then a region shared by the two stages: the
+// head scores and page keys of score/select, or the split partials of decode.
+size_t counter_bytes(const locks_config_t* c, int32_t batch) {
+  return align_up((size_t)batch * c->num_kv_heads * sizeof(int32_t));
+}
+
 size_t score_ws_bytes(const locks_config_t* c, int32_t batch, int32_t max_pages) {
   const size_t scores = (size_t)batch * c->num_q_heads * max_pages * sizeof(float);
   const size_t sigma = (size_t)batch * c->num_kv_heads * max_pages * sizeof(float);
-  return align_up(scores) + align_up(sigma);
+  return counter_bytes(c, batch) + align_up(scores) + align_up(sigma);
 }
 
+int decode_pages_per_split(const locks_config_t* c) { return locks::decode_pages_per_split(c->page_size); }
+
 int decode_splits(const locks_config_t* c) {
-  return (c->budget_pages + kDecodePagesPerSplit - 1) / kDecodePagesPerSplit;
+  const int pps = decode_pages_per_split(c);
+  return (c->budget_pages + pps - 1) / pps;
 }
 
 size_t decode_ws_bytes(const locks_config_t* c, int32_t batch) {
   const size_t rows = (size_t)batch * c->num_q_heads * decode_splits(c);
-  return align_up(rows * c->head_dim * sizeof(float)) + align_up(rows * sizeof(float));
+  return counter_bytes(c, batch) + align_up(rows * c->head_dim * sizeof(float)) +
+         align_up(rows * sizeof(float));
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LOCKS_OK : LOCKS_E_HIP; }
 
-int pages_per_wave(int32_t batch, int hkv, int32_t max_pages) {
-  const int64_t total = (int64_t)batch * hkv * max_pages;
-  int64_t ppw = (total + 2048 * 4 - 1) / (2048 * 4);
-  if (ppw < 1) ppw = 1;
-  if (ppw > 64) ppw = 64;
-  return (int)ppw;
-}
 
 }  // namespace
 
@@ -154,7 +157,6 @@ int locks_page_score(const locks_config_t* cfg, const void* q, const void* summa
   a.P = cfg->page_size;
   a.r = cfg->rank;
   a.max_pages = max_pages;
-  a.ppw = pages_per_wave(batch, a.Hkv, max_pages);
   a.scale = cfg->softmax_scale;
   return hip_status(locks::launch_page_score(a, cfg->kv_dtype, cfg->head_dim, batch, stream));
 }
@@ -178,6 +180,8 @@ int locks_select_pages(const locks_config_t* cfg, const float* head_scores, cons
   a.P = cfg->page_size;
   a.k = cfg->budget_pages;
   a.max_pages = max_pages;
+  a.idbits = 1;
+  while (a.idbits < 31 && (int64_t(1) << a.idbits) < max_pages) ++a.idbits;
   return hip_status(locks::launch_select(a, batch, stream));
 }
 
@@ -193,8 +197,9 @@ int locks_score_select(const locks_config_t* cfg, const void* q, const void* sum
   if (batch == 0) return LOCKS_OK;
   if (!q || !summary_pool || !block_table || !seq_lens || !selected) return LOCKS_E_INVALID_ARG;
   if (!ws || ws_bytes < score_ws_bytes(cfg, batch, max_pages)) return LOCKS_E_WORKSPACE;
-  float* scores = static_cast<float*>(ws);
-  float* sigma = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+  uint8_t* region = static_cast<uint8_t*>(ws) + counter_bytes(cfg, batch);
+  float* scores = reinterpret_cast<float*>(region);
+  float* sigma = reinterpret_cast<float*>(region +
                                           align_up((size_t)batch * cfg->num_q_heads * max_pages * sizeof(float)));
   st = locks_page_score(cfg, q, summary_pool, num_blocks, block_table, seq_lens, batch, max_pages,
                         scores, stream);
@@ -225,9 +230,10 @@ int locks_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.selected = selected;
-  a.part_o = static_cast<float*>(ws);
-  a.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
-                                        align_up(rows * cfg->head_dim * sizeof(float)));
+  uint8_t* region = static_cast<uint8_t*>(ws) + counter_bytes(cfg, batch);
+  a.counters = static_cast<int32_t*>(ws);
+  a.part_o = reinterpret_cast<float*>(region);
+  a.part_lse = reinterpret_cast<float*>(region + align_up(rows * cfg->head_dim * sizeof(float)));
   a.out = out;
   a.lse = lse;
   a.num_blocks = num_blocks;
@@ -236,7 +242,7 @@ int locks_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_
   a.P = cfg->page_size;
   a.k = cfg->budget_pages;
   a.max_pages = max_pages;
-  a.pages_per_split = kDecodePagesPerSplit;
+  a.pages_per_split = decode_pages_per_split(cfg);
   a.splits = splits;
   a.scale = cfg->softmax_scale;
   return hip_status(locks::launch_sparse_decode(a, cfg->kv_dtype, cfg->head_dim, batch, stream));

@@ -331,14 +331,16 @@ __global__ __launch_bounds__(256, 2) void page_score_lds_kernel(ScoreArgs a) {
   const int b = blockIdx.z;
   const int h = blockIdx.y;
   const int Hq = a.Hkv * G;
+  const int p0 = __builtin_amdgcn_readfirstlane((blockIdx.x * kScoreWaves + wave) * a.ppw);
+  if (p0 >= a.max_pages) return;
+  // block ids are loaded before the length is known (entries up to max_pages
+  // are addressable), so the two loads are in flight together
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+  int my_bid = lane < a.ppw && p0 + lane < a.max_pages ? bt_row[p0 + lane] : -1;
   const int T_b = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.max_pages, P));
   const int Jc = T_b / P;
-  const int p0 = __builtin_amdgcn_readfirstlane((blockIdx.x * kScoreWaves + wave) * a.ppw);
   if (p0 >= Jc) return;
   const int np = min(a.ppw, Jc - p0);
-
-  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
-  int my_bid = lane < np ? bt_row[p0 + lane] : -1;
 
   const int n = lane & 15;
   const int kg = lane >> 4;

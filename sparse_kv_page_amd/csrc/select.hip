@@ -1,48 +1,106 @@
 // (a3 + a4) Share-average combine and top-(k-2) page selection, [Locks] §2, §4.
 //
-// One workgroup per (sequence, KV head). From the per-head page scores s_g(j)
-// of the Jc complete pages:
+// One workgroup (1024 threads) per (sequence, KV head). From the per-head page
+// scores s_g(j) of the Jc complete pages:
 //   log Z_g  = log sum_j exp(s_g(j))
 //   sigma_j  = log((1/G) sum_g exp(s_g(j) - log Z_g))   (log of the share average)
 // Pages 0 (sink) and J-1 (current) are always kept; the other k-2 slots take
 // the largest sigma among the remaining complete pages, ties to the lower
-// page id. The ranking runs as a radix select over 64-bit keys
-// (order-preserving image of sigma, then the complemented page id) with 8-bit
-// digits and an LDS histogram, most significant digit first; it stops as soon
-// as the bucket holding the k-2'th key is taken whole.
+// page id.
+//
+// Scores are read once: thread t keeps pages t, t + 1024, ... (up to NPT of
+// them) in registers for both the normaliser and sigma. A generic variant
+// (NPT = 0) loops over global memory for longer contexts.
+//
+// Ranking: every candidate gets the composite key
+//   key(j) = (order-preserving image of sigma_j) << idbits | (2^idbits - 1 - j)
+// which is unique and orders by (sigma desc, id asc). The bits above the
+// highest bit in which two candidates differ are common and skipped; the rest
+// is radix-selected with 11-bit digits (2048-bin LDS histogram, most
+// significant digit first), stopping as soon as the bin holding the K-th key
+// is taken whole. The chosen pages are written in ascending order by a
+// block-wide scan over page flags.
 #include "common.h"
 #include "kernels.h"
 
 namespace locks {
 
-constexpr int kSelThreads = 256;
-constexpr int kSelMaxK = 1024;
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelLdsKeys = 16384;  // sigma keys kept in LDS up to this many pages
+constexpr int kSelBins = 2048;
+constexpr int kSelDigit = 11;
 
 namespace {
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+template <typename F>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, F op) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = op(v, (uint32_t)__shfl_xor((int)v, o, 64));
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+
+// inclusive scan over the wave
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(v, o, 64);
+    if (lane >= o) v += x;
+  }
   return v;
+}
+
+// exclusive scan over the block; `tot` receives the block total (2 barriers)
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int inc = wave_incl_scan(v, lane);
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int x = wsum[w];
+    before += w < wave ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  return before + inc - v;
+}
+
+// block-wide max / sum of up to 8 per-head values; every thread gets the result
+template <bool kMax>
+__device__ __forceinline__ void block_reduce_heads(float* v, int G, float (*red)[8], float* out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (g < G) {
+      const float r = kMax ? group_max<64>(v[g]) : group_sum<64>(v[g]);
+      if (lane == 0) red[wave][g] = r;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < G) {
+    float r = red[0][threadIdx.x];
+    for (int w = 1; w < kSelWaves; ++w) r = kMax ? fmaxf(r, red[w][threadIdx.x]) : r + red[w][threadIdx.x];
+    out[threadIdx.x] = r;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < 8; ++g) v[g] = g < G ? out[g] : 0.f;
 }
 
 }  // namespace
 
+template <int NPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
-  extern __shared__ uint32_t keys_lds[];
-  __shared__ float red[kSelThreads / 64][8];
-  __shared__ float logz_s[8];
-  __shared__ float mx_s[8];
-  __shared__ uint32_t hist[256];
-  __shared__ int32_t list[kSelMaxK];
-  __shared__ int list_n;
-  __shared__ uint32_t dig_s;
-  __shared__ int kr_s;
-  __shared__ int done_s;
+  __shared__ uint32_t keys_lds[kSelLdsKeys];
+  __shared__ uint32_t hist[2][kSelBins];
+  __shared__ float red[kSelWaves][8];
+  __shared__ float hv[8];
+  __shared__ uint32_t redu[kSelWaves][2];
+  __shared__ int wsum[kSelWaves];
+  __shared__ int pick_s[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -50,7 +108,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int P = a.P, G = a.G, k = a.k;
-  const int T = clamp_len(a.seq_lens[b], a.max_pages, P);
+  const float* srow = a.scores + ((int64_t)b * a.Hkv * G + (int64_t)h * G) * a.max_pages;
+  // the register path loads its scores before the length is known (pages up
+  // to max_pages are addressable), so both loads are in flight together
+  constexpr int kRegs = NPT > 0 ? NPT : 1;
+  float sc[kRegs][8];
+  if constexpr (NPT > 0) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int j = tid + kSelThreads * i;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) sc[i][g] = (g < G && j < a.max_pages) ? srow[(int64_t)g * a.max_pages + j] : 0.f;
+    }
+  }
+  const int T = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.max_pages, P));
   const int J = (T + P - 1) / P;
   const int Jc = T / P;
   int32_t* sel_row = a.selected + ((int64_t)b * a.Hkv + h) * k;
@@ -60,68 +131,64 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     return;
   }
 
-  const float* srow = a.scores + ((int64_t)b * a.Hkv * G + (int64_t)h * G) * a.max_pages;
   float* sig_row = a.sigma + ((int64_t)b * a.Hkv + h) * a.max_pages;
   const bool keys_in_lds = Jc <= kSelLdsKeys;
   uint32_t* keys = keys_in_lds ? keys_lds : reinterpret_cast<uint32_t*>(sig_row);
+  auto is_cand = [&](int j) { return j >= 1 && j < Jc && j != J - 1; };
+  for (int x = tid; x < kSelBins; x += kSelThreads) hist[0][x] = 0;
 
   // ---- per-head normaliser log Z_g ----
-  float mx[8], sm[8];
+  float mx[8];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) { mx[g] = -INFINITY; sm[g] = 0.f; }
-  for (int j = tid; j < Jc; j += kSelThreads)
+  for (int g = 0; g < 8; ++g) mx[g] = -INFINITY;
+  if constexpr (NPT > 0) {
 #pragma unroll
-    for (int g = 0; g < 8; ++g)
-      if (g < G) mx[g] = fmaxf(mx[g], srow[(int64_t)g * a.max_pages + j]);
+    for (int i = 0; i < NPT; ++i) {
+      const int j = tid + kSelThreads * i;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    if (g < G) {
-      float v = wave_max(mx[g]);
-      if (lane == 0) red[wave][g] = v;
+      for (int g = 0; g < 8; ++g) {
+        if (!(g < G && j < Jc)) sc[i][g] = -INFINITY;
+        mx[g] = fmaxf(mx[g], sc[i][g]);
+      }
     }
-  }
-  __syncthreads();
-  if (tid < G) {
-    float v = red[0][tid];
-    for (int w = 1; w < kSelThreads / 64; ++w) v = fmaxf(v, red[w][tid]);
-    mx_s[tid] = v;
-  }
-  __syncthreads();
+  } else {
+    for (int j = tid; j < Jc; j += kSelThreads)
 #pragma unroll
-  for (int g = 0; g < 8; ++g) mx[g] = g < G ? mx_s[g] : -INFINITY;
-  for (int j = tid; j < Jc; j += kSelThreads)
-#pragma unroll
-    for (int g = 0; g < 8; ++g)
-      if (g < G && mx[g] > -INFINITY)
-        sm[g] += exp2_fast((srow[(int64_t)g * a.max_pages + j] - mx[g]) * kLog2e);
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    if (g < G) {
-      float v = wave_sum(sm[g]);
-      if (lane == 0) red[wave][g] = v;
-    }
+      for (int g = 0; g < 8; ++g)
+        if (g < G) mx[g] = fmaxf(mx[g], srow[(int64_t)g * a.max_pages + j]);
   }
-  __syncthreads();
-  if (tid < G) {
-    float v = 0.f;
-    for (int w = 0; w < kSelThreads / 64; ++w) v += red[w][tid];
-    logz_s[tid] = mx_s[tid] > -INFINITY ? mx_s[tid] + log2_fast(v) * kLn2 : -INFINITY;
+  block_reduce_heads<true>(mx, G, red, hv);
+  float sm[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) sm[g] = 0.f;
+  if constexpr (NPT > 0) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i)
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        if (g < G && mx[g] > -INFINITY) sm[g] += exp2_fast((sc[i][g] - mx[g]) * kLog2e);
+  } else {
+    for (int j = tid; j < Jc; j += kSelThreads)
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        if (g < G && mx[g] > -INFINITY) sm[g] += exp2_fast((srow[(int64_t)g * a.max_pages + j] - mx[g]) * kLog2e);
   }
-  __syncthreads();
-
-  // ---- sigma_j = log of the share average, and its sortable key ----
+  block_reduce_heads<false>(sm, G, red, hv);
   float lz[8];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) lz[g] = g < G ? logz_s[g] : 0.f;
+  for (int g = 0; g < 8; ++g) lz[g] = (g < G && mx[g] > -INFINITY) ? mx[g] + log2_fast(sm[g]) * kLn2 : -INFINITY;
+
+  // ---- sigma_j, its sortable key, and the spread of candidate keys ----
   const float log2G = log2_fast((float)G);
-  for (int j = tid; j < Jc; j += kSelThreads) {
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+  auto sigma_key = [&](int j, const float* sv) {
     float tg[8];
     float m = -INFINITY;
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       tg[g] = -INFINITY;
       if (g < G && lz[g] > -INFINITY) {
-        tg[g] = (srow[(int64_t)g * a.max_pages + j] - lz[g]) * kLog2e;
+        tg[g] = (sv[g] - lz[g]) * kLog2e;
         m = fmaxf(m, tg[g]);
       }
     }
@@ -137,94 +204,121 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     } else {
       sig_row[j] = __uint_as_float(key);  // global scratch holds the key; rewritten below
     }
+    if (is_cand(j)) {
+      kmax = key > kmax ? key : kmax;
+      kmin = key < kmin ? key : kmin;
+    }
+  };
+  if constexpr (NPT > 0) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int j = tid + kSelThreads * i;
+      if (j < Jc) sigma_key(j, sc[i]);
+    }
+  } else {
+    for (int j = tid; j < Jc; j += kSelThreads) {
+      float sv[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) sv[g] = g < G ? srow[(int64_t)g * a.max_pages + j] : 0.f;
+      sigma_key(j, sv);
+    }
   }
-  if (tid == 0) list_n = 0;
-  __syncthreads();
+  kmax = wave_reduce_u32(kmax, [](uint32_t p, uint32_t q) { return p > q ? p : q; });
+  kmin = wave_reduce_u32(kmin, [](uint32_t p, uint32_t q) { return p < q ? p : q; });
+  if (lane == 0) { redu[wave][0] = kmax; redu[wave][1] = kmin; }
+  __syncthreads();  // also publishes keys[] and the cleared hist[0]
+  kmax = redu[0][0];
+  kmin = redu[0][1];
+#pragma unroll
+  for (int w = 1; w < kSelWaves; ++w) {
+    kmax = redu[w][0] > kmax ? redu[w][0] : kmax;
+    kmin = redu[w][1] < kmin ? redu[w][1] : kmin;
+  }
 
-  // ---- radix select of the top K candidates ----
+  // ---- radix select of the K best candidates ----
   int ncand = Jc - 1 - ((J - 1 >= 1 && J - 1 < Jc) ? 1 : 0);
   if (ncand < 0) ncand = 0;
   const int K = min(k - 2, ncand);
-  auto is_cand = [&](int j) { return j >= 1 && j < Jc && j != J - 1; };
-  auto key64 = [&](int j) -> uint64_t {
-    return ((uint64_t)keys[j] << 32) | (uint64_t)(0xffffffffu - (uint32_t)j);
-  };
+  const int idb = a.idbits;
+  const uint64_t idmask = ((uint64_t)1 << idb) - 1;
+  auto key64 = [&](int j) -> uint64_t { return ((uint64_t)keys[j] << idb) | (idmask - (uint64_t)j); };
 
-  uint64_t prefix = 0;
-  int shift = 64;
+  // highest bit in which two candidate keys can differ: within sigma's key
+  // when the keys differ, else within the page id
+  int hi = kmax != kmin ? idb + 32 - __builtin_clz(kmax ^ kmin) : idb;
+  // common bits above `hi` (taken from the largest key)
+  uint64_t prefix = (((uint64_t)kmax << idb) >> hi) << hi;
   int kr = K;
-  if (K > 0) {
-    for (int pass = 0; pass < 8; ++pass) {
-      shift -= 8;
-      for (int x = tid; x < 256; x += kSelThreads) hist[x] = 0;
-      __syncthreads();
-      for (int j = tid; j < Jc; j += kSelThreads) {
-        if (!is_cand(j)) continue;
-        const uint64_t kv = key64(j);
-        if (pass > 0 && (kv >> (shift + 8)) != (prefix >> (shift + 8))) continue;
-        atomicAdd(&hist[(uint32_t)(kv >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (wave == 0) {
-        const uint32_t c0 = hist[4 * lane + 0], c1 = hist[4 * lane + 1];
-        const uint32_t c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
-        const int cs = (int)(c0 + c1 + c2 + c3);
-        int S = cs;  // inclusive suffix sum over lanes >= lane
-        for (int o = 1; o < 64; o <<= 1) {
-          const int v = __shfl_down(S, o, 64);
-          if (lane + o < 64) S += v;
-        }
-        const uint64_t bal = __ballot(S >= kr);
-        const int L = 63 - __builtin_clzll(bal);
-        if (lane == L) {
-          int above = S - cs;
-          int dsel, cnt;
-          if (above + (int)c3 >= kr) {
-            dsel = 4 * lane + 3; cnt = (int)c3;
-          } else if (above + (int)(c3 + c2) >= kr) {
-            above += (int)c3; dsel = 4 * lane + 2; cnt = (int)c2;
-          } else if (above + (int)(c3 + c2 + c1) >= kr) {
-            above += (int)(c3 + c2); dsel = 4 * lane + 1; cnt = (int)c1;
-          } else {
-            above += (int)(c3 + c2 + c1); dsel = 4 * lane; cnt = (int)c0;
-          }
-          dig_s = (uint32_t)dsel;
-          kr_s = kr - above;
-          done_s = (cnt == kr - above) ? 1 : 0;
-        }
-      }
-      __syncthreads();
-      prefix |= (uint64_t)dig_s << shift;
-      kr = kr_s;
-      const int done = done_s;
-      __syncthreads();
-      if (done) break;
+  const bool take_all = K >= ncand;  // every candidate fits
+  int cur = 0;
+  while (!take_all && hi > 0) {
+    const int lo = hi > kSelDigit ? hi - kSelDigit : 0;
+    const uint32_t dmask = (1u << (hi - lo)) - 1u;
+    uint32_t* hc = hist[cur];
+    for (int j = tid; j < Jc; j += kSelThreads) {
+      if (!is_cand(j)) continue;
+      const uint64_t kv = key64(j);
+      if ((kv >> hi) != (prefix >> hi)) continue;
+      atomicAdd(&hc[(uint32_t)(kv >> lo) & dmask], 1u);
     }
+    __syncthreads();
+    // bins in descending order, kPer per thread; the next pass's buffer is
+    // cleared meanwhile
+    constexpr int kPer = kSelBins / kSelThreads;
+    const int top = kSelBins - 1 - tid * kPer;
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) local += (int)hc[top - i];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) hist[cur ^ 1][top - i] = 0;
+    int tot;
+    const int before = block_excl_scan(local, wsum, tot);
+    if (before < kr && before + local >= kr) {
+      int acc = before;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int c = (int)hc[top - i];
+        if (acc + c >= kr) {
+          pick_s[0] = top - i;
+          pick_s[1] = kr - acc;  // still needed from this bin
+          pick_s[2] = c;
+          break;
+        }
+        acc += c;
+      }
+    }
+    __syncthreads();
+    const int dsel = pick_s[0];
+    const int need = pick_s[1];
+    const int cnt = pick_s[2];
+    prefix |= (uint64_t)dsel << lo;
+    hi = lo;
+    kr = need;
+    cur ^= 1;
+    if (cnt == need) break;  // the whole bin is taken
   }
 
-  // ---- gather the chosen ids, then place them in ascending order ----
-  for (int j = tid; j < Jc; j += kSelThreads) {
-    if (K > 0 && is_cand(j) && (key64(j) >> shift) >= (prefix >> shift)) {
-      const int pos = atomicAdd(&list_n, 1);
-      if (pos < kSelMaxK) list[pos] = j;
+  // ---- ascending output: sink, current and the chosen candidates ----
+  auto chosen = [&](int j) -> bool {
+    if (j == 0 || j == J - 1) return true;
+    if (!is_cand(j) || K == 0) return false;
+    if (take_all) return true;
+    return (key64(j) >> hi) >= (prefix >> hi);
+  };
+  const int ppt = (J + kSelThreads - 1) / kSelThreads;
+  const int j0 = tid * ppt;
+  const int j1 = min(J, j0 + ppt);
+  int cnt = 0;
+  for (int j = j0; j < j1; ++j) cnt += chosen(j) ? 1 : 0;
+  int total;
+  int pos = block_excl_scan(cnt, wsum, total);
+  for (int j = j0; j < j1; ++j) {
+    if (chosen(j)) {
+      if (pos < k) sel_row[pos] = j;
+      ++pos;
     }
   }
-  __syncthreads();
-  if (tid == 0) {
-    const int n0 = list_n;
-    list[n0] = 0;
-    list[n0 + 1] = J - 1;
-    list_n = n0 + 2;
-  }
-  __syncthreads();
-  const int nl = list_n;
-  for (int t = tid; t < nl; t += kSelThreads) {
-    const int v = list[t];
-    int rank = 0;
-    for (int x = 0; x < nl; ++x) rank += list[x] < v ? 1 : 0;
-    if (rank < k) sel_row[rank] = v;
-  }
-  for (int t = nl + tid; t < k; t += kSelThreads) sel_row[t] = -1;
+  for (int t = total + tid; t < k; t += kSelThreads) sel_row[t] = -1;
 
   // when the keys lived in the global scratch, leave sigma there as documented
   if (!keys_in_lds) {
@@ -238,9 +332,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 }
 
 hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t stream) {
-  const int lds_keys = a.max_pages < kSelLdsKeys ? a.max_pages : kSelLdsKeys;
   dim3 grid(a.Hkv, batch);
-  hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), (size_t)lds_keys * 4, stream, a);
+  if (a.max_pages <= 2 * kSelThreads)
+    hipLaunchKernelGGL(select_kernel<2>, grid, dim3(kSelThreads), 0, stream, a);
+  else if (a.max_pages <= 8 * kSelThreads)
+    hipLaunchKernelGGL(select_kernel<8>, grid, dim3(kSelThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(select_kernel<0>, grid, dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -135,7 +135,7 @@ def gpu_decode(wl, cfg, g, sel):
     out = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), float("nan"), dtype=dt, device=DEV)
     lse = torch.full((wl.batch, wl.num_q_heads), float("nan"), device=DEV)
     nbytes = L.locks_workspace_size(cfg, wl.batch, wl.max_pages)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=DEV)
     L.locks_sparse_decode(cfg, g["q"], g["k_pool"], g["v_pool"], wl.num_blocks, g["block_table"],
                           g["seq_lens"], sel, wl.batch, wl.max_pages, out, lse, ws, nbytes)
     return out, lse
@@ -144,7 +144,7 @@ def gpu_decode(wl, cfg, g, sel):
 def gpu_score_select(wl, cfg, g, pool):
     sel = torch.full((wl.batch, wl.num_kv_heads, wl.budget_pages), -7, dtype=torch.int32, device=DEV)
     nbytes = L.locks_workspace_size(cfg, wl.batch, wl.max_pages)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=DEV)
     L.locks_score_select(cfg, g["q"], pool, wl.num_blocks, g["block_table"], g["seq_lens"], wl.batch,
                          wl.max_pages, sel, ws, nbytes)
     return sel
