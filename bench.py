@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run 3 plain device copies of MIB MiB "
+                         "(reference dispatches for scaling memory counters)")
     return ap.parse_args()
 
 
@@ -102,10 +105,21 @@ def main():
     scores = torch.empty((B, Hq, maxp), dtype=torch.float32, device=dev)
     sigma = torch.empty((B, Hkv, maxp), dtype=torch.float32, device=dev)
 
-    def step():
-        L.locks_score_select(cfg, q, pool, wl.num_blocks, bt, sl, B, maxp, sel, ws, ws_bytes)
+    def score():
+        L.locks_page_score(cfg, q, pool, wl.num_blocks, bt, sl, B, maxp, scores)
+
+    def select():
+        L.locks_select_pages(cfg, scores, sl, B, maxp, sel, sigma)
+
+    def decode():
         L.locks_sparse_decode(cfg, q, kp, vp, wl.num_blocks, bt, sl, sel, B, maxp, out, lse, ws,
                               ws_bytes)
+
+    def step():
+        # page scoring -> combine + selection -> sparse decode, on torch's stream
+        score()
+        select()
+        decode()
 
     for _ in range(args.warmup):
         step()
@@ -123,26 +137,32 @@ def main():
     wall1 = time.perf_counter()
     step_ms = t0.elapsed_time(t1) / args.steps
 
-    # ---- per-stage timing with events on the launch stream ----
-    names = ("build_step", "page_score", "select", "sparse_decode")
-    acc = {n: 0.0 for n in names}
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    for it in range(args.steps):
-        ev[0].record()
-        if n_step:
-            L.locks_build_summaries(cfg, kp, wl.num_blocks, step_ids, n_step, pool)
-        ev[1].record()
-        L.locks_page_score(cfg, q, pool, wl.num_blocks, bt, sl, B, maxp, scores)
-        ev[2].record()
-        L.locks_select_pages(cfg, scores, sl, B, maxp, sel, sigma)
-        ev[3].record()
-        L.locks_sparse_decode(cfg, q, kp, vp, wl.num_blocks, bt, sl, sel, B, maxp, out, lse, ws,
-                              ws_bytes)
-        ev[4].record()
+    # ---- per-kernel launch time: K back-to-back launches of each kernel on the
+    # same stream and inputs, bracketed by HIP events ----
+    stage_us = {}
+    for name, fn in (("page_score", score), ("select", select), ("sparse_decode", decode)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
         torch.cuda.synchronize()
-        for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1])
-    stage_us = {n: 1e3 * acc[n] / args.steps for n in names}
+        stage_us[name] = 1e3 * e0.elapsed_time(e1) / args.steps
+
+    # ---- summary build of the pages that complete in a step (off the decode path) ----
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    build_ms = 0.0
+    if n_step:
+        for _ in range(3):
+            L.locks_build_summaries(cfg, kp, wl.num_blocks, step_ids, n_step, pool)
+        b0.record()
+        for _ in range(args.steps):
+            L.locks_build_summaries(cfg, kp, wl.num_blocks, step_ids, n_step, pool)
+        b1.record()
+        torch.cuda.synchronize()
+        build_ms = b0.elapsed_time(b1) / args.steps
+    stage_us["build_step"] = 1e3 * build_ms
 
     # ---- algorithmic bytes (what the method must move per step) ----
     summary_bytes = 0
@@ -158,10 +178,18 @@ def main():
             A = (k - 1) * P + (T - (J - 1) * P)
         kv_bytes += Hkv * A * 2 * d * ekv
     step_bytes = summary_bytes + kv_bytes
-    score_gbs = summary_bytes / (stage_us["page_score"] * 1e-6) / 1e9
     step_gbs = step_bytes / (step_ms * 1e-3) / 1e9
     gram_flops = 2.0 * P * d * d * n_full * Hkv
     build_tflops = gram_flops / (prefill_build_ms * 1e-3) / 1e12
+
+    if args.copy_calibration > 0:
+        nb = args.copy_calibration << 20
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- CPU oracle on a bounded sample of the same step ----
     cpu = None
@@ -188,10 +216,7 @@ def main():
         "hbm_roofline_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": step_bytes,
         "step_achieved_GBps": round(step_gbs, 1),
-        "roofline": {"bound": "hbm", "kernel": "page_score", "achieved": round(score_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": summary_bytes,
-                     "avg_launch_us": round(stage_us["page_score"], 3)},
+        "roofline": roofline("page_score", wl.name, summary_bytes, stage_us["page_score"]),
         "stages_us": {n: round(v, 3) for n, v in stage_us.items()},
         "step_with_build_us": round(step_ms * 1e3 + stage_us["build_step"], 3),
         "build": {"pages_per_step": int(n_step) * Hkv, "step_build_us": round(stage_us["build_step"], 3),
@@ -202,6 +227,43 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def _sha1(paths):
+    import hashlib
+    h = hashlib.sha1()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def roofline(kernel, workload, alg_bytes, avg_us):
+    """Roofline record of one kernel: algorithmic bytes per launch over its
+    average launch time (HIP events in the timed region), against the HBM
+    peak. `traffic` is the measured memory traffic per launch from the
+    committed counter record of this workload (FETCH_SIZE + WRITE_SIZE, each
+    scaled by a plain copy of known size), and null when that record is
+    missing or was taken from a different version of the kernel source."""
+    achieved = alg_bytes / (avg_us * 1e-6) / 1e9
+    rec = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+           "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(avg_us, 3)}
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"traffic_{workload}.json")
+    if os.path.exists(path):
+        with open(path) as f:
+            tr = json.load(f)
+        k = tr.get("kernels", {}).get(kernel)
+        csrc = os.path.join(here, "sparse_kv_page_amd", "csrc")
+        srcs = {"page_score": "page_score.hip", "select": "select.hip", "sparse_decode": "sparse_decode.hip"}
+        if k and kernel in srcs:
+            cur = _sha1([os.path.join(csrc, srcs[kernel]), os.path.join(csrc, "common.h"),
+                         os.path.join(csrc, "kernels.h")])
+            if cur == k.get("source_sha1"):
+                rec["traffic"] = int(k["hbm_bytes_per_launch"])
+                rec["traffic_over_algorithmic"] = round(k["hbm_bytes_per_launch"] / alg_bytes, 4)
+    return rec
 
 
 def cpu_baseline(wl, cfg, data, seconds):
