@@ -22,6 +22,7 @@
 #include "kernels.h"
 
 #include <atomic>
+#include <type_traits>
 
 namespace locks {
 
@@ -288,7 +289,7 @@ __device__ __forceinline__ void wait_vm_pages(int pages) {
   compiler_fence();
 }
 
-template <int D, int RT, int P>
+template <int D, int RT, int P, int G>
 struct LdsRec {
   static constexpr int kE = 2;
   static constexpr int kHeadBytes = kE * D * (1 + RT);      // mu | V^T
@@ -299,7 +300,8 @@ struct LdsRec {
   static constexpr int kRowChunks = kE * D / 16;            // 16-byte chunks per row
   static constexpr int kHeadChunks = kHeadBytes / 16;
   static constexpr int kBudget = 80 * 1024;                 // LDS bytes per workgroup
-  static constexpr int kNs0 = (kBudget - 4 * 1024) / (4 * kBytes);
+  static constexpr int kExtra = 4 * (2 * G * 16 + 64 * G) * 4; // w and score staging of 4 waves
+  static constexpr int kNs0 = (kBudget - kExtra) / (4 * kBytes);
   static constexpr int kNs = kNs0 < 2 ? 2 : (kNs0 > 8 ? 8 : kNs0);
   static_assert(kBytes % 16 == 0, "records are whole 16-byte chunks");
   // LDS chunk x holds global chunk swz(x) (an involution inside each row)
@@ -315,7 +317,7 @@ struct LdsRec {
 template <int D, int RT, int GQ, int P>
 __global__ __launch_bounds__(256, 2) void page_score_lds_kernel(ScoreArgs a) {
   using M = ScoreMfma<bf16_t, D>;
-  using R = LdsRec<D, RT, P>;
+  using R = LdsRec<D, RT, P, GQ>;
   constexpr int G = GQ;
   constexpr int lph = 64 / G;
   constexpr int TPL = P / lph;
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void page_score_lds_kernel(ScoreArgs a) {
   constexpr int kWVec = (RT + 1 + 3) / 4;
   static_assert(TPL >= 1 && TPL * lph == P, "P * G must be a multiple of 64");
   __shared__ __attribute__((aligned(16))) uint8_t slots[kScoreWaves][NS][R::kBytes];
-  __shared__ __attribute__((aligned(16))) float wbuf[kScoreWaves][G][16];
+  __shared__ __attribute__((aligned(16))) float wbuf[kScoreWaves][2][G][16];
   __shared__ __attribute__((aligned(16))) float sbuf[kScoreWaves][64][G];
 
   const int lane = threadIdx.x & 63;
@@ -388,68 +390,109 @@ __global__ __launch_bounds__(256, 2) void page_score_lds_kernel(ScoreArgs a) {
   const int npre = np < NS ? np : NS;
   for (int t = 0; t < npre; ++t) issue(t, t);
 
-  int slot = 0;
-  for (int t = 0; t < np; ++t) {
-    const int later = min(np - 1 - t, NS - 1);  // records issued after page t
-    wait_vm_pages<R::kInstr, NS - 1>(later);
-    const uint8_t* rec = &slots[wave][slot][0];
+  // Two pages per iteration: their dependent chains (LDS reads -> MFMA ->
+  // transpose through LDS -> logits -> DPP reductions) interleave, which hides
+  // the chain latency the two resident waves per SIMD cannot.
+  auto score_pages = [&](auto npg_tag, int t, int s0) {
+    constexpr int NPG = decltype(npg_tag)::value;
+    const uint8_t* rec[NPG];
+    rec[0] = &slots[wave][s0][0];
+    if constexpr (NPG == 2) rec[1] = &slots[wave][s0 + 1 == NS ? 0 : s0 + 1][0];
 
     // ---- A: w_g and q_g . mu ----
-    typename M::Op av[M::kSteps];
+    typename M::Op av[NPG][M::kSteps];
 #pragma unroll
-    for (int s = 0; s < M::kSteps; ++s) av[s] = *reinterpret_cast<const bf16x8_t*>(rec + a_off[s]);
-    const f32x4_t acc = M::product(av, qb);
-    if (n < G) *reinterpret_cast<f32x4_t*>(&wbuf[wave][n][kg * 4]) = acc;
-    wave_lds_sync();
-    float w[kWVec * 4];
+    for (int p = 0; p < NPG; ++p)
 #pragma unroll
-    for (int v = 0; v < kWVec; ++v) {
-      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&wbuf[wave][g][v * 4]);
-      w[4 * v] = x[0]; w[4 * v + 1] = x[1]; w[4 * v + 2] = x[2]; w[4 * v + 3] = x[3];
+      for (int s = 0; s < M::kSteps; ++s) av[p][s] = *reinterpret_cast<const bf16x8_t*>(rec[p] + a_off[s]);
+    f32x4_t acc[NPG];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) acc[p] = M::product(av[p], qb);
+    if (n < G) {
+#pragma unroll
+      for (int p = 0; p < NPG; ++p) *reinterpret_cast<f32x4_t*>(&wbuf[wave][p][n][kg * 4]) = acc[p];
     }
-    const float qmu = w[RT];
+    wave_lds_sync();
+    float ws[NPG][RT], qmu[NPG];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      float w[kWVec * 4];
+#pragma unroll
+      for (int v = 0; v < kWVec; ++v) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&wbuf[wave][p][g][v * 4]);
+        w[4 * v] = x[0]; w[4 * v + 1] = x[1]; w[4 * v + 2] = x[2]; w[4 * v + 3] = x[3];
+      }
+      qmu[p] = w[RT];
+#pragma unroll
+      for (int rho = 0; rho < RT; ++rho) ws[p][rho] = w[rho] * zscale;
+    }
 
     // ---- B: logits of the lane's tokens u, u + lph, ... ----
-    float ws[RT];
+    float z[NPG][TPL];
 #pragma unroll
-    for (int rho = 0; rho < RT; ++rho) ws[rho] = w[rho] * zscale;
-    const uint8_t* cb = rec + R::kHeadBytes;
-    float z[TPL];
+    for (int p = 0; p < NPG; ++p) {
+      const uint8_t* cb = rec[p] + R::kHeadBytes;
 #pragma unroll
-    for (int tt = 0; tt < TPL; ++tt) {
-      const int tok = u + lph * tt;
-      uint32_t cw[RT / 2];
-      if constexpr (RT == 8) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cb + tok * 16);
-        cw[0] = v[0]; cw[1] = v[1]; cw[2] = v[2]; cw[3] = v[3];
-      } else if constexpr (RT == 4) {
-        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(cb + tok * 8);
-        cw[0] = v[0]; cw[1] = v[1];
-      } else {
-        cw[0] = *reinterpret_cast<const uint32_t*>(cb + tok * 4);
+      for (int tt = 0; tt < TPL; ++tt) {
+        const int tok = u + lph * tt;
+        uint32_t cw[RT / 2];
+        if constexpr (RT == 8) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cb + tok * 16);
+          cw[0] = v[0]; cw[1] = v[1]; cw[2] = v[2]; cw[3] = v[3];
+        } else if constexpr (RT == 4) {
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(cb + tok * 8);
+          cw[0] = v[0]; cw[1] = v[1];
+        } else {
+          cw[0] = *reinterpret_cast<const uint32_t*>(cb + tok * 4);
+        }
+        float sacc = 0.f;
+#pragma unroll
+        for (int rho = 0; rho < RT; ++rho)
+          sacc = fmaf(ws[p][rho], (rho & 1) ? bf16_hi(cw[rho >> 1]) : bf16_lo(cw[rho >> 1]), sacc);
+        z[p][tt] = sacc;
       }
-      float s = 0.f;
-#pragma unroll
-      for (int rho = 0; rho < RT; ++rho)
-        s = fmaf(ws[rho], (rho & 1) ? bf16_hi(cw[rho >> 1]) : bf16_lo(cw[rho >> 1]), s);
-      z[tt] = s;
     }
-    float mx = z[0];
+    float mx[NPG], sm[NPG];
 #pragma unroll
-    for (int tt = 1; tt < TPL; ++tt) mx = fmaxf(mx, z[tt]);
-    mx = group_max<lph>(mx);
-    float sm = 0.f;
+    for (int p = 0; p < NPG; ++p) {
+      mx[p] = z[p][0];
 #pragma unroll
-    for (int tt = 0; tt < TPL; ++tt) sm += exp2_fast(z[tt] - mx);
-    sm = group_sum<lph>(sm);
+      for (int tt = 1; tt < TPL; ++tt) mx[p] = fmaxf(mx[p], z[p][tt]);
+    }
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) mx[p] = group_max<lph>(mx[p]);
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      sm[p] = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < TPL; ++tt) sm[p] += exp2_fast(z[p][tt] - mx[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) sm[p] = group_sum<lph>(sm[p]);
     if (u == 0) {
-      const int bid = __builtin_amdgcn_readlane(my_bid, t);
-      const float sc = qmu * a.scale + (mx + log2_fast(sm)) * kLn2;
-      sbuf[wave][t][g] = bid_ok(bid) ? sc : -INFINITY;
+#pragma unroll
+      for (int p = 0; p < NPG; ++p) {
+        const int bid = __builtin_amdgcn_readlane(my_bid, t + p);
+        const float sc = qmu[p] * a.scale + (mx[p] + log2_fast(sm[p])) * kLn2;
+        sbuf[wave][t + p][g] = bid_ok(bid) ? sc : -INFINITY;
+      }
     }
-    // every read of this slot has been consumed; refill it
+  };
+
+  int slot = 0;
+  int t = 0;
+  for (; t + 1 < np; t += 2) {
+    wait_vm_pages<R::kInstr, NS - 1>(min(np, t + NS) - (t + 2));  // records issued after page t+1
+    score_pages(std::integral_constant<int, 2>{}, t, slot);
+    // every read of these two slots has been consumed; refill them
+    const int s1 = slot + 1 == NS ? 0 : slot + 1;
     if (t + NS < np) issue(t + NS, slot);
-    slot = slot + 1 == NS ? 0 : slot + 1;
+    if (t + 1 + NS < np) issue(t + 1 + NS, s1);
+    slot = s1 + 1 == NS ? 0 : s1 + 1;
+  }
+  if (t < np) {
+    wait_vm_pages<R::kInstr, NS - 1>(0);
+    score_pages(std::integral_constant<int, 1>{}, t, slot);
   }
   wave_lds_sync();
   // coalesced store of the wave's scores: lane t writes page p0 + t of each head
