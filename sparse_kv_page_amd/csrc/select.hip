@@ -33,27 +33,55 @@ constexpr int kSelDigit = 11;
 
 namespace {
 
-template <typename F>
-__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, F op) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = op(v, (uint32_t)__shfl_xor((int)v, o, 64));
+// ---- wave-wide helpers on DPP (no LDS permutes) ----
+// inclusive prefix sum over the 64 lanes: row_shr 1/2/4/8 inside each row of
+// 16 lanes, then row_bcast 15 / 31 carry the row totals forward
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
-// inclusive scan over the wave
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int x = __shfl_up(v, o, 64);
-    if (lane >= o) v += x;
-  }
-  return v;
+// max / min of a uint32 over the wave (uniform result)
+template <bool kMax>
+__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
+  auto op = [](uint32_t x, uint32_t y) { return kMax ? (x > y ? x : y) : (x < y ? x : y); };
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor1, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor2, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppMirror, 0xf, 0xf, false));
+  const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+  return op(op(r0, r1), op(r2, r3));
 }
 
-// exclusive scan over the block; `tot` receives the block total (2 barriers)
+// float max / sum over the wave (uniform result)
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max<16>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// exclusive scan over the block; `tot` receives the block total. One barrier:
+// the caller puts another barrier between two uses of the same wsum.
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int inc = wave_incl_scan(v, lane);
+  const int inc = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
   int before = 0;
@@ -64,30 +92,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& tot) {
     before += w < wave ? x : 0;
     tot += x;
   }
-  __syncthreads();
   return before + inc - v;
-}
-
-// block-wide max / sum of up to 8 per-head values; every thread gets the result
-template <bool kMax>
-__device__ __forceinline__ void block_reduce_heads(float* v, int G, float (*red)[8], float* out) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    if (g < G) {
-      const float r = kMax ? group_max<64>(v[g]) : group_sum<64>(v[g]);
-      if (lane == 0) red[wave][g] = r;
-    }
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < G) {
-    float r = red[0][threadIdx.x];
-    for (int w = 1; w < kSelWaves; ++w) r = kMax ? fmaxf(r, red[w][threadIdx.x]) : r + red[w][threadIdx.x];
-    out[threadIdx.x] = r;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < 8; ++g) v[g] = g < G ? out[g] : 0.f;
 }
 
 }  // namespace
@@ -96,8 +101,8 @@ template <int NPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ uint32_t keys_lds[kSelLdsKeys];
   __shared__ uint32_t hist[2][kSelBins];
-  __shared__ float red[kSelWaves][8];
-  __shared__ float hv[8];
+  __shared__ float red_m[kSelWaves][8];
+  __shared__ float red_s[kSelWaves][8];
   __shared__ uint32_t redu[kSelWaves][2];
   __shared__ int wsum[kSelWaves];
   __shared__ int pick_s[3];
@@ -137,7 +142,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   auto is_cand = [&](int j) { return j >= 1 && j < Jc && j != J - 1; };
   for (int x = tid; x < kSelBins; x += kSelThreads) hist[0][x] = 0;
 
-  // ---- per-head normaliser log Z_g ----
+  // ---- per-head normaliser log Z_g: block max, then block sum of
+  // 2^(s - max); each reduction is DPP inside the waves, one LDS exchange and
+  // one barrier, with every thread combining the wave results itself ----
   float mx[8];
 #pragma unroll
   for (int g = 0; g < 8; ++g) mx[g] = -INFINITY;
@@ -157,7 +164,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       for (int g = 0; g < 8; ++g)
         if (g < G) mx[g] = fmaxf(mx[g], srow[(int64_t)g * a.max_pages + j]);
   }
-  block_reduce_heads<true>(mx, G, red, hv);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (g < G) {
+      const float r = wave_max(mx[g]);
+      if (lane == 0) red_m[wave][g] = r;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (g < G) {
+      float r = red_m[0][g];
+#pragma unroll
+      for (int w = 1; w < kSelWaves; ++w) r = fmaxf(r, red_m[w][g]);
+      mx[g] = r;
+    }
+  }
   float sm[8];
 #pragma unroll
   for (int g = 0; g < 8; ++g) sm[g] = 0.f;
@@ -173,10 +196,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       for (int g = 0; g < 8; ++g)
         if (g < G && mx[g] > -INFINITY) sm[g] += exp2_fast((srow[(int64_t)g * a.max_pages + j] - mx[g]) * kLog2e);
   }
-  block_reduce_heads<false>(sm, G, red, hv);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (g < G) {
+      const float r = wave_sum(sm[g]);
+      if (lane == 0) red_s[wave][g] = r;
+    }
+  }
+  __syncthreads();
   float lz[8];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) lz[g] = (g < G && mx[g] > -INFINITY) ? mx[g] + log2_fast(sm[g]) * kLn2 : -INFINITY;
+  for (int g = 0; g < 8; ++g) {
+    lz[g] = -INFINITY;
+    if (g < G && mx[g] > -INFINITY) {
+      float r = red_s[0][g];
+#pragma unroll
+      for (int w = 1; w < kSelWaves; ++w) r += red_s[w][g];
+      lz[g] = mx[g] + log2_fast(r) * kLn2;
+    }
+  }
 
   // ---- sigma_j, its sortable key, and the spread of candidate keys ----
   const float log2G = log2_fast((float)G);
@@ -223,8 +261,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       sigma_key(j, sv);
     }
   }
-  kmax = wave_reduce_u32(kmax, [](uint32_t p, uint32_t q) { return p > q ? p : q; });
-  kmin = wave_reduce_u32(kmin, [](uint32_t p, uint32_t q) { return p < q ? p : q; });
+  kmax = wave_minmax_u32<true>(kmax);
+  kmin = wave_minmax_u32<false>(kmin);
   if (lane == 0) { redu[wave][0] = kmax; redu[wave][1] = kmin; }
   __syncthreads();  // also publishes keys[] and the cleared hist[0]
   kmax = redu[0][0];
