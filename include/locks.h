@@ -84,13 +84,15 @@ int locks_version(void);
  * its per-token coefficients C_j. */
 size_t locks_summary_record_bytes(const locks_config_t* cfg);
 
-/* Workspace bytes needed by locks_score_select and locks_sparse_decode for a
- * batch of `batch` sequences of at most `max_pages` pages (one buffer of
- * this size serves both calls). Writes *bytes; returns a status.
+/* Workspace bytes needed by locks_score_select, locks_sparse_decode and
+ * locks_decode_step for a batch of `batch` sequences of at most `max_pages`
+ * pages (one buffer of this size serves all three, in any interleaving).
+ * Writes *bytes; returns a status.
  * The workspace must be zero-filled once before its first use: its first
- * bytes hold per-(sequence, KV head) arrival counters of the decode split
- * merge, which every locks_sparse_decode call returns to zero. Calls that
- * share a workspace must not overlap in time (same stream, or synchronised). */
+ * bytes hold control words (per-(sequence, KV head) arrival counters and
+ * ready flags, work tickets) that every call returns to zero and that no
+ * call uses as scratch; the rest is scratch. Calls that share a workspace
+ * must not overlap in time (same stream, or synchronised). */
 int locks_workspace_size(const locks_config_t* cfg, int32_t batch, int32_t max_pages,
                          size_t* bytes);
 
@@ -161,6 +163,16 @@ int locks_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_
                         const int32_t* seq_lens, const int32_t* selected, int32_t batch,
                         int32_t max_pages, void* out, float* lse, void* ws, size_t ws_bytes,
                         hipStream_t stream);
+
+/* One whole decode step, [Locks] §2 and §4: locks_score_select, then
+ * locks_sparse_decode on the page ids it wrote, sharing one workspace (ws as
+ * for locks_score_select). `selected`, out and lse are those two calls'
+ * results. */
+int locks_decode_step(const locks_config_t* cfg, const void* q, const void* summary_pool,
+                      const void* k_pool, const void* v_pool, int64_t num_blocks,
+                      const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                      int32_t max_pages, int32_t* selected, void* out, float* lse, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

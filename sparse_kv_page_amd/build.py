@@ -23,7 +23,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["locks_api.cpp", "page_score.hip", "select.hip", "sparse_decode.hip",
            "build_summaries.hip"]
-HEADERS = ["common.h", "kernels.h", os.path.join("..", "..", "include", "locks.h")]
+HEADERS = ["common.h", "kernels.h", "score_lds.h", "select_unit.h", "decode_split.h",
+           os.path.join("..", "..", "include", "locks.h")]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-fno-gpu-rdc",
          # packed fp32 VALU instructions are kept out of the generated code

@@ -49,17 +49,23 @@ int64_t rec_elems(const locks_config_t* c) {
   return (int64_t)c->head_dim * (1 + c->rank) + (int64_t)c->page_size * c->rank;
 }
 
-// Workspace layout: [decode arrival counters, one int32 per (sequence, KV
-// head), zero between calls] then a region shared by the two stages: the
-// head scores and page keys of score/select, or the split partials of decode.
-size_t counter_bytes(const locks_config_t* c, int32_t batch) {
+// Workspace layout, shared by every entry point that takes a workspace:
+//   control region: the decode arrival counters, one int32 per (sequence,
+//     KV head); zero between calls, never written as scratch
+//   data region (scratch, overwritten by every call):
+//     score/select: head scores, page keys
+//     decode:       split partials
+//     decode step:  the two above in turn
+// Because the control words sit in front of every data region, calls of
+// different entry points may share one workspace.
+size_t ctl_bytes(const locks_config_t* c, int32_t batch) {
   return align_up((size_t)batch * c->num_kv_heads * sizeof(int32_t));
 }
 
 size_t score_ws_bytes(const locks_config_t* c, int32_t batch, int32_t max_pages) {
   const size_t scores = (size_t)batch * c->num_q_heads * max_pages * sizeof(float);
   const size_t sigma = (size_t)batch * c->num_kv_heads * max_pages * sizeof(float);
-  return counter_bytes(c, batch) + align_up(scores) + align_up(sigma);
+  return ctl_bytes(c, batch) + align_up(scores) + align_up(sigma);
 }
 
 int decode_pages_per_split(const locks_config_t* c) { return locks::decode_pages_per_split(c->page_size); }
@@ -71,12 +77,76 @@ int decode_splits(const locks_config_t* c) {
 
 size_t decode_ws_bytes(const locks_config_t* c, int32_t batch) {
   const size_t rows = (size_t)batch * c->num_q_heads * decode_splits(c);
-  return counter_bytes(c, batch) + align_up(rows * c->head_dim * sizeof(float)) +
+  return ctl_bytes(c, batch) + align_up(rows * c->head_dim * sizeof(float)) +
          align_up(rows * sizeof(float));
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LOCKS_OK : LOCKS_E_HIP; }
 
+locks::ScoreArgs score_args(const locks_config_t* cfg, const void* q, const void* summary_pool,
+                            int64_t num_blocks, const int32_t* block_table, const int32_t* seq_lens,
+                            int32_t max_pages, float* head_scores) {
+  locks::ScoreArgs a{};
+  a.q = q;
+  a.sum_pool = static_cast<const uint8_t*>(summary_pool);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.scores = head_scores;
+  a.num_blocks = num_blocks;
+  a.rec_elems = rec_elems(cfg);
+  a.Hkv = cfg->num_kv_heads;
+  a.G = cfg->num_q_heads / cfg->num_kv_heads;
+  a.P = cfg->page_size;
+  a.r = cfg->rank;
+  a.max_pages = max_pages;
+  a.scale = cfg->softmax_scale;
+  return a;
+}
+
+locks::SelectArgs select_args(const locks_config_t* cfg, const float* head_scores, const int32_t* seq_lens,
+                              int32_t max_pages, int32_t* selected, float* page_sigma) {
+  locks::SelectArgs a{};
+  a.scores = head_scores;
+  a.seq_lens = seq_lens;
+  a.selected = selected;
+  a.sigma = page_sigma;
+  a.Hkv = cfg->num_kv_heads;
+  a.G = cfg->num_q_heads / cfg->num_kv_heads;
+  a.P = cfg->page_size;
+  a.k = cfg->budget_pages;
+  a.max_pages = max_pages;
+  a.idbits = 1;
+  while (a.idbits < 31 && (int64_t(1) << a.idbits) < max_pages) ++a.idbits;
+  return a;
+}
+
+locks::DecodeArgs decode_args(const locks_config_t* cfg, const void* q, const void* k_pool, const void* v_pool,
+                              int64_t num_blocks, const int32_t* block_table, const int32_t* seq_lens,
+                              const int32_t* selected, int32_t max_pages, void* out, float* lse,
+                              int32_t* counters, float* part_o, float* part_lse) {
+  locks::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.selected = selected;
+  a.counters = counters;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.out = out;
+  a.lse = lse;
+  a.num_blocks = num_blocks;
+  a.Hkv = cfg->num_kv_heads;
+  a.G = cfg->num_q_heads / cfg->num_kv_heads;
+  a.P = cfg->page_size;
+  a.k = cfg->budget_pages;
+  a.max_pages = max_pages;
+  a.pages_per_split = decode_pages_per_split(cfg);
+  a.splits = decode_splits(cfg);
+  a.scale = cfg->softmax_scale;
+  return a;
+}
 
 }  // namespace
 
@@ -144,20 +214,7 @@ int locks_page_score(const locks_config_t* cfg, const void* q, const void* summa
   if (num_blocks < 0) return LOCKS_E_INVALID_ARG;
   if (batch == 0) return LOCKS_OK;
   if (!q || !summary_pool || !block_table || !seq_lens || !head_scores) return LOCKS_E_INVALID_ARG;
-  locks::ScoreArgs a{};
-  a.q = q;
-  a.sum_pool = static_cast<const uint8_t*>(summary_pool);
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.scores = head_scores;
-  a.num_blocks = num_blocks;
-  a.rec_elems = rec_elems(cfg);
-  a.Hkv = cfg->num_kv_heads;
-  a.G = cfg->num_q_heads / cfg->num_kv_heads;
-  a.P = cfg->page_size;
-  a.r = cfg->rank;
-  a.max_pages = max_pages;
-  a.scale = cfg->softmax_scale;
+  locks::ScoreArgs a = score_args(cfg, q, summary_pool, num_blocks, block_table, seq_lens, max_pages, head_scores);
   return hip_status(locks::launch_page_score(a, cfg->kv_dtype, cfg->head_dim, batch, stream));
 }
 
@@ -170,18 +227,7 @@ int locks_select_pages(const locks_config_t* cfg, const float* head_scores, cons
   if (st != LOCKS_OK) return st;
   if (batch == 0) return LOCKS_OK;
   if (!head_scores || !seq_lens || !selected || !page_sigma) return LOCKS_E_INVALID_ARG;
-  locks::SelectArgs a{};
-  a.scores = head_scores;
-  a.seq_lens = seq_lens;
-  a.selected = selected;
-  a.sigma = page_sigma;
-  a.Hkv = cfg->num_kv_heads;
-  a.G = cfg->num_q_heads / cfg->num_kv_heads;
-  a.P = cfg->page_size;
-  a.k = cfg->budget_pages;
-  a.max_pages = max_pages;
-  a.idbits = 1;
-  while (a.idbits < 31 && (int64_t(1) << a.idbits) < max_pages) ++a.idbits;
+  locks::SelectArgs a = select_args(cfg, head_scores, seq_lens, max_pages, selected, page_sigma);
   return hip_status(locks::launch_select(a, batch, stream));
 }
 
@@ -197,7 +243,7 @@ int locks_score_select(const locks_config_t* cfg, const void* q, const void* sum
   if (batch == 0) return LOCKS_OK;
   if (!q || !summary_pool || !block_table || !seq_lens || !selected) return LOCKS_E_INVALID_ARG;
   if (!ws || ws_bytes < score_ws_bytes(cfg, batch, max_pages)) return LOCKS_E_WORKSPACE;
-  uint8_t* region = static_cast<uint8_t*>(ws) + counter_bytes(cfg, batch);
+  uint8_t* region = static_cast<uint8_t*>(ws) + ctl_bytes(cfg, batch);
   float* scores = reinterpret_cast<float*>(region);
   float* sigma = reinterpret_cast<float*>(region +
                                           align_up((size_t)batch * cfg->num_q_heads * max_pages * sizeof(float)));
@@ -221,31 +267,36 @@ int locks_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !selected || !out)
     return LOCKS_E_INVALID_ARG;
   if (!ws || ws_bytes < decode_ws_bytes(cfg, batch)) return LOCKS_E_WORKSPACE;
-  const int splits = decode_splits(cfg);
-  const size_t rows = (size_t)batch * cfg->num_q_heads * splits;
-  locks::DecodeArgs a{};
-  a.q = q;
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.selected = selected;
-  uint8_t* region = static_cast<uint8_t*>(ws) + counter_bytes(cfg, batch);
-  a.counters = static_cast<int32_t*>(ws);
-  a.part_o = reinterpret_cast<float*>(region);
-  a.part_lse = reinterpret_cast<float*>(region + align_up(rows * cfg->head_dim * sizeof(float)));
-  a.out = out;
-  a.lse = lse;
-  a.num_blocks = num_blocks;
-  a.Hkv = cfg->num_kv_heads;
-  a.G = cfg->num_q_heads / cfg->num_kv_heads;
-  a.P = cfg->page_size;
-  a.k = cfg->budget_pages;
-  a.max_pages = max_pages;
-  a.pages_per_split = decode_pages_per_split(cfg);
-  a.splits = splits;
-  a.scale = cfg->softmax_scale;
+  const size_t rows = (size_t)batch * cfg->num_q_heads * decode_splits(cfg);
+  uint8_t* region = static_cast<uint8_t*>(ws) + ctl_bytes(cfg, batch);
+  locks::DecodeArgs a = decode_args(cfg, q, k_pool, v_pool, num_blocks, block_table, seq_lens, selected,
+                                    max_pages, out, lse, static_cast<int32_t*>(ws),
+                                    reinterpret_cast<float*>(region),
+                                    reinterpret_cast<float*>(region + align_up(rows * cfg->head_dim * sizeof(float))));
   return hip_status(locks::launch_sparse_decode(a, cfg->kv_dtype, cfg->head_dim, batch, stream));
+}
+
+int locks_decode_step(const locks_config_t* cfg, const void* q, const void* summary_pool, const void* k_pool,
+                      const void* v_pool, int64_t num_blocks, const int32_t* block_table,
+                      const int32_t* seq_lens, int32_t batch, int32_t max_pages, int32_t* selected,
+                      void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != LOCKS_OK) return st;
+  st = check_batch(batch, max_pages);
+  if (st != LOCKS_OK) return st;
+  if (num_blocks < 0) return LOCKS_E_INVALID_ARG;
+  if (batch == 0) return LOCKS_OK;
+  if (!q || !summary_pool || !k_pool || !v_pool || !block_table || !seq_lens || !selected || !out)
+    return LOCKS_E_INVALID_ARG;
+  if (!ws || ws_bytes < score_ws_bytes(cfg, batch, max_pages) || ws_bytes < decode_ws_bytes(cfg, batch))
+    return LOCKS_E_WORKSPACE;
+  // the head scores and page keys of the first call are consumed before the
+  // second call's partials overwrite them (same stream)
+  st = locks_score_select(cfg, q, summary_pool, num_blocks, block_table, seq_lens, batch, max_pages, selected,
+                          ws, ws_bytes, stream);
+  if (st != LOCKS_OK) return st;
+  return locks_sparse_decode(cfg, q, k_pool, v_pool, num_blocks, block_table, seq_lens, selected, batch,
+                             max_pages, out, lse, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

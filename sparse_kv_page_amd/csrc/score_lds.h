@@ -1,0 +1,345 @@
+// Device code of the page scorer shared by the scoring kernel and the fused
+// decode-step kernel: MFMA operand helpers, direct global->LDS record loads
+// and the LDS-staged per-wave scoring of a run of pages, [Locks] §4 Eq. (2).
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+#include <type_traits>
+
+namespace locks {
+
+constexpr int kScoreWaves = 4;
+
+template <typename T, int D>
+struct ScoreMfma;
+
+// bf16: v_mfma_f32_16x16x32_bf16. Lane l supplies row/col (l % 16) and the
+// k-range 8*(l/16) .. +8 of each 32-wide k step.
+template <int D>
+struct ScoreMfma<bf16_t, D> {
+  static constexpr int kSteps = D / 32;
+  using Op = bf16x8_t;
+  static __device__ __forceinline__ void load_a(Op* a, const bf16_t* row, int kg) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) a[s] = __builtin_bit_cast(Op, ld_nt4(row + s * 32 + kg * 8));
+  }
+  static __device__ __forceinline__ void load_b(Op* b, const bf16_t* qrow, bool ok, int kg) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+      b[s] = ok ? *reinterpret_cast<const Op*>(qrow + s * 32 + kg * 8) : Op{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  static __device__ __forceinline__ f32x4_t product(const Op* a, const Op* b) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
+    return acc;
+  }
+};
+
+// fp32: v_mfma_f32_16x16x4_f32. Lane l supplies row/col (l % 16) and k = l/16
+// of each 4-wide k step.
+template <int D>
+struct ScoreMfma<float, D> {
+  static constexpr int kSteps = D / 4;
+  using Op = float;
+  static __device__ __forceinline__ void load_a(Op* a, const float* row, int kg) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) a[s] = __uint_as_float(ld_nt1(row + s * 4 + kg));
+  }
+  static __device__ __forceinline__ void load_b(Op* b, const float* qrow, bool ok, int kg) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) b[s] = ok ? qrow[s * 4 + kg] : 0.f;
+  }
+  static __device__ __forceinline__ f32x4_t product(const Op* a, const Op* b) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    return acc;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// LDS-staged variant for bf16 summaries with rank 2, 4 or 8 and G * P >= 64.
+//
+// Each wave keeps a ring of NS record slots in LDS and fills them with
+// direct global->LDS loads (global_load_lds_dwordx4, non-temporal), so NS-1
+// records per wave are in flight without holding registers. The 16-byte
+// chunks of every row of the mu / V^T block are XOR-swizzled by their row
+// index on the way in (the source address is per lane), which makes the
+// row-wise MFMA operand reads conflict-free. Coefficient rows are read
+// token-strided (lane u of a head takes tokens u, u + 64/G, ...), again
+// conflict-free, with the G head groups reading the same addresses.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+__host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
+__device__ __forceinline__ void compiler_fence() { __asm__ __volatile__("" ::: "memory"); }
+
+// One direct global->LDS load of 16 bytes per active lane, non-temporal: lane
+// i writes LDS bytes [lds + 16 i, lds + 16 i + 16). Issued from inline
+// assembly so that the compiler does not guard every later LDS read with a
+// wait for all outstanding loads; completion is awaited explicitly with
+// s_waitcnt vmcnt before a slot is read. M0 is saved and restored.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  __asm__ __volatile__(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_ptr)(p);
+}
+
+// wait until at most n vector-memory instructions of this wave are pending
+template <int I>
+__device__ __forceinline__ void wait_vm_const() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(I));
+}
+
+template <int STEP, int MAXN>
+__device__ __forceinline__ void wait_vm_pages(int pages) {
+  // pages in 0 .. MAXN; the immediate must be a constant, hence the switch
+  switch (pages) {
+    case 0: wait_vm_const<0>(); break;
+    case 1: if constexpr (MAXN >= 1) wait_vm_const<1 * STEP>(); break;
+    case 2: if constexpr (MAXN >= 2) wait_vm_const<2 * STEP>(); break;
+    case 3: if constexpr (MAXN >= 3) wait_vm_const<3 * STEP>(); break;
+    case 4: if constexpr (MAXN >= 4) wait_vm_const<4 * STEP>(); break;
+    case 5: if constexpr (MAXN >= 5) wait_vm_const<5 * STEP>(); break;
+    case 6: if constexpr (MAXN >= 6) wait_vm_const<6 * STEP>(); break;
+    default: if constexpr (MAXN >= 7) wait_vm_const<7 * STEP>(); break;
+  }
+  compiler_fence();
+}
+
+template <int D, int RT, int P, int G>
+struct LdsRec {
+  static constexpr int kE = 2;
+  static constexpr int kHeadBytes = kE * D * (1 + RT);      // mu | V^T
+  static constexpr int kBytes = kHeadBytes + kE * P * RT;   // + C
+  static constexpr int kChunks = kBytes / 16;
+  static constexpr int kInstr = (kChunks + 63) / 64;        // DMA instructions per record
+  static constexpr int kTail = kChunks - (kInstr - 1) * 64; // lanes of the last one
+  static constexpr int kRowChunks = kE * D / 16;            // 16-byte chunks per row
+  static constexpr int kHeadChunks = kHeadBytes / 16;
+  static constexpr int kBudget = 80 * 1024;                 // LDS bytes per workgroup
+  static constexpr int kExtra = 4 * (2 * G * 16 + 64 * G) * 4; // w and score staging of 4 waves
+  static constexpr int kNs0 = (kBudget - kExtra) / (4 * kBytes);
+  static constexpr int kNs = kNs0 < 2 ? 2 : (kNs0 > 8 ? 8 : kNs0);
+  static_assert(kBytes % 16 == 0, "records are whole 16-byte chunks");
+  // LDS chunk x holds global chunk swz(x) (an involution inside each row)
+  static __device__ __forceinline__ int swz(int x) {
+    if (x >= kHeadChunks) return x;
+    const int row = x / kRowChunks;
+    return row * kRowChunks + ((x % kRowChunks) ^ (row % kRowChunks));
+  }
+};
+
+template <int D, int RT, int GQ, int P>
+struct alignas(16) ScoreLds {
+  using R = LdsRec<D, RT, P, GQ>;
+  uint8_t slots[kScoreWaves][R::kNs][R::kBytes];
+  float wbuf[kScoreWaves][2][GQ][16];
+  float sbuf[kScoreWaves][64][GQ];
+};
+
+// One wave scores pages [p0, p0 + min(ppw, Jc - p0)) of the unit (b, h) for
+// all G heads (ppw <= 64, p0 wave-uniform).
+template <int D, int RT, int GQ, int P>
+__device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h, int p0, int ppw,
+                                               ScoreLds<D, RT, GQ, P>& L) {
+  using M = ScoreMfma<bf16_t, D>;
+  using R = LdsRec<D, RT, P, GQ>;
+  constexpr int G = GQ;
+  constexpr int lph = 64 / G;
+  constexpr int TPL = P / lph;
+  constexpr int NS = R::kNs;
+  constexpr int kWVec = (RT + 1 + 3) / 4;
+  static_assert(TPL >= 1 && TPL * lph == P, "P * G must be a multiple of 64");
+  auto& slots = L.slots;
+  auto& wbuf = L.wbuf;
+  auto& sbuf = L.sbuf;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int Hq = a.Hkv * G;
+  if (p0 >= a.max_pages) return;
+  // block ids are loaded before the length is known (entries up to max_pages
+  // are addressable), so the two loads are in flight together
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+  int my_bid = lane < ppw && p0 + lane < a.max_pages ? bt_row[p0 + lane] : -1;
+  const int T_b = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.max_pages, P));
+  const int Jc = T_b / P;
+  if (p0 >= Jc) return;
+  const int np = min(ppw, Jc - p0);
+
+  const int n = lane & 15;
+  const int kg = lane >> 4;
+  typename M::Op qb[M::kSteps];
+  M::load_b(qb, reinterpret_cast<const bf16_t*>(a.q) + ((int64_t)b * Hq + (int64_t)h * G + (n < G ? n : 0)) * D,
+            n < G, kg);
+  // settle the ordinary loads before the record loads start (the wait counts
+  // below assume only record loads are pending)
+  wait_vm_const<0>();
+  my_bid = __builtin_amdgcn_mov_dpp(my_bid, 0xE4, 0xf, 0xf, false);  // identity; orders the use after the wait
+  const int g = lane / lph;
+  const int u = lane - g * lph;
+  const float zscale = a.scale * kLog2e;
+
+  auto bid_ok = [&](int bid) { return bid >= 0 && (int64_t)bid < a.num_blocks; };
+  const uint8_t* pool = a.sum_pool + (int64_t)h * R::kBytes;
+  const int64_t blk_stride = (int64_t)a.Hkv * R::kBytes;
+
+  // per-lane DMA source offsets (swizzled) for each instruction of a record
+  int src_off[R::kInstr];
+#pragma unroll
+  for (int j = 0; j < R::kInstr; ++j) {
+    const int x = 64 * j + lane;
+    src_off[j] = (x < R::kChunks ? R::swz(x) : 0) * 16;
+  }
+  // MFMA A operand: LDS row of record row n (basis row n, or the centroid)
+  const int arow = n < RT ? n + 1 : 0;
+  int a_off[M::kSteps];
+#pragma unroll
+  for (int s = 0; s < M::kSteps; ++s) {
+    const int c = s * 4 + kg;
+    a_off[s] = (arow * R::kRowChunks + (c ^ (arow % R::kRowChunks))) * 16;
+  }
+
+  auto issue = [&](int t, int slot) {
+    const int bid = __builtin_amdgcn_readlane(my_bid, t);
+    const uint8_t* rec = pool + (int64_t)(bid_ok(bid) ? bid : 0) * blk_stride;
+    const uint32_t dst = lds_addr(&slots[wave][slot][0]);
+#pragma unroll
+    for (int j = 0; j < R::kInstr; ++j) {
+      if (j < R::kInstr - 1 || lane < R::kTail) dma16(rec + src_off[j], dst + j * 1024);
+    }
+  };
+
+  const int npre = np < NS ? np : NS;
+  for (int t = 0; t < npre; ++t) issue(t, t);
+
+  // Two pages per iteration: their dependent chains (LDS reads -> MFMA ->
+  // transpose through LDS -> logits -> DPP reductions) interleave, which hides
+  // the chain latency the two resident waves per SIMD cannot.
+  auto score_pages = [&](auto npg_tag, int t, int s0) {
+    constexpr int NPG = decltype(npg_tag)::value;
+    const uint8_t* rec[NPG];
+    rec[0] = &slots[wave][s0][0];
+    if constexpr (NPG == 2) rec[1] = &slots[wave][s0 + 1 == NS ? 0 : s0 + 1][0];
+
+    // ---- A: w_g and q_g . mu ----
+    typename M::Op av[NPG][M::kSteps];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p)
+#pragma unroll
+      for (int s = 0; s < M::kSteps; ++s) av[p][s] = *reinterpret_cast<const bf16x8_t*>(rec[p] + a_off[s]);
+    f32x4_t acc[NPG];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) acc[p] = M::product(av[p], qb);
+    if (n < G) {
+#pragma unroll
+      for (int p = 0; p < NPG; ++p) *reinterpret_cast<f32x4_t*>(&wbuf[wave][p][n][kg * 4]) = acc[p];
+    }
+    wave_lds_sync();
+    float ws[NPG][RT], qmu[NPG];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      float w[kWVec * 4];
+#pragma unroll
+      for (int v = 0; v < kWVec; ++v) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&wbuf[wave][p][g][v * 4]);
+        w[4 * v] = x[0]; w[4 * v + 1] = x[1]; w[4 * v + 2] = x[2]; w[4 * v + 3] = x[3];
+      }
+      qmu[p] = w[RT];
+#pragma unroll
+      for (int rho = 0; rho < RT; ++rho) ws[p][rho] = w[rho] * zscale;
+    }
+
+    // ---- B: logits of the lane's tokens u, u + lph, ... ----
+    float z[NPG][TPL];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      const uint8_t* cb = rec[p] + R::kHeadBytes;
+#pragma unroll
+      for (int tt = 0; tt < TPL; ++tt) {
+        const int tok = u + lph * tt;
+        uint32_t cw[RT / 2];
+        if constexpr (RT == 8) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cb + tok * 16);
+          cw[0] = v[0]; cw[1] = v[1]; cw[2] = v[2]; cw[3] = v[3];
+        } else if constexpr (RT == 4) {
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(cb + tok * 8);
+          cw[0] = v[0]; cw[1] = v[1];
+        } else {
+          cw[0] = *reinterpret_cast<const uint32_t*>(cb + tok * 4);
+        }
+        float sacc = 0.f;
+#pragma unroll
+        for (int rho = 0; rho < RT; ++rho)
+          sacc = fmaf(ws[p][rho], (rho & 1) ? bf16_hi(cw[rho >> 1]) : bf16_lo(cw[rho >> 1]), sacc);
+        z[p][tt] = sacc;
+      }
+    }
+    float mx[NPG], sm[NPG];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      mx[p] = z[p][0];
+#pragma unroll
+      for (int tt = 1; tt < TPL; ++tt) mx[p] = fmaxf(mx[p], z[p][tt]);
+    }
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) mx[p] = group_max<lph>(mx[p]);
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      sm[p] = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < TPL; ++tt) sm[p] += exp2_fast(z[p][tt] - mx[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) sm[p] = group_sum<lph>(sm[p]);
+    if (u == 0) {
+#pragma unroll
+      for (int p = 0; p < NPG; ++p) {
+        const int bid = __builtin_amdgcn_readlane(my_bid, t + p);
+        const float sc = qmu[p] * a.scale + (mx[p] + log2_fast(sm[p])) * kLn2;
+        sbuf[wave][t + p][g] = bid_ok(bid) ? sc : -INFINITY;
+      }
+    }
+  };
+
+  int slot = 0;
+  int t = 0;
+  for (; t + 1 < np; t += 2) {
+    wait_vm_pages<R::kInstr, NS - 1>(min(np, t + NS) - (t + 2));  // records issued after page t+1
+    score_pages(std::integral_constant<int, 2>{}, t, slot);
+    // every read of these two slots has been consumed; refill them
+    const int s1 = slot + 1 == NS ? 0 : slot + 1;
+    if (t + NS < np) issue(t + NS, slot);
+    if (t + 1 + NS < np) issue(t + 1 + NS, s1);
+    slot = s1 + 1 == NS ? 0 : s1 + 1;
+  }
+  if (t < np) {
+    wait_vm_pages<R::kInstr, NS - 1>(0);
+    score_pages(std::integral_constant<int, 1>{}, t, slot);
+  }
+  wave_lds_sync();
+  // coalesced store of the wave's scores: lane t writes page p0 + t of each head
+  float* out = a.scores + ((int64_t)b * Hq + (int64_t)h * G) * a.max_pages + p0;
+  if (lane < np) {
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) out[(int64_t)gg * a.max_pages + lane] = sbuf[wave][lane][gg];
+  }
+}
+
+}  // namespace locks

@@ -1,6 +1,6 @@
 // (a3 + a4) Share-average combine and top-(k-2) page selection, [Locks] §2, §4.
 //
-// One workgroup (1024 threads) per (sequence, KV head). From the per-head page
+// One workgroup (512 or 1024 threads) per (sequence, KV head). From the per-head page
 // scores s_g(j) of the Jc complete pages:
 //   log Z_g  = log sum_j exp(s_g(j))
 //   sigma_j  = log((1/G) sum_g exp(s_g(j) - log Z_g))   (log of the share average)
@@ -8,7 +8,7 @@
 // the largest sigma among the remaining complete pages, ties to the lower
 // page id.
 //
-// Scores are read once: thread t keeps pages t, t + 1024, ... (up to NPT of
+// Scores are read once: thread t keeps pages t, t + NT, ... (up to NPT of
 // them) in registers for both the normaliser and sigma. A generic variant
 // (NPT = 0) loops over global memory for longer contexts.
 //
@@ -22,361 +22,30 @@
 // block-wide scan over page flags.
 #include "common.h"
 #include "kernels.h"
+#include "select_unit.h"
 
 namespace locks {
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelLdsKeys = 16384;  // sigma keys kept in LDS up to this many pages
-constexpr int kSelBins = 2048;
-constexpr int kSelDigit = 11;
 
-namespace {
-
-// ---- wave-wide helpers on DPP (no LDS permutes) ----
-// inclusive prefix sum over the 64 lanes: row_shr 1/2/4/8 inside each row of
-// 16 lanes, then row_bcast 15 / 31 carry the row totals forward
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return v;
+// NT threads, NPT register pages per thread (0: loop over global memory)
+template <int NT, int NPT>
+__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
+  __shared__ SelectLds<NT, kSelLdsKeys> lds;
+  select_unit<NT, NPT, kSelLdsKeys>(a, blockIdx.y, blockIdx.x, lds);
 }
 
-// max / min of a uint32 over the wave (uniform result)
-template <bool kMax>
-__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
-  auto op = [](uint32_t x, uint32_t y) { return kMax ? (x > y ? x : y) : (x < y ? x : y); };
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor1, 0xf, 0xf, false));
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor2, 0xf, 0xf, false));
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xf, 0xf, false));
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppMirror, 0xf, 0xf, false));
-  const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
-  return op(op(r0, r1), op(r2, r3));
-}
-
-// float max / sum over the wave (uniform result)
-__device__ __forceinline__ float wave_max(float v) {
-  v = group_max<16>(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  v = group_sum<16>(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (r0 + r1) + (r2 + r3);
-}
-
-// exclusive scan over the block; `tot` receives the block total. One barrier:
-// the caller puts another barrier between two uses of the same wsum.
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int inc = wave_incl_scan(v);
-  if (lane == 63) wsum[wave] = inc;
-  __syncthreads();
-  int before = 0;
-  tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int x = wsum[w];
-    before += w < wave ? x : 0;
-    tot += x;
-  }
-  return before + inc - v;
-}
-
-}  // namespace
-
-template <int NPT>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
-  __shared__ uint32_t keys_lds[kSelLdsKeys];
-  __shared__ uint32_t hist[2][kSelBins];
-  __shared__ float red_m[kSelWaves][8];
-  __shared__ float red_s[kSelWaves][8];
-  __shared__ uint32_t redu[kSelWaves][2];
-  __shared__ int wsum[kSelWaves];
-  __shared__ int pick_s[3];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int P = a.P, G = a.G, k = a.k;
-  const float* srow = a.scores + ((int64_t)b * a.Hkv * G + (int64_t)h * G) * a.max_pages;
-  // the register path loads its scores before the length is known (pages up
-  // to max_pages are addressable), so both loads are in flight together
-  constexpr int kRegs = NPT > 0 ? NPT : 1;
-  float sc[kRegs][8];
-  if constexpr (NPT > 0) {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int j = tid + kSelThreads * i;
-#pragma unroll
-      for (int g = 0; g < 8; ++g) sc[i][g] = (g < G && j < a.max_pages) ? srow[(int64_t)g * a.max_pages + j] : 0.f;
-    }
-  }
-  const int T = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.max_pages, P));
-  const int J = (T + P - 1) / P;
-  const int Jc = T / P;
-  int32_t* sel_row = a.selected + ((int64_t)b * a.Hkv + h) * k;
-
-  if (J <= k) {
-    for (int t = tid; t < k; t += kSelThreads) sel_row[t] = t < J ? t : -1;
-    return;
-  }
-
-  float* sig_row = a.sigma + ((int64_t)b * a.Hkv + h) * a.max_pages;
-  const bool keys_in_lds = Jc <= kSelLdsKeys;
-  uint32_t* keys = keys_in_lds ? keys_lds : reinterpret_cast<uint32_t*>(sig_row);
-  auto is_cand = [&](int j) { return j >= 1 && j < Jc && j != J - 1; };
-  for (int x = tid; x < kSelBins; x += kSelThreads) hist[0][x] = 0;
-
-  // ---- per-head normaliser log Z_g: block max, then block sum of
-  // 2^(s - max); each reduction is DPP inside the waves, one LDS exchange and
-  // one barrier, with every thread combining the wave results itself ----
-  float mx[8];
-#pragma unroll
-  for (int g = 0; g < 8; ++g) mx[g] = -INFINITY;
-  if constexpr (NPT > 0) {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int j = tid + kSelThreads * i;
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        if (!(g < G && j < Jc)) sc[i][g] = -INFINITY;
-        mx[g] = fmaxf(mx[g], sc[i][g]);
-      }
-    }
-  } else {
-    for (int j = tid; j < Jc; j += kSelThreads)
-#pragma unroll
-      for (int g = 0; g < 8; ++g)
-        if (g < G) mx[g] = fmaxf(mx[g], srow[(int64_t)g * a.max_pages + j]);
-  }
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    if (g < G) {
-      const float r = wave_max(mx[g]);
-      if (lane == 0) red_m[wave][g] = r;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    if (g < G) {
-      float r = red_m[0][g];
-#pragma unroll
-      for (int w = 1; w < kSelWaves; ++w) r = fmaxf(r, red_m[w][g]);
-      mx[g] = r;
-    }
-  }
-  float sm[8];
-#pragma unroll
-  for (int g = 0; g < 8; ++g) sm[g] = 0.f;
-  if constexpr (NPT > 0) {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i)
-#pragma unroll
-      for (int g = 0; g < 8; ++g)
-        if (g < G && mx[g] > -INFINITY) sm[g] += exp2_fast((sc[i][g] - mx[g]) * kLog2e);
-  } else {
-    for (int j = tid; j < Jc; j += kSelThreads)
-#pragma unroll
-      for (int g = 0; g < 8; ++g)
-        if (g < G && mx[g] > -INFINITY) sm[g] += exp2_fast((srow[(int64_t)g * a.max_pages + j] - mx[g]) * kLog2e);
-  }
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    if (g < G) {
-      const float r = wave_sum(sm[g]);
-      if (lane == 0) red_s[wave][g] = r;
-    }
-  }
-  __syncthreads();
-  float lz[8];
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    lz[g] = -INFINITY;
-    if (g < G && mx[g] > -INFINITY) {
-      float r = red_s[0][g];
-#pragma unroll
-      for (int w = 1; w < kSelWaves; ++w) r += red_s[w][g];
-      lz[g] = mx[g] + log2_fast(r) * kLn2;
-    }
-  }
-
-  // ---- sigma_j, its sortable key, and the spread of candidate keys ----
-  const float log2G = log2_fast((float)G);
-  uint32_t kmax = 0u, kmin = 0xffffffffu;
-  auto sigma_key = [&](int j, const float* sv) {
-    float tg[8];
-    float m = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      tg[g] = -INFINITY;
-      if (g < G && lz[g] > -INFINITY) {
-        tg[g] = (sv[g] - lz[g]) * kLog2e;
-        m = fmaxf(m, tg[g]);
-      }
-    }
-    float s = 0.f;
-#pragma unroll
-    for (int g = 0; g < 8; ++g)
-      if (g < G && m > -INFINITY) s += exp2_fast(tg[g] - m);
-    const float sigma = m > -INFINITY ? (m + log2_fast(s) - log2G) * kLn2 : -INFINITY;
-    const uint32_t key = float_key(sigma);
-    if (keys_in_lds) {
-      keys[j] = key;
-      sig_row[j] = sigma;
-    } else {
-      sig_row[j] = __uint_as_float(key);  // global scratch holds the key; rewritten below
-    }
-    if (is_cand(j)) {
-      kmax = key > kmax ? key : kmax;
-      kmin = key < kmin ? key : kmin;
-    }
-  };
-  if constexpr (NPT > 0) {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int j = tid + kSelThreads * i;
-      if (j < Jc) sigma_key(j, sc[i]);
-    }
-  } else {
-    for (int j = tid; j < Jc; j += kSelThreads) {
-      float sv[8];
-#pragma unroll
-      for (int g = 0; g < 8; ++g) sv[g] = g < G ? srow[(int64_t)g * a.max_pages + j] : 0.f;
-      sigma_key(j, sv);
-    }
-  }
-  kmax = wave_minmax_u32<true>(kmax);
-  kmin = wave_minmax_u32<false>(kmin);
-  if (lane == 0) { redu[wave][0] = kmax; redu[wave][1] = kmin; }
-  __syncthreads();  // also publishes keys[] and the cleared hist[0]
-  kmax = redu[0][0];
-  kmin = redu[0][1];
-#pragma unroll
-  for (int w = 1; w < kSelWaves; ++w) {
-    kmax = redu[w][0] > kmax ? redu[w][0] : kmax;
-    kmin = redu[w][1] < kmin ? redu[w][1] : kmin;
-  }
-
-  // ---- radix select of the K best candidates ----
-  int ncand = Jc - 1 - ((J - 1 >= 1 && J - 1 < Jc) ? 1 : 0);
-  if (ncand < 0) ncand = 0;
-  const int K = min(k - 2, ncand);
-  const int idb = a.idbits;
-  const uint64_t idmask = ((uint64_t)1 << idb) - 1;
-  auto key64 = [&](int j) -> uint64_t { return ((uint64_t)keys[j] << idb) | (idmask - (uint64_t)j); };
-
-  // highest bit in which two candidate keys can differ: within sigma's key
-  // when the keys differ, else within the page id
-  int hi = kmax != kmin ? idb + 32 - __builtin_clz(kmax ^ kmin) : idb;
-  // common bits above `hi` (taken from the largest key)
-  uint64_t prefix = (((uint64_t)kmax << idb) >> hi) << hi;
-  int kr = K;
-  const bool take_all = K >= ncand;  // every candidate fits
-  int cur = 0;
-  while (!take_all && hi > 0) {
-    const int lo = hi > kSelDigit ? hi - kSelDigit : 0;
-    const uint32_t dmask = (1u << (hi - lo)) - 1u;
-    uint32_t* hc = hist[cur];
-    for (int j = tid; j < Jc; j += kSelThreads) {
-      if (!is_cand(j)) continue;
-      const uint64_t kv = key64(j);
-      if ((kv >> hi) != (prefix >> hi)) continue;
-      atomicAdd(&hc[(uint32_t)(kv >> lo) & dmask], 1u);
-    }
-    __syncthreads();
-    // bins in descending order, kPer per thread; the next pass's buffer is
-    // cleared meanwhile
-    constexpr int kPer = kSelBins / kSelThreads;
-    const int top = kSelBins - 1 - tid * kPer;
-    int local = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) local += (int)hc[top - i];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) hist[cur ^ 1][top - i] = 0;
-    int tot;
-    const int before = block_excl_scan(local, wsum, tot);
-    if (before < kr && before + local >= kr) {
-      int acc = before;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int c = (int)hc[top - i];
-        if (acc + c >= kr) {
-          pick_s[0] = top - i;
-          pick_s[1] = kr - acc;  // still needed from this bin
-          pick_s[2] = c;
-          break;
-        }
-        acc += c;
-      }
-    }
-    __syncthreads();
-    const int dsel = pick_s[0];
-    const int need = pick_s[1];
-    const int cnt = pick_s[2];
-    prefix |= (uint64_t)dsel << lo;
-    hi = lo;
-    kr = need;
-    cur ^= 1;
-    if (cnt == need) break;  // the whole bin is taken
-  }
-
-  // ---- ascending output: sink, current and the chosen candidates ----
-  auto chosen = [&](int j) -> bool {
-    if (j == 0 || j == J - 1) return true;
-    if (!is_cand(j) || K == 0) return false;
-    if (take_all) return true;
-    return (key64(j) >> hi) >= (prefix >> hi);
-  };
-  const int ppt = (J + kSelThreads - 1) / kSelThreads;
-  const int j0 = tid * ppt;
-  const int j1 = min(J, j0 + ppt);
-  int cnt = 0;
-  for (int j = j0; j < j1; ++j) cnt += chosen(j) ? 1 : 0;
-  int total;
-  int pos = block_excl_scan(cnt, wsum, total);
-  for (int j = j0; j < j1; ++j) {
-    if (chosen(j)) {
-      if (pos < k) sel_row[pos] = j;
-      ++pos;
-    }
-  }
-  for (int t = total + tid; t < k; t += kSelThreads) sel_row[t] = -1;
-
-  // when the keys lived in the global scratch, leave sigma there as documented
-  if (!keys_in_lds) {
-    __syncthreads();
-    for (int j = tid; j < Jc; j += kSelThreads) {
-      const uint32_t key = keys[j];
-      const uint32_t u = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
-      sig_row[j] = key == 0u ? __uint_as_float(0x7fc00000u) : __uint_as_float(u);
-    }
-  }
-}
-
+// Up to 2048 pages, 512 threads with 4 pages each: the selection is a chain
+// of block-wide steps, and a smaller block shortens every barrier (measured
+// faster than 1024 threads x 2 pages). Longer contexts use 1024 threads.
 hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t stream) {
   dim3 grid(a.Hkv, batch);
-  if (a.max_pages <= 2 * kSelThreads)
-    hipLaunchKernelGGL(select_kernel<2>, grid, dim3(kSelThreads), 0, stream, a);
-  else if (a.max_pages <= 8 * kSelThreads)
-    hipLaunchKernelGGL(select_kernel<8>, grid, dim3(kSelThreads), 0, stream, a);
+  if (a.max_pages <= 512 * 4)
+    hipLaunchKernelGGL((select_kernel<512, 4>), grid, dim3(512), 0, stream, a);
+  else if (a.max_pages <= 1024 * 8)
+    hipLaunchKernelGGL((select_kernel<1024, 8>), grid, dim3(1024), 0, stream, a);
   else
-    hipLaunchKernelGGL(select_kernel<0>, grid, dim3(kSelThreads), 0, stream, a);
+    hipLaunchKernelGGL((select_kernel<1024, 0>), grid, dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -18,349 +18,16 @@
 // the splits by LSE and writes the output.
 #include "common.h"
 #include "kernels.h"
+#include "decode_split.h"
 
 namespace locks {
 
-constexpr int kDecWaves = 4;
-constexpr int kDecTile = 16;
-constexpr int kDecTilesPerWave = 2;
-constexpr int kDecTilesPerWg = kDecWaves * kDecTilesPerWave;
-
-namespace {
-
-template <typename T, int D>
-struct QkMfma;
-
-template <int D>
-struct QkMfma<bf16_t, D> {
-  static constexpr int kSteps = D / 32;
-  using Op = bf16x8_t;
-  static __device__ __forceinline__ Op zero() { return Op{0, 0, 0, 0, 0, 0, 0, 0}; }
-  // row element offset of step s for lane group kg
-  static __device__ __forceinline__ int off(int s, int kg) { return s * 32 + kg * 8; }
-  static __device__ __forceinline__ Op load_nt(const bf16_t* p) { return __builtin_bit_cast(Op, ld_nt4(p)); }
-  static __device__ __forceinline__ Op load(const bf16_t* p) { return *reinterpret_cast<const Op*>(p); }
-  static __device__ __forceinline__ f32x4_t mfma(Op a, Op b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <int D>
-struct QkMfma<float, D> {
-  static constexpr int kSteps = D / 4;
-  using Op = float;
-  static __device__ __forceinline__ Op zero() { return 0.f; }
-  static __device__ __forceinline__ int off(int s, int kg) { return s * 4 + kg; }
-  static __device__ __forceinline__ Op load_nt(const float* p) { return __uint_as_float(ld_nt1(p)); }
-  static __device__ __forceinline__ Op load(const float* p) { return *p; }
-  static __device__ __forceinline__ f32x4_t mfma(Op a, Op b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-  }
-};
-
-// 8 consecutive V elements of one row as raw words (bf16: 4 words, fp32: 8)
-template <typename T>
-struct VRow {
-  static constexpr int kWords = 8 * (int)sizeof(T) / 4;
-  uint32_t w[kWords];
-  __device__ __forceinline__ void load(const T* p) { ld_nt_words<kWords>(p, w); }
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int i = 0; i < kWords; ++i) w[i] = 0u;
-  }
-  __device__ __forceinline__ float at(int e) const {
-    if constexpr (sizeof(T) == 2) return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-    else return __uint_as_float(w[e]);
-  }
-};
-
-}  // namespace
-
-template <typename T, int D, int GQ>
 // bf16 with G <= 4: 4 workgroups (16 waves) per CU, so the whole grid of the
 // common shapes is resident at once; G = 8 and fp32 need more registers.
+template <typename T, int D, int GQ>
 __global__ __launch_bounds__(256, (sizeof(T) == 2 && GQ <= 4) ? 4 : 2) void sparse_decode_kernel(DecodeArgs a) {
-  using Q = QkMfma<T, D>;
-  constexpr int G = GQ;
-  constexpr int NC = D / 8;  // 8-wide column slices; PV lanes: 16 slices x 4 token groups per pass
-  static_assert(NC % 8 == 0, "d must be a multiple of 64");
-  constexpr int kColPasses = NC >= 16 ? NC / 16 : 1;  // d = 64: lanes with c >= 8 idle
-  __shared__ __attribute__((aligned(16))) float pbuf[kDecWaves][4][G][4];
-  __shared__ float abuf[kDecWaves][G];
-  __shared__ __attribute__((aligned(16))) float mo[kDecWaves][4][G][D];
-  __shared__ float mm[kDecWaves][G];
-  __shared__ float ml[kDecWaves][G];
-  __shared__ int last_s;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // uniform: tile lookups use scalar loads
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int P = a.P;
-  const int Hq = a.Hkv * G;
-  const int Tl = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.max_pages, P));
-  const int J = (Tl + P - 1) / P;
-  const int64_t unit = (int64_t)b * a.Hkv + h;
-  const int32_t* sel = a.selected + unit * a.k;
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
-  const T* kp = reinterpret_cast<const T*>(a.k_pool);
-  const T* vp = reinterpret_cast<const T*>(a.v_pool);
-  const float zscale = a.scale * kLog2e;
-  const int tiles_per_page = P / kDecTile;
-
-  // MFMA roles: n = head column / token row inside a tile, kg = k group
-  const int n = lane & 15;
-  const int kg = lane >> 4;
-  // PV roles: c = 8-column slice, tg = token group (4 tokens)
-  const int c = lane & 15;
-  const int tg = lane >> 4;
-  const bool c_ok = c < NC;
-
-  typename Q::Op qb[Q::kSteps];
-  {
-    const T* qrow = reinterpret_cast<const T*>(a.q) + ((int64_t)b * Hq + (int64_t)h * G + (n < G ? n : 0)) * D;
-#pragma unroll
-    for (int s = 0; s < Q::kSteps; ++s) qb[s] = n < G ? Q::load(qrow + Q::off(s, kg)) : Q::zero();
-  }
-
-  // ---- locate this wave's tiles (scalar loads), then issue every K/V load ----
-  int ntok[kDecTilesPerWave];
-  int64_t tile_off[kDecTilesPerWave];
-  int jsel[kDecTilesPerWave];
-  const int slot_end = min((split + 1) * a.pages_per_split, a.k);
-#pragma unroll
-  for (int i = 0; i < kDecTilesPerWave; ++i) {
-    const int ti = wave_u + kDecWaves * i;
-    const int slot = split * a.pages_per_split + ti / tiles_per_page;
-    jsel[i] = slot < slot_end ? sel[slot] : -1;
-  }
-#pragma unroll
-  for (int i = 0; i < kDecTilesPerWave; ++i) {
-    const int ti = wave_u + kDecWaves * i;
-    const int sub = ti % tiles_per_page;
-    const int j = jsel[i];
-    int nt = 0;
-    int64_t off = 0;
-    if (j >= 0 && j < J) {
-      const int blk = bt[j];
-      if (blk >= 0 && (int64_t)blk < a.num_blocks) {
-        nt = min(P, Tl - j * P) - sub * kDecTile;
-        nt = nt < 0 ? 0 : (nt > kDecTile ? kDecTile : nt);
-        off = (((int64_t)blk * a.Hkv + h) * P + sub * kDecTile) * D;
-      }
-    }
-    ntok[i] = nt;
-    tile_off[i] = off;
-  }
-  // Loads are unconditional (an empty tile reads row 0 of the pool, a lane
-  // past the valid tokens reads the tile's first row) so that no load sits
-  // inside a branch; K rows past ntok only reach S rows that are masked to
-  // -inf, and V rows past ntok are zeroed below.
-  typename Q::Op ka[kDecTilesPerWave][Q::kSteps];
-  VRow<T> vr[kDecTilesPerWave][kColPasses][4];
-  const int cc = c_ok ? c : 0;
-#pragma unroll
-  for (int i = 0; i < kDecTilesPerWave; ++i) {
-    const T* kt = kp + tile_off[i];
-    const T* vt = vp + tile_off[i];
-    const int krow = n < ntok[i] ? n : 0;
-#pragma unroll
-    for (int s = 0; s < Q::kSteps; ++s) ka[i][s] = Q::load_nt(kt + (int64_t)krow * D + Q::off(s, kg));
-#pragma unroll
-    for (int cp = 0; cp < kColPasses; ++cp)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = 4 * tg + e;
-        vr[i][cp][e].load(vt + (int64_t)(tok < ntok[i] ? tok : 0) * D + (cp * 16 + cc) * 8);
-      }
-  }
-#pragma unroll
-  for (int i = 0; i < kDecTilesPerWave; ++i) {
-    if (ntok[i] < kDecTile || !c_ok) {
-#pragma unroll
-      for (int cp = 0; cp < kColPasses; ++cp)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (!c_ok || 4 * tg + e >= ntok[i]) vr[i][cp][e].zero();
-    }
-  }
-
-  // ---- online softmax and P V over the tiles ----
-  float m_run = -INFINITY, l_run = 0.f;  // head n, valid in lanes n < G
-  float o[kColPasses][G][8];
-#pragma unroll
-  for (int cp = 0; cp < kColPasses; ++cp)
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[cp][g][e] = 0.f;
-
-#pragma unroll
-  for (int i = 0; i < kDecTilesPerWave; ++i) {
-    if (ntok[i] == 0) continue;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < Q::kSteps; ++s) acc = Q::mfma(ka[i][s], qb[s], acc);
-    // lane holds S[token 4 kg + e][head n]
-    float z[4];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      z[e] = 4 * kg + e < ntok[i] ? acc[e] * zscale : -INFINITY;
-      mt = fmaxf(mt, z[e]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    const float m_new = fmaxf(m_run, mt);          // finite: the tile has a valid token
-    const float alpha = exp2_fast(m_run - m_new);  // m_run = -inf -> 0
-    float pe[4];
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pe[e] = exp2_fast(z[e] - m_new);
-      ps += pe[e];
-    }
-    ps += __shfl_xor(ps, 16, kWave);
-    ps += __shfl_xor(ps, 32, kWave);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-    if (n < G) {
-      *reinterpret_cast<f32x4_t*>(&pbuf[wave][kg][n][0]) = f32x4_t{pe[0], pe[1], pe[2], pe[3]};
-      if (kg == 0) abuf[wave][n] = alpha;
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float al = abuf[wave][g];
-      const f32x4_t pv = *reinterpret_cast<const f32x4_t*>(&pbuf[wave][tg][g][0]);
-#pragma unroll
-      for (int cp = 0; cp < kColPasses; ++cp)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float x = o[cp][g][e] * al;
-          x = fmaf(pv[0], vr[i][cp][0].at(e), x);
-          x = fmaf(pv[1], vr[i][cp][1].at(e), x);
-          x = fmaf(pv[2], vr[i][cp][2].at(e), x);
-          x = fmaf(pv[3], vr[i][cp][3].at(e), x);
-          o[cp][g][e] = x;
-        }
-    }
-    wave_lds_sync();
-  }
-
-  // ---- merge the waves of the workgroup ----
-  if (c_ok) {
-#pragma unroll
-    for (int cp = 0; cp < kColPasses; ++cp)
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float* dst = &mo[wave][tg][g][(cp * 16 + c) * 8];
-        *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{o[cp][g][0], o[cp][g][1], o[cp][g][2], o[cp][g][3]};
-        *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{o[cp][g][4], o[cp][g][5], o[cp][g][6], o[cp][g][7]};
-      }
-  }
-  if (kg == 0 && n < G) { mm[wave][n] = m_run; ml[wave][n] = l_run; }
-  __syncthreads();
-
-  // Partials are published with device-scope (write-through) stores and read
-  // back with device-scope loads, so no cache-wide write-back or invalidate
-  // is needed: the stores of every wave are complete (vmcnt 0) before the
-  // arrival counter moves, and the merging workgroup loads only after it has
-  // seen the last arrival.
-  const int splits = gridDim.x;
-  float* part_o = a.part_o + (unit * splits + split) * (int64_t)(G * D);
-  float* part_l = a.part_lse + (unit * splits + split) * (int64_t)G;
-  for (int x = threadIdx.x; x < G * D; x += 256) {
-    const int g = x / D;
-    const int e = x - g * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, mm[w][g]);
-    float L = 0.f, O = 0.f;
-    if (M > -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
-        if (mm[w][g] > -INFINITY) {
-          const float cw = exp2_fast(mm[w][g] - M);
-          L += cw * ml[w][g];
-          O += cw * (mo[w][0][g][e] + mo[w][1][g][e] + mo[w][2][g][e] + mo[w][3][g][e]);
-        }
-      }
-    }
-    __hip_atomic_store(&part_o[x], L > 0.f ? O / L : 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (e == 0)
-      __hip_atomic_store(&part_l[g], L > 0.f ? (M + log2_fast(L)) * kLn2 : -INFINITY, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  // ---- the last workgroup of this (sequence, KV head) merges the splits ----
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&a.counters[unit], 1);
-    last_s = prev == splits - 1;
-  }
-  __syncthreads();
-  if (!last_s) return;
-  const float* po = a.part_o + unit * splits * (int64_t)(G * D);
-  const float* pl = a.part_lse + unit * splits * (int64_t)G;
-  // every output of this thread (kNx of them) and splits in chunks of
-  // kMergeChunk: all loads of a chunk are issued before any is used, then the
-  // chunk is folded into a running (M, L, O) per output
-  constexpr int kMergeChunk = 16;
-  constexpr int kNx = (G * D + 255) / 256;
-  float M[kNx], L[kNx], O[kNx];
-#pragma unroll
-  for (int xi = 0; xi < kNx; ++xi) { M[xi] = -INFINITY; L[xi] = 0.f; O[xi] = 0.f; }
-  for (int s0 = 0; s0 < splits; s0 += kMergeChunk) {
-    float ls[kNx][kMergeChunk], ov[kNx][kMergeChunk];
-#pragma unroll
-    for (int xi = 0; xi < kNx; ++xi) {
-      const int x = threadIdx.x + 256 * xi;
-      const int xc = x < G * D ? x : 0;
-      const int g = xc / D;
-#pragma unroll
-      for (int i = 0; i < kMergeChunk; ++i) {
-        const int sp = s0 + i < splits ? s0 + i : splits - 1;
-        ls[xi][i] = __hip_atomic_load(&pl[sp * G + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ov[xi][i] = __hip_atomic_load(&po[(int64_t)sp * G * D + xc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-#pragma unroll
-    for (int xi = 0; xi < kNx; ++xi) {
-      float Mc = M[xi];
-#pragma unroll
-      for (int i = 0; i < kMergeChunk; ++i)
-        if (s0 + i < splits) Mc = fmaxf(Mc, ls[xi][i]);
-      if (Mc > -INFINITY) {
-        const float r = exp2_fast((M[xi] - Mc) * kLog2e);  // M = -inf -> 0
-        L[xi] *= r;
-        O[xi] *= r;
-#pragma unroll
-        for (int i = 0; i < kMergeChunk; ++i) {
-          if (s0 + i < splits && ls[xi][i] > -INFINITY) {
-            const float cw = exp2_fast((ls[xi][i] - Mc) * kLog2e);
-            L[xi] += cw;
-            O[xi] = fmaf(cw, ov[xi][i], O[xi]);
-          }
-        }
-        M[xi] = Mc;
-      }
-    }
-  }
-  T* out = reinterpret_cast<T*>(a.out) + ((int64_t)b * Hq + (int64_t)h * G) * D;
-#pragma unroll
-  for (int xi = 0; xi < kNx; ++xi) {
-    const int x = threadIdx.x + 256 * xi;
-    if (x >= G * D) continue;
-    const int g = x / D;
-    out[x] = Elem<T>::from_f32(L[xi] > 0.f ? O[xi] / L[xi] : 0.f);
-    if (a.lse && x % D == 0)
-      a.lse[(int64_t)b * Hq + (int64_t)h * G + g] = L[xi] > 0.f ? M[xi] + log2_fast(L[xi]) * kLn2 : -INFINITY;
-  }
-  if (threadIdx.x == 0) atomicExch(&a.counters[unit], 0);
+  __shared__ DecodeLds<D, GQ> lds;
+  decode_split<T, D, GQ>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x, lds);
 }
 
 int decode_pages_per_split(int page_size) { return kDecTilesPerWg * kDecTile / page_size; }

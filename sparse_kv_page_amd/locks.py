@@ -26,7 +26,8 @@ LOCKS_F32 = 1
 # every exported entry point declared in include/locks.h
 EXPORTED = ("locks_status_string", "locks_version", "locks_summary_record_bytes",
             "locks_workspace_size", "locks_build_summaries", "locks_page_score",
-            "locks_select_pages", "locks_score_select", "locks_sparse_decode")
+            "locks_select_pages", "locks_score_select", "locks_sparse_decode",
+            "locks_decode_step")
 
 
 class LocksError(RuntimeError):
@@ -83,8 +84,11 @@ def lib():
         L.locks_score_select.argtypes = [cp, vp, vp, i64, vp, vp, i32, i32, vp, vp, sz, vp]
         L.locks_sparse_decode.argtypes = [cp, vp, vp, vp, i64, vp, vp, vp, i32, i32, vp, vp, vp,
                                           sz, vp]
+        L.locks_decode_step.argtypes = [cp, vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp, vp,
+                                        sz, vp]
         for name in ("locks_workspace_size", "locks_build_summaries", "locks_page_score",
-                     "locks_select_pages", "locks_score_select", "locks_sparse_decode"):
+                     "locks_select_pages", "locks_score_select", "locks_sparse_decode",
+                     "locks_decode_step"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -169,6 +173,15 @@ def locks_sparse_decode(cfg, q, k_pool, v_pool, num_blocks, block_table, seq_len
                                      int(num_blocks), _ptr(block_table), _ptr(seq_lens),
                                      _ptr(selected), int(batch), int(max_pages), _ptr(out),
                                      _ptr(lse), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def locks_decode_step(cfg, q, summary_pool, k_pool, v_pool, num_blocks, block_table, seq_lens, batch,
+                      max_pages, selected, out, lse, ws, ws_bytes, stream=None):
+    _check("locks_decode_step",
+           lib().locks_decode_step(ctypes.byref(cfg), _ptr(q), _ptr(summary_pool), _ptr(k_pool),
+                                   _ptr(v_pool), int(num_blocks), _ptr(block_table), _ptr(seq_lens),
+                                   int(batch), int(max_pages), _ptr(selected), _ptr(out), _ptr(lse),
+                                   _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 # --------------------------------------------------------------------------

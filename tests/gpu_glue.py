@@ -130,21 +130,23 @@ def gpu_select(wl, cfg, g, head_scores):
     return sel, sig
 
 
-def gpu_decode(wl, cfg, g, sel):
+def gpu_decode(wl, cfg, g, sel, ws=None):
     dt = synth.torch_dtype(wl.kv_dtype)
     out = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), float("nan"), dtype=dt, device=DEV)
     lse = torch.full((wl.batch, wl.num_q_heads), float("nan"), device=DEV)
     nbytes = L.locks_workspace_size(cfg, wl.batch, wl.max_pages)
-    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    if ws is None:
+        ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=DEV)
     L.locks_sparse_decode(cfg, g["q"], g["k_pool"], g["v_pool"], wl.num_blocks, g["block_table"],
                           g["seq_lens"], sel, wl.batch, wl.max_pages, out, lse, ws, nbytes)
     return out, lse
 
 
-def gpu_score_select(wl, cfg, g, pool):
+def gpu_score_select(wl, cfg, g, pool, ws=None):
     sel = torch.full((wl.batch, wl.num_kv_heads, wl.budget_pages), -7, dtype=torch.int32, device=DEV)
     nbytes = L.locks_workspace_size(cfg, wl.batch, wl.max_pages)
-    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    if ws is None:
+        ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=DEV)
     L.locks_score_select(cfg, g["q"], pool, wl.num_blocks, g["block_table"], g["seq_lens"], wl.batch,
                          wl.max_pages, sel, ws, nbytes)
     return sel
@@ -207,3 +209,17 @@ def check_selection(wl, b, sel_gpu, sel_ora, sigma_ora, tol=SCORE_TOL):
         assert j in cand and abs(sigma_ora[j] - kth) <= win, \
             f"page {j} (sigma {sigma_ora[j]}) outside window around {kth}"
     return len(diff)
+
+
+def gpu_decode_step(wl, cfg, g, pool, ws=None):
+    """One fused decode step (locks_decode_step); returns (selected, out, lse)."""
+    dt = synth.torch_dtype(wl.kv_dtype)
+    sel = torch.full((wl.batch, wl.num_kv_heads, wl.budget_pages), -7, dtype=torch.int32, device=DEV)
+    out = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), float("nan"), dtype=dt, device=DEV)
+    lse = torch.full((wl.batch, wl.num_q_heads), float("nan"), device=DEV)
+    nbytes = L.locks_workspace_size(cfg, wl.batch, wl.max_pages)
+    if ws is None:
+        ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    L.locks_decode_step(cfg, g["q"], pool, g["k_pool"], g["v_pool"], wl.num_blocks, g["block_table"],
+                        g["seq_lens"], wl.batch, wl.max_pages, sel, out, lse, ws, nbytes)
+    return sel, out, lse

@@ -88,6 +88,8 @@ def test_config_errors(kw, status):
                                      stream=0),
         lambda: L.locks_sparse_decode(cfg, fake, fake, fake, 10, fake, fake, fake, 1, 4, fake,
                                       None, fake, 1 << 30, stream=0),
+        lambda: L.locks_decode_step(cfg, fake, fake, fake, fake, 10, fake, fake, 1, 4, fake, fake,
+                                    None, fake, 1 << 30, stream=0),
     ]
     for c in calls:
         with pytest.raises(L.LocksError) as ei:
@@ -115,6 +117,12 @@ def test_null_pointers_and_sizes():
                                       None, fake, 1 << 30, stream=0),
         lambda: L.locks_sparse_decode(cfg, fake, fake, fake, 10, fake, fake, fake, 1, 4, None,
                                       None, fake, 1 << 30, stream=0),
+        lambda: L.locks_decode_step(cfg, fake, None, fake, fake, 10, fake, fake, 1, 4, fake, fake,
+                                    None, fake, 1 << 30, stream=0),
+        lambda: L.locks_decode_step(cfg, fake, fake, fake, fake, 10, fake, fake, 1, 4, None, fake,
+                                    None, fake, 1 << 30, stream=0),
+        lambda: L.locks_decode_step(cfg, fake, fake, fake, fake, -1, fake, fake, 1, 4, fake, fake,
+                                    None, fake, 1 << 30, stream=0),
     ]
     for c in cases:
         with pytest.raises(L.LocksError) as ei:
@@ -136,6 +144,11 @@ def test_workspace_checks():
             L.locks_sparse_decode(cfg, fake, fake, fake, 10, fake, fake, fake, 8, 2048, fake, None,
                                   ws, nbytes, stream=0)
         assert ei.value.status == L.LOCKS_E_WORKSPACE
+        with pytest.raises(L.LocksError) as ei:
+            L.locks_decode_step(cfg, fake, fake, fake, fake, 10, fake, fake, 8, 2048, fake, fake, None,
+                                ws, nbytes, stream=0)
+        assert ei.value.status == L.LOCKS_E_WORKSPACE
+
 
 
 def test_workspace_monotone_and_empty_calls():
@@ -150,3 +163,5 @@ def test_workspace_monotone_and_empty_calls():
     L.locks_score_select(cfg, None, None, 0, None, None, 0, 0, None, None, 0, stream=0)
     L.locks_sparse_decode(cfg, None, None, None, 0, None, None, None, 0, 0, None, None, None, 0,
                           stream=0)
+    L.locks_decode_step(cfg, None, None, None, None, 0, None, None, 0, 0, None, None, None, None, 0,
+                        stream=0)

@@ -464,3 +464,132 @@ def test_headline_sampled():
             p6g = vt.T @ vt
             p6o = vt_o[i, :6].T @ vt_o[i, :6]
             assert np.linalg.norm(p6o @ p6g @ p6o - p6o) <= 5e-2
+
+
+# --------------------------------------------------------------------------
+# whole decode step (score/select then decode on one workspace) vs the oracle
+# and the stages
+# --------------------------------------------------------------------------
+# a ragged batch: partial current pages, a sequence with J <= k and one with a
+# single page
+RAGGED = synth.Workload("ragged_bf16", 5, 2, 4, 128, 64,
+                       (64 * 40 + 37, 64 * 24, 64 * 9 + 1, 64 * 5, 17), 8, 8, "bf16", "bf16",
+                       n_needles=3, extra_blocks=4)
+
+
+def test_decode_step_end_to_end():
+    wl = RAGGED
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=21)
+    summ, _, _ = gg.oracle_summaries(wl, data)
+    pool = gg.pool_from_summaries(wl, cfg, summ)
+    sel, out, lse = gg.gpu_decode_step(wl, cfg, g, pool)
+    torch.cuda.synchronize()
+    sel, out, lse = sel.cpu(), gg.f64(out.cpu()), gg.f64(lse.cpu())
+    same = units = 0
+    for b in range(wl.batch):
+        _, J, Jc = gg.lens(wl, b)
+        for h in range(wl.num_kv_heads):
+            units += 1
+            if J > wl.budget_pages:
+                blocks = [int(x) for x in data["block_table"][b, :Jc]]
+                mu = np.stack([summ[(x, h)][0] for x in blocks])
+                vt = np.stack([summ[(x, h)][1] for x in blocks])
+                cf = np.stack([summ[(x, h)][2] for x in blocks])
+                s_o = gg.oracle_unit_scores(wl, data, b, h, mu, vt, cf)
+            else:
+                s_o = None
+            sel_o, sigma_o = gg.oracle_unit_select(wl, b, s_o)
+            if gg.check_selection(wl, b, sel[b, h].tolist(), sel_o.tolist(), sigma_o) == 0:
+                same += 1
+                o_ref, lse_ref = gg.oracle_unit_attend(wl, data, b, h, sel_o)
+                sl = slice(h * wl.group, (h + 1) * wl.group)
+                assert np.max(np.abs(out[b, sl] - o_ref)) <= gg.out_tol(wl)
+                assert np.max(np.abs(lse[b, sl] - lse_ref)) <= 1e-3 * max(1.0, float(np.max(np.abs(lse_ref))))
+    assert same >= units - 1
+
+
+@pytest.mark.parametrize("wl", [RAGGED, W["llama8b_128k_b8"], W["llama8b_512k"].with_(rank=8)],
+                         ids=["ragged_bf16", "llama8b_128k_b8", "llama8b_512k_r8"])
+def test_decode_step_matches_stages(wl):
+    """The step equals locks_score_select then locks_sparse_decode, bit for bit."""
+    cfg = _cfg(wl)
+    d = synth.generate(wl, 4, gg.DEV)
+    pool = gg.synthetic_pool(wl, cfg, seed=4)
+    sel_f, out_f, lse_f = gg.gpu_decode_step(wl, cfg, d, pool)
+    sel_s = gg.gpu_score_select(wl, cfg, d, pool)
+    out_s, lse_s = gg.gpu_decode(wl, cfg, d, sel_s)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_f, sel_s)
+    assert torch.equal(out_f.view(torch.uint8), out_s.view(torch.uint8))
+    assert torch.equal(lse_f, lse_s)
+
+
+def test_decode_step_repeats_and_resets():
+    """Counters and flags return to zero: repeated calls on one workspace give
+    bitwise identical results, also after a call with a different batch."""
+    wl = RAGGED
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=22)
+    pool = gg.synthetic_pool(wl, cfg, seed=22)
+    nbytes = L.locks_workspace_size(cfg, wl.batch, wl.max_pages)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=gg.DEV)
+    ref = gg.gpu_decode_step(wl, cfg, g, pool, ws)
+    # same pool (num_blocks) for the smaller batch
+    small = wl.with_(batch=2, seq_lens=wl.seq_lens[:2], extra_blocks=wl.num_blocks - 2 * wl.max_pages)
+    g2 = dict(g, block_table=g["block_table"][:2].contiguous(), seq_lens=g["seq_lens"][:2].contiguous(),
+              q=g["q"][:2].contiguous())
+    for it in range(3):
+        got = gg.gpu_decode_step(wl, cfg, g, pool, ws)
+        got_small = gg.gpu_decode_step(small, cfg, g2, pool, ws)
+        torch.cuda.synchronize()
+        for a_, b_ in zip(ref, got):
+            assert torch.equal(a_.contiguous().view(torch.uint8), b_.contiguous().view(torch.uint8))
+        assert torch.equal(got_small[0], ref[0][:2])
+        assert torch.equal(got_small[1], ref[1][:2])
+    # control words are back to zero (first bytes of the workspace)
+    assert int(ws[:256].count_nonzero()) == 0
+
+
+def test_decode_step_shares_workspace_with_stages():
+    """The staged entry points write only scratch: staged calls and fused
+    steps interleaved on one workspace give the results of each alone, and
+    the control words stay zero between calls."""
+    wl = RAGGED
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=24)
+    pool = gg.synthetic_pool(wl, cfg, seed=24)
+    ref_f = gg.gpu_decode_step(wl, cfg, g, pool)
+    ref_sel = gg.gpu_score_select(wl, cfg, g, pool)
+    ref_out, ref_lse = gg.gpu_decode(wl, cfg, g, ref_sel)
+    torch.cuda.synchronize()
+    nbytes = L.locks_workspace_size(cfg, wl.batch, wl.max_pages)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=gg.DEV)
+    ctl = wl.batch * wl.num_kv_heads * 4
+    for it in range(2):
+        sel = gg.gpu_score_select(wl, cfg, g, pool, ws)
+        out, lse = gg.gpu_decode(wl, cfg, g, sel, ws)
+        got_f = gg.gpu_decode_step(wl, cfg, g, pool, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, ref_sel)
+        assert torch.equal(out.view(torch.uint8), ref_out.view(torch.uint8))
+        assert torch.equal(lse, ref_lse)
+        for a_, b_ in zip(ref_f, got_f):
+            assert torch.equal(a_.contiguous().view(torch.uint8), b_.contiguous().view(torch.uint8))
+        assert int(ws[:ctl].count_nonzero()) == 0
+
+
+def test_decode_step_large_budget():
+    """A large budget (260 pages of 16, over 33 decode splits) gives exactly
+    the staged results."""
+    wl = synth.Workload("budget_260", 2, 1, 4, 64, 16, (16 * 300 + 5, 16 * 280), 4, 260, "bf16", "bf16",
+                        n_needles=2)
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=23)
+    pool = gg.synthetic_pool(wl, cfg, seed=23)
+    sel_f, out_f, _ = gg.gpu_decode_step(wl, cfg, g, pool)
+    sel_s = gg.gpu_score_select(wl, cfg, g, pool)
+    out_s, _ = gg.gpu_decode(wl, cfg, g, sel_s)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_f, sel_s)
+    assert torch.equal(out_f, out_s)
