@@ -44,11 +44,17 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run 3 plain device copies of MIB MiB "
                          "(reference dispatches for scaling memory counters)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: turn the rocprofv3 outputs of the commands in profiles/*.md into "
+                         "profiles/traffic_<workload>.json and the two summaries")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.workload, *args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by (sequence, KV head) with no exchange, so N GPUs would run N "
@@ -172,19 +178,7 @@ def main():
         build_ms = b0.elapsed_time(b1) / args.steps
     stage_us["build_step"] = 1e3 * build_ms
 
-    # ---- algorithmic bytes (what the method must move per step) ----
-    summary_bytes = 0
-    kv_bytes = 0
-    ekv = 2 if wl.kv_dtype == "bf16" else 4
-    for b in range(B):
-        T = int(wl.seq_lens[b])
-        J, Jc = -(-T // P), T // P
-        summary_bytes += Hkv * Jc * rec_bytes
-        if J <= k:
-            A = T
-        else:
-            A = (k - 1) * P + (T - (J - 1) * P)
-        kv_bytes += Hkv * A * 2 * d * ekv
+    summary_bytes, kv_bytes = algorithmic_bytes(wl, rec_bytes)
     step_bytes = summary_bytes + kv_bytes
     step_gbs = step_bytes / (step_ms * 1e-3) / 1e9
     gram_flops = 2.0 * P * d * d * n_full * Hkv
@@ -237,6 +231,165 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def algorithmic_bytes(wl, rec_bytes):
+    """Bytes the method must move per step: the summary record of every
+    complete page and the K/V rows of every attended token (sink, top-(k-2)
+    and the current page's valid tokens; all tokens when J <= k)."""
+    P, k, d, Hkv = wl.page_size, wl.budget_pages, wl.head_dim, wl.num_kv_heads
+    ekv = 2 if wl.kv_dtype == "bf16" else 4
+    summary_bytes = kv_bytes = 0
+    for T in wl.seq_lens:
+        T = int(T)
+        J, Jc = -(-T // P), T // P
+        summary_bytes += Hkv * Jc * rec_bytes
+        A = T if J <= k else (k - 1) * P + (T - (J - 1) * P)
+        kv_bytes += Hkv * A * 2 * d * ekv
+    return summary_bytes, kv_bytes
+
+
+PROFILE_CMDS = {
+    "stats": ("export TMPDIR=/tmp && cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv \\\n"
+              "    -d $R/gpurun_out/prof_stats -o locks -- python3 -u $R/bench.py --steps 20 --warmup 5 "
+              "--no-cpu-baseline"),
+    "fetch": ("export TMPDIR=/tmp && cd /tmp && timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE \\\n"
+              "    --kernel-include-regex 'locks::|copyBuffer' --output-format csv -d $R/gpurun_out/prof_fetch "
+              "-o fetch \\\n    -- python3 -u $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
+              "--copy-calibration 256"),
+    "summarize": ("python bench.py --summarize-profiles gpurun_out/prof_stats gpurun_out/prof_fetch "
+                  "gpurun_out/prof_write"),
+}
+
+KERNEL_PATTERNS = (("page_score", ("page_score_lds_kernel", "page_score_kernel")),
+                   ("select", ("select_kernel",)),
+                   ("sparse_decode", ("sparse_decode_kernel",)),
+                   ("build", ("build_kernel",)))
+
+
+def _clean(name):
+    """`void locks::k<...>(locks::Args)` -> `locks::k<...>`"""
+    if name.startswith("void "):
+        name = name[5:]
+    if name.endswith(")") and "(" in name:
+        name = name[:name.rindex("(")]
+    return name
+
+
+def _kernel_key(name):
+    for key, pats in KERNEL_PATTERNS:
+        if any(p in name for p in pats):
+            return key
+    return None
+
+
+def summarize_profiles(workload, stats_dir, fetch_dir, write_dir):
+    """Write profiles/traffic_<workload>.json, profiles/decode_step_kernels_<workload>.md and
+    profiles/memory_traffic_<workload>.md from rocprofv3 CSV output (kernel stats, one
+    FETCH_SIZE pass, one WRITE_SIZE pass, each pass ending with plain 256 MiB copies)."""
+    import csv
+    import glob
+
+    from sparse_kv_page_amd import locks as L
+    from sparse_kv_page_amd import synth
+
+    wl = synth.WORKLOADS[workload]
+    cfg = L.config_for(wl)
+    summary_bytes, kv_bytes = algorithmic_bytes(wl, L.locks_summary_record_bytes(cfg))
+    alg = {"page_score": summary_bytes, "sparse_decode": kv_bytes}
+
+    def one(pattern):
+        hits = sorted(glob.glob(pattern, recursive=True))
+        if not hits:
+            raise SystemExit(f"no file matches {pattern}")
+        return hits[0]
+
+    stats = {}
+    with open(one(os.path.join(stats_dir, "**", "*kernel_stats.csv"))) as f:
+        for row in csv.DictReader(f):
+            if _clean(row["Name"]).startswith("locks::"):
+                stats[_clean(row["Name"])] = (int(row["Calls"]), float(row["AverageNs"]) / 1e3,
+                                      float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3)
+
+    def counters(d, counter):
+        per_kernel, copies = {}, []
+        with open(one(os.path.join(d, "**", "*counter_collection.csv"))) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                v = float(row["Counter_Value"])
+                name = _clean(row["Kernel_Name"])
+                if "copyBuffer" in name:
+                    copies.append(v)
+                elif name.startswith("locks::"):
+                    per_kernel.setdefault(name, []).append(v)
+        copies = sorted(copies)[-3:]  # the three calibration copies are the largest
+        return {n: sum(v) / len(v) for n, v in per_kernel.items()}, sum(copies) / len(copies), \
+            {n: len(v) for n, v in per_kernel.items()}
+
+    fetch, fetch_copy, calls = counters(fetch_dir, "FETCH_SIZE")
+    write, write_copy, _ = counters(write_dir, "WRITE_SIZE")
+    copy_kib = 256 * 1024.0
+    fs, wsc = copy_kib / fetch_copy, copy_kib / write_copy
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(here, "sparse_kv_page_amd", "csrc")
+    rec = {"workload": workload, "fetch_scale": round(fs, 6), "write_scale": round(wsc, 6),
+           "calibration": f"3 device copies of 256 MiB (__amd_rocclr_copyBuffer): FETCH_SIZE "
+                          f"{fetch_copy:.1f} KiB, WRITE_SIZE {write_copy:.1f} KiB per dispatch",
+           "kernels": {}}
+    rows_t = []
+    for name in sorted(fetch):
+        key = _kernel_key(name)
+        if key is None or key == "build" or name not in write:
+            continue
+        traffic = int(round((fetch[name] * fs + write[name] * wsc) * 1024))
+        a = alg.get(key)
+        avg = next((v[1] for n, v in stats.items() if n == name), None)
+        rec["kernels"][key] = {
+            "symbol": name, "source_sha1": _sha1([os.path.join(csrc, x) for x in KERNEL_SOURCES[key]]),
+            "fetch_kib": round(fetch[name], 1), "write_kib": round(write[name], 1),
+            "hbm_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": a,
+            "avg_duration_ns": round(avg * 1e3, 1) if avg else None, "calls": calls[name]}
+        rows_t.append(f"| {key} (`{name}`) | {fetch[name]:.1f} | {write[name]:.1f} | {traffic:,} | "
+                      f"{a:,} | {traffic / a:.3f} |" if a else
+                      f"| {key} (`{name}`) | {fetch[name]:.1f} | {write[name]:.1f} | {traffic:,} | n/a | n/a |")
+    os.makedirs(os.path.join(here, "profiles"), exist_ok=True)
+    with open(os.path.join(here, "profiles", f"traffic_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+
+    rows_s = [f"| `{n}` | {c} | {a:.2f} | {lo:.2f} | {hi:.2f} |"
+              for n, (c, a, lo, hi) in sorted(stats.items(), key=lambda kv: -kv[1][1])]
+    rates = []
+    for n, (c, a, lo, hi) in stats.items():
+        key = _kernel_key(n)
+        if key in alg:
+            rates.append(f"{key}: {alg[key]:,} B per launch / {a:.2f} us = "
+                         f"{alg[key] / (a * 1e-6) / 1e9:.0f} GB/s ({alg[key] / (a * 1e-6) / 1e9 / HBM_PEAK_GBS:.1%} "
+                         f"of 8 TB/s).")
+    shape = (f"batch {wl.batch}, {wl.num_q_heads} query / {wl.num_kv_heads} KV heads, d = {wl.head_dim}, "
+             f"P = {wl.page_size}, T = {wl.seq_lens[0]}, r = {wl.rank}, k = {wl.budget_pages}, "
+             f"{wl.kv_dtype} K/V and {wl.summary_dtype} summaries")
+    with open(os.path.join(here, "profiles", f"decode_step_kernels_{workload}.md"), "w") as f:
+        f.write(f"# Decode-step kernels, {workload}\n\nWorkload: {shape}; MI355X (gfx950), one GPU, "
+                f"ROCm 7.2.\n\nCommand (repository root on the GPU box = `R`):\n\n    "
+                + PROFILE_CMDS["stats"].replace("\n", "\n    ") +
+                "\n\nThen, without a GPU:\n\n    " + PROFILE_CMDS["summarize"] +
+                "\n\n| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|\n" +
+                "\n".join(rows_s) + "\n\n" + "\n".join(rates) + "\n")
+    with open(os.path.join(here, "profiles", f"memory_traffic_{workload}.md"), "w") as f:
+        f.write(f"# Memory traffic of the decode-step kernels, {workload}\n\nSame workload as "
+                f"decode_step_kernels_{workload}.md. Two counter passes, one counter each, followed by "
+                f"three plain 256 MiB device copies used as the calibration:\n\n    "
+                + PROFILE_CMDS["fetch"].replace("\n", "\n    ") +
+                "\n    (the same with --pmc WRITE_SIZE, -d $R/gpurun_out/prof_write -o write)\n\n"
+                f"Calibration: a 256 MiB copy reads FETCH_SIZE = {fetch_copy:.1f} KiB and WRITE_SIZE = "
+                f"{write_copy:.1f} KiB, so FETCH_SIZE is scaled by {fs:.6f} and WRITE_SIZE by {wsc:.6f}.\n\n"
+                "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled traffic B/launch | algorithmic B/launch "
+                "| ratio |\n|---|---|---|---|---|---|\n" + "\n".join(rows_t) +
+                f"\n\ntraffic_{workload}.json holds these figures with the SHA-1 of the kernel sources "
+                "they were measured on; bench.py reports them only while the sources match.\n")
+    print(json.dumps(rec, indent=1))
 
 
 # the sources each kernel is compiled from (a measured traffic record is
