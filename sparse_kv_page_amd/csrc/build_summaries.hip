@@ -17,10 +17,16 @@
 //  3. Subspace iteration on a 16-column block X: Y = H X (fp32 MFMA), then
 //     X = Y R^-1 from a Cholesky factor of the column-scaled Gram Y^T Y
 //     (columns that collapse are replaced by fresh pseudo-random vectors).
+//     Each pass has two workgroup barriers: the waves' partial Grams meet in
+//     LDS, then every wave factors the 16 x 16 Gram and inverts the factor
+//     in registers (lane l holds row l, broadcasts by readlane) and forms its
+//     own rows of X on the matrix cores.
 //  4. A second Cholesky-QR pass, then Rayleigh-Ritz: T = X^T H X (16 x 16)
-//     diagonalised by parallel cyclic Jacobi; the r largest Ritz pairs give
-//     V = X W_r, each column sign-fixed so its largest-magnitude entry is
-//     positive (lowest index on ties).
+//     diagonalised by parallel cyclic Jacobi (8 disjoint rotations per
+//     round applied in one pass, stopping once the off-diagonal mass is
+//     negligible); the r largest Ritz pairs give V = X W_r, each column
+//     sign-fixed so its largest-magnitude entry is positive (lowest index on
+//     ties).
 //  5. C = D V in fp32 from the unrounded V; mu, V, C are rounded to the
 //     summary dtype independently.
 #include "common.h"
@@ -81,17 +87,14 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
   __shared__ float mu[D];
   __shared__ __attribute__((aligned(16))) float X[D][kBlk];
   __shared__ __attribute__((aligned(16))) float Y[D][kBlk];
-  __shared__ float Mp[4][kBlk][kBlk];
-  __shared__ float Ms[kBlk][kBlk + 1];
-  __shared__ float Lm[kBlk][kBlk + 1];
-  __shared__ float Li[kBlk][kBlk + 1];
-  __shared__ float Ri[kBlk][kBlk];
-  __shared__ float Wm[kBlk][kBlk + 1];
-  __shared__ float sdiag[kBlk];
-  __shared__ int dead[kBlk];
-  __shared__ float rot[8][2];
-  __shared__ int rpq[8][2];
+  __shared__ __attribute__((aligned(16))) float Mp[4][kBlk][kBlk];
+  __shared__ __attribute__((aligned(16))) float RiW[4][kBlk][kBlk];  // each wave's copy of R^-1
+  __shared__ float Ms[2][kBlk][kBlk + 1];  // Rayleigh quotient, ping-pong
+  __shared__ float Wm[2][kBlk][kBlk + 1];  // its eigenvectors, ping-pong
+  __shared__ float jsc[kBlk], joc[kBlk];   // rotation of the index's pair: self / other coefficient
+  __shared__ int jpt[kBlk];                // partner index
   __shared__ int order[kBlk];
+  __shared__ int cur_s;  // which Ms / Wm buffer holds the result
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -192,185 +195,213 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
       for (int i = 0; i < 4; ++i) Y[16 * tc + 4 * (lane >> 4) + i][lane & 15] = yt[t][i];
     }
   };
-  // Sum Mp into Ms (wave 0), symmetrised.
+  // Sum Mp into Ms[0] (wave 0), symmetrised.
   auto reduce_gram = [&]() {
     if (wave == 0) {
       for (int e = lane; e < kBlk * kBlk; e += 64) {
         const int i = e / kBlk, j = e % kBlk;
         const float v = Mp[0][i][j] + Mp[1][i][j] + Mp[2][i][j] + Mp[3][i][j];
         const float vt = Mp[0][j][i] + Mp[1][j][i] + Mp[2][j][i] + Mp[3][j][i];
-        Ms[i][j] = 0.5f * (v + vt);
+        Ms[0][i][j] = 0.5f * (v + vt);
       }
     }
   };
-  // Wave 0: Ri = S L^-T from the Cholesky factor of the column-scaled Ms.
-  auto cholesky_inverse = [&]() {
-    if (wave != 0) return;
+  auto rdl = [](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  // Every wave, in registers (lane l holds row l & 15 of the block Gram M in
+  // a[]): column scaling S (columns with a vanishing norm are dead), Cholesky
+  // S M S = L L^T (right-looking; a column whose pivot vanishes is dead and
+  // gets L = unit column), then L^-1 column by column (lane c forms column c)
+  // and Ri = S L^-T with dead columns zeroed, written to this wave's RiW.
+  // Returns the dead-column mask (uniform).
+  auto chol_rinv = [&](float* am) -> uint32_t {
+    const int row = lane & 15;
+    float sd[kBlk];
     float dmax = 0.f;
-    for (int j = 0; j < kBlk; ++j) dmax = fmaxf(dmax, Ms[j][j]);
-    if (lane < kBlk) {
-      const float dj = Ms[lane][lane];
-      const bool dd = !(dj > 1e-30f * fmaxf(dmax, 1e-30f));
-      dead[lane] = dd ? 1 : 0;
-      sdiag[lane] = dd ? 0.f : 1.0f / sqrtf(dj);
-    }
-    wave_lds_sync();
-    // scaled matrix into Lm (lower triangle becomes L)
-    for (int e = lane; e < kBlk * kBlk; e += 64) {
-      const int i = e / kBlk, j = e % kBlk;
-      Lm[i][j] = Ms[i][j] * sdiag[i] * sdiag[j];
-    }
-    wave_lds_sync();
+#pragma unroll
     for (int j = 0; j < kBlk; ++j) {
-      // column j: v_i = Lm[i][j] - sum_{k<j} L[i][k] L[j][k] for i >= j
-      float v = 0.f;
-      if (lane >= j && lane < kBlk) {
-        v = Lm[lane][j];
-        for (int k = 0; k < j; ++k) v -= Lm[lane][k] * Lm[j][k];
-      }
-      const float vjj = __shfl(v, j, 64);
-      const bool ok = vjj > 1e-12f && !dead[j];
-      const float ljj = ok ? sqrtf(vjj) : 1.0f;
-      if (lane == j) Lm[j][j] = ljj;
-      if (lane > j && lane < kBlk) Lm[lane][j] = ok ? v / ljj : 0.f;
-      if (lane == j && !ok) dead[j] = 1;
-      wave_lds_sync();
+      sd[j] = rdl(am[j], j);  // diagonal
+      dmax = fmaxf(dmax, sd[j]);
     }
-    // Li = L^-1 (lower), column c by forward substitution in lane c
+    uint32_t dead = 0u;
+#pragma unroll
+    for (int j = 0; j < kBlk; ++j) {
+      const bool dd = !(sd[j] > 1e-30f * fmaxf(dmax, 1e-30f));
+      dead |= dd ? 1u << j : 0u;
+      sd[j] = dd ? 0.f : __builtin_amdgcn_rsqf(sd[j]);
+    }
+    float srow = 0.f;
+#pragma unroll
+    for (int j = 0; j < kBlk; ++j) srow = row == j ? sd[j] : srow;
+#pragma unroll
+    for (int c = 0; c < kBlk; ++c) am[c] *= srow * sd[c];
+    // the chain of pivots uses the hardware reciprocal square root (about
+    // 1 ulp): the factor only has to orthonormalise the block to fp32 level
+    float invd[kBlk];  // 1 / L[j][j]
+#pragma unroll
+    for (int j = 0; j < kBlk; ++j) {
+      const float vjj = rdl(am[j], j);
+      const bool ok = vjj > 1e-12f && !((dead >> j) & 1u);
+      const float rj = ok ? __builtin_amdgcn_rsqf(vjj) : 1.0f;
+      invd[j] = rj;
+      const float lij = row > j ? (ok ? am[j] * rj : 0.f) : (row == j ? (ok ? vjj * rj : 1.0f) : 0.f);
+      am[j] = lij;
+      dead |= ok ? 0u : 1u << j;
+#pragma unroll
+      for (int k = j + 1; k < kBlk; ++k) am[k] = fmaf(-lij, rdl(lij, k), am[k]);
+    }
+    // li[i] = (L^-1)[i][row]
+    float li[kBlk];
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i) {
+      float t = row == i ? 1.f : 0.f;
+#pragma unroll
+      for (int k = 0; k < i; ++k) t = fmaf(-rdl(am[k], i), li[k], t);
+      li[i] = t * invd[i];
+    }
+    // Ri[row][j] = s_row * (L^-1)[j][row] for j >= row, live j
     if (lane < kBlk) {
-      const int c = lane;
-      for (int i = 0; i < kBlk; ++i) Li[i][c] = 0.f;
-      Li[c][c] = 1.0f / Lm[c][c];
-      for (int i = c + 1; i < kBlk; ++i) {
-        float s = 0.f;
-        for (int k = c; k < i; ++k) s += Lm[i][k] * Li[k][c];
-        Li[i][c] = -s / Lm[i][i];
-      }
+#pragma unroll
+      for (int j = 0; j < kBlk; ++j) RiW[wave][row][j] = (j >= row && !((dead >> j) & 1u)) ? srow * li[j] : 0.f;
     }
-    wave_lds_sync();
-    for (int e = lane; e < kBlk * kBlk; e += 64) {
-      const int i = e / kBlk, j = e % kBlk;  // Ri[i][j] = s_i * Li[j][i]
-      Ri[i][j] = (j >= i && !dead[j]) ? sdiag[i] * Li[j][i] : 0.f;
-    }
+    return dead;
   };
-  // X = Y Ri (all threads), collapsed columns replaced by pseudo-random vectors
-  auto apply_rinv = [&](uint32_t salt) {
-    for (int e = tid; e < D * kBlk; e += 256) {
-      const int row = e / kBlk, c = e % kBlk;
-      float s;
-      if (dead[c]) {
-        s = hash_unit((uint32_t)row, (uint32_t)c, salt);
-      } else {
-        s = 0.f;
-        for (int j = 0; j <= c; ++j) s += Y[row][j] * Ri[j][c];
-      }
-      X[row][c] = s;
-    }
-  };
-  // One Cholesky-QR pass of the block currently in Y (rows also in `yt`).
+  // One Cholesky-QR pass of the block Y whose rows owned by this wave are in
+  // yt: X = Y Ri for the wave's rows (matrix cores), dead columns replaced by
+  // fresh pseudo-random vectors, X -> LDS. Two workgroup barriers.
   auto cholqr = [&](const f32x4_t* yt, uint32_t salt) {
+    store_y_tiles(yt);  // read back below by this wave only
     partial_gram(yt, yt);
     __syncthreads();
-    reduce_gram();
-    __syncthreads();
-    cholesky_inverse();
-    __syncthreads();
-    apply_rinv(salt);
-    __syncthreads();
+    float am[kBlk];
+    {
+      const int row = lane & 15;
+#pragma unroll
+      for (int c = 0; c < kBlk; c += 4) {
+        f32x4_t v = *reinterpret_cast<const f32x4_t*>(&Mp[0][row][c]);
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+          const f32x4_t u = *reinterpret_cast<const f32x4_t*>(&Mp[w][row][c]);
+          v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
+        }
+        am[c] = v[0]; am[c + 1] = v[1]; am[c + 2] = v[2]; am[c + 3] = v[3];
+      }
+    }
+    const uint32_t dead = chol_rinv(am);
+    wave_lds_sync();  // RiW[wave] and this wave's Y rows are visible to the wave
+    const bool dcol = (dead >> (lane & 15)) & 1u;
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      const int tc = wave * RTW + t;
+      f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < kBlk; k0 += 4)
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(Y[16 * tc + (lane & 15)][k0 + (lane >> 4)],
+                                                 RiW[wave][k0 + (lane >> 4)][lane & 15], x, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * tc + 4 * (lane >> 4) + i;
+        X[row][lane & 15] = dcol ? hash_unit((uint32_t)row, (uint32_t)(lane & 15), salt) : x[i];
+      }
+    }
+    __syncthreads();  // X complete
   };
 
   // ---- 3. subspace iteration ----
   f32x4_t yt[RTW];
-  for (int e = tid; e < D * kBlk; e += 256) Y[e / kBlk][e % kBlk] = hash_unit((uint32_t)(e / kBlk), (uint32_t)(e % kBlk), 1u);
-  __syncthreads();
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
     const int tc = wave * RTW + t;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) yt[t][i] = Y[16 * tc + 4 * (lane >> 4) + i][lane & 15];
+    for (int i = 0; i < 4; ++i)
+      yt[t][i] = hash_unit((uint32_t)(16 * tc + 4 * (lane >> 4) + i), (uint32_t)(lane & 15), 1u);
   }
   cholqr(yt, 2u);
   for (int it = 0; it < kBuildIters; ++it) {
     matmul_hx(yt);
-    store_y_tiles(yt);
     cholqr(yt, 3u + (uint32_t)it);
   }
   // second pass for orthonormality
   load_x_tiles(yt);
-  __syncthreads();
-  store_y_tiles(yt);
   cholqr(yt, 101u);
 
-  // ---- 4. Rayleigh-Ritz: T = X^T H X ----
+  // ---- 4. Rayleigh-Ritz: T = X^T H X, diagonalised by cyclic Jacobi ----
+  int cur = 0;
   {
     f32x4_t xt[RTW];
     load_x_tiles(xt);
     matmul_hx(yt);
     partial_gram(xt, yt);
     __syncthreads();
-    reduce_gram();  // Ms = T (symmetrised)
+    reduce_gram();  // Ms[0] = T (symmetrised)
     if (wave == 0) {
-      for (int e = lane; e < kBlk * kBlk; e += 64) Wm[e / kBlk][e % kBlk] = (e / kBlk == e % kBlk) ? 1.f : 0.f;
-    }
-    __syncthreads();
-    if (wave == 0) {
+      for (int e = lane; e < kBlk * kBlk; e += 64) Wm[0][e / kBlk][e % kBlk] = (e / kBlk == e % kBlk) ? 1.f : 0.f;
+      wave_lds_sync();
+      // Each round rotates 8 disjoint index pairs (round-robin schedule) at
+      // once: T <- R T R^T, W <- W R^T in one pass per element into the other
+      // buffer. A pair is rotated only while its off-diagonal entry is
+      // significant both against its own diagonal entries and against 1e-7
+      // of the trace (fp32 rounding leaves about one ulp of the largest
+      // eigenvalue behind); the sweeps stop after one in which no pair was.
+      float tr = lane < kBlk ? Ms[0][lane][lane] : 0.f;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o, 64);
+      const float floor_abs = 1e-7f * fabsf(tr);
+      const int ey = lane & 15;  // this lane's column in the update pass
       for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
+        bool any = false;
         for (int rnd = 0; rnd < kBlk - 1; ++rnd) {
           if (lane < 8) {
             int p, q;
             if (lane == 0) { p = kBlk - 1; q = rnd; }
             else { p = (rnd + lane) % (kBlk - 1); q = (rnd - lane + (kBlk - 1)) % (kBlk - 1); }
-            const float apq = Ms[p][q];
-            const float app = Ms[p][p], aqq = Ms[q][q];
-            float c = 1.f, s = 0.f;
-            if (apq != 0.f && fabsf(apq) > 1e-10f * sqrtf(fabsf(app * aqq))) {
-              const float theta = (aqq - app) / (2.f * apq);
-              const float tt = (theta >= 0.f ? 1.f : -1.f) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
-              c = 1.f / sqrtf(tt * tt + 1.f);
-              s = tt * c;
+            const float apq = Ms[cur][p][q];
+            const float app = Ms[cur][p][p], aqq = Ms[cur][q][q];
+            float c = 1.f, sn = 0.f;
+            if (fabsf(apq) > floor_abs && fabsf(apq) > 1e-6f * sqrtf(fabsf(app * aqq))) {
+              any = true;
+              const float theta = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
+              const float tt = (theta >= 0.f ? 1.f : -1.f) *
+                               __builtin_amdgcn_rcpf(fabsf(theta) + sqrtf(theta * theta + 1.f));
+              c = __builtin_amdgcn_rsqf(tt * tt + 1.f);
+              sn = tt * c;
             }
-            rot[lane][0] = c; rot[lane][1] = s;
-            rpq[lane][0] = p; rpq[lane][1] = q;
+            jsc[p] = c; joc[p] = -sn; jpt[p] = q;
+            jsc[q] = c; joc[q] = sn;  jpt[q] = p;
           }
           wave_lds_sync();
-          // rows p, q of Ms
-          for (int e = lane; e < 8 * kBlk; e += 64) {
-            const int pi = e / kBlk, x = e % kBlk;
-            const int p = rpq[pi][0], q = rpq[pi][1];
-            const float c = rot[pi][0], s = rot[pi][1];
-            const float vp = Ms[p][x], vq = Ms[q][x];
-            Ms[p][x] = c * vp - s * vq;
-            Ms[q][x] = s * vp + c * vq;
+          {
+            const int py = jpt[ey];
+            const float sy = jsc[ey], oy = joc[ey];
+#pragma unroll
+            for (int k = 0; k < kBlk * kBlk / 64; ++k) {
+              const int x = (lane >> 4) + 4 * k;
+              const int px = jpt[x];
+              const float sx = jsc[x], ox = joc[x];
+              Ms[cur ^ 1][x][ey] = sx * (sy * Ms[cur][x][ey] + oy * Ms[cur][x][py]) +
+                                   ox * (sy * Ms[cur][px][ey] + oy * Ms[cur][px][py]);
+              Wm[cur ^ 1][x][ey] = sy * Wm[cur][x][ey] + oy * Wm[cur][x][py];
+            }
           }
           wave_lds_sync();
-          // columns p, q of Ms and of Wm
-          for (int e = lane; e < 8 * kBlk; e += 64) {
-            const int pi = e / kBlk, x = e % kBlk;
-            const int p = rpq[pi][0], q = rpq[pi][1];
-            const float c = rot[pi][0], s = rot[pi][1];
-            const float vp = Ms[x][p], vq = Ms[x][q];
-            Ms[x][p] = c * vp - s * vq;
-            Ms[x][q] = s * vp + c * vq;
-            const float wp = Wm[x][p], wq = Wm[x][q];
-            Wm[x][p] = c * wp - s * wq;
-            Wm[x][q] = s * wp + c * wq;
-          }
-          wave_lds_sync();
+          cur ^= 1;
         }
+        if (!__builtin_amdgcn_ballot_w64(any)) break;
       }
       // descending order of the Ritz values, ties by index
       if (lane < kBlk) {
-        const float v = Ms[lane][lane];
+        const float v = Ms[cur][lane][lane];
         int rank = 0;
         for (int j = 0; j < kBlk; ++j) {
-          const float u = Ms[j][j];
+          const float u = Ms[cur][j][j];
           rank += (u > v || (u == v && j < lane)) ? 1 : 0;
         }
         order[rank] = lane;
       }
     }
+    if (tid == 0) cur_s = cur;
     __syncthreads();
   }
+  const int cw = cur_s;
   // V = X W[:, order[0..r-1]] into Y[:, 0..r-1]
   for (int e = tid; e < D * kBlk; e += 256) {
     const int row = e / kBlk, rho = e % kBlk;
@@ -378,7 +409,7 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
       const int col = order[rho];
       float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < kBlk; ++j) s += X[row][j] * Wm[j][col];
+      for (int j = 0; j < kBlk; ++j) s += X[row][j] * Wm[cw][j][col];
       Y[row][rho] = s;
     }
   }
