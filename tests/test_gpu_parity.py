@@ -467,6 +467,61 @@ def test_headline_sampled():
 
 
 # --------------------------------------------------------------------------
+# long-context stress (one 512K-token sequence, J = 8192, r in {2, 4, 8}):
+# the whole step on GPU-built summaries, sampled units against the oracle
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("rank", [2, 4, 8])
+def test_stress_512k_sampled(rank):
+    wl = W["llama8b_512k"].with_(rank=rank)
+    cfg = _cfg(wl)
+    d = synth.generate(wl, 0, gg.DEV)
+    ids = d["block_table"].reshape(-1).contiguous()
+    pool = L.summary_pool_for(cfg, wl.num_blocks, gg.DEV)
+    L.locks_build_summaries(cfg, d["k_pool"], wl.num_blocks, ids, ids.numel(), pool)
+    hs = gg.gpu_scores(wl, cfg, d, pool)
+    sel, out, lse = gg.gpu_decode_step(wl, cfg, d, pool)
+    torch.cuda.synchronize()
+    T, J, Jc = gg.lens(wl, 0)
+    bt_c = d["block_table"].cpu()
+    q_c = d["q"].cpu()
+    out_c, sel_c = gg.f64(out.cpu()), sel.cpu()
+    G = wl.group
+    idx = bt_c[0, :Jc].long().to(gg.DEV)
+    for h in (1, 6):
+        rec = pool[idx, h].cpu()
+        mu, vt, cf = (gg.f64(x) for x in L.split_records(cfg, rec))
+        s_o = oracle.page_scores(gg.f64(q_c[0, h * G:(h + 1) * G]), mu, vt, cf, wl.softmax_scale)
+        assert gg.mixed_violation(gg.f64(hs[0, h * G:(h + 1) * G, :Jc].cpu()), s_o) <= 1.0
+        sel_o, sigma_o = gg.oracle_unit_select(wl, 0, s_o)
+        gg.check_selection(wl, 0, sel_c[0, h].tolist(), sel_o.tolist(), sigma_o)
+        # attention over the GPU's own selection
+        ks, vs = [], []
+        for j in sel_c[0, h].tolist():
+            if j < 0:
+                continue
+            nv = min(wl.page_size, T - j * wl.page_size)
+            blk = int(bt_c[0, j])
+            ks.append(gg.f64(d["k_pool"][blk, h, :nv].cpu()))
+            vs.append(gg.f64(d["v_pool"][blk, h, :nv].cpu()))
+        o_ref, _ = oracle.attend(gg.f64(q_c[0, h * G:(h + 1) * G]), np.concatenate(ks), np.concatenate(vs),
+                                 wl.softmax_scale)
+        assert np.max(np.abs(out_c[0, h * G:(h + 1) * G] - o_ref)) <= gg.out_tol(wl)
+    # build: a sample of pages against the oracle's fit (Eckart-Young residual)
+    rng = np.random.default_rng(rank)
+    sample = [(int(bt_c[0, j]), int(h)) for j, h in zip(rng.integers(0, Jc, 6), rng.integers(0, 8, 6))]
+    keys = np.stack([gg.f64(d["k_pool"][blk, h].cpu()) for blk, h in sample])
+    _, _, _, ev, _ = oracle.build_pages(keys, rank)
+    recs = pool[torch.tensor([x for x, _ in sample], device=gg.DEV), torch.tensor([y for _, y in sample], device=gg.DEV)]
+    _, vt_g, _ = L.split_records(cfg, recs.cpu())
+    for i, (blk, h) in enumerate(sample):
+        D = keys[i] - keys[i].mean(0)
+        vt = gg.f64(vt_g[i])
+        tau = float(np.sum(np.clip(ev[i, rank:], 0, None)))
+        resid = float(np.linalg.norm(D - D @ vt.T @ vt) ** 2)
+        assert resid <= tau + 2e-2 * float(np.sum(np.clip(ev[i], 0, None)))
+
+
+# --------------------------------------------------------------------------
 # whole decode step (score/select then decode on one workspace) vs the oracle
 # and the stages
 # --------------------------------------------------------------------------
