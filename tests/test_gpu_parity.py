@@ -634,6 +634,49 @@ def test_decode_step_shares_workspace_with_stages():
         assert int(ws[:ctl].count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("wl", [RAGGED, W["llama8b_128k_b8"]], ids=["ragged_bf16", "llama8b_128k_b8"])
+def test_decode_step_graph_replay(wl):
+    """The step only enqueues kernels (no allocation, memset or sync), so it
+    can be captured into a HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager step bit for bit."""
+    cfg = _cfg(wl)
+    d = synth.generate(wl, 5, gg.DEV)
+    pool = gg.synthetic_pool(wl, cfg, seed=5)
+    ref = gg.gpu_decode_step(wl, cfg, d, pool)
+    torch.cuda.synchronize()
+    nbytes = L.locks_workspace_size(cfg, wl.batch, wl.max_pages)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=gg.DEV)
+    sel = torch.empty_like(ref[0])
+    out = torch.empty_like(ref[1])
+    lse = torch.empty_like(ref[2])
+
+    def step():
+        L.locks_decode_step(cfg, d["q"], pool, d["k_pool"], d["v_pool"], wl.num_blocks, d["block_table"],
+                            d["seq_lens"], wl.batch, wl.max_pages, sel, out, lse, ws, nbytes)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(4):
+        sel.fill_(-7)
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sel, ref[0])
+        assert torch.equal(out.view(torch.uint8), ref[1].view(torch.uint8))
+        assert torch.equal(lse, ref[2])
+    # the control words are back to zero after the replays
+    assert int(ws[:4 * wl.batch * wl.num_kv_heads].count_nonzero()) == 0
+
+
 def test_decode_step_large_budget():
     """A large budget (260 pages of 16, over 33 decode splits) gives exactly
     the staged results."""
