@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void page_score_kernel(ScoreArgs a) {
   }
 }
 
-// LDS-staged variant (bf16 records, rank 2/4/8, G * P >= 64): see score_lds.h.
+// LDS-staged variant (bf16 records, rank 1/2/4/8, G * P >= 64): see score_lds.h.
 template <int D, int RT, int GQ, int P>
 __global__ __launch_bounds__(256, 2) void page_score_lds_kernel(ScoreArgs a) {
   __shared__ ScoreLds<D, RT, GQ, P> lds;
@@ -265,25 +265,30 @@ hipError_t launch_tpl(const ScoreArgs& a, int batch, hipStream_t s) {
   if constexpr (sizeof(T) == 2 && RT > 0) {
     if (a.G == 4 || a.G == 8) return launch_lds_pg<D, RT>(a, batch, s);
   }
-  const int lph = 64 / a.G;
-  const int tpl = a.P > lph ? a.P / lph : 1;
-  switch (a.G * 16 + tpl) {
-    case 1 * 16 + 1: return launch_one<T, D, RT, 1, 1>(a, batch, s);
-    case 2 * 16 + 1: return launch_one<T, D, RT, 2, 1>(a, batch, s);
-    case 2 * 16 + 2: return launch_one<T, D, RT, 2, 2>(a, batch, s);
-    case 4 * 16 + 1: return launch_one<T, D, RT, 4, 1>(a, batch, s);
-    case 4 * 16 + 2: return launch_one<T, D, RT, 4, 2>(a, batch, s);
-    case 4 * 16 + 4: return launch_one<T, D, RT, 4, 4>(a, batch, s);
-    case 8 * 16 + 2: return launch_one<T, D, RT, 8, 2>(a, batch, s);
-    case 8 * 16 + 4: return launch_one<T, D, RT, 8, 4>(a, batch, s);
-    case 8 * 16 + 8: return launch_one<T, D, RT, 8, 8>(a, batch, s);
-    default: return hipErrorInvalidValue;
+  if constexpr (RT == 1) {
+    return launch_tpl<T, D, 0>(a, batch, s);  // the register kernel's packed layout needs RT >= 2
+  } else {
+    const int lph = 64 / a.G;
+    const int tpl = a.P > lph ? a.P / lph : 1;
+    switch (a.G * 16 + tpl) {
+      case 1 * 16 + 1: return launch_one<T, D, RT, 1, 1>(a, batch, s);
+      case 2 * 16 + 1: return launch_one<T, D, RT, 2, 1>(a, batch, s);
+      case 2 * 16 + 2: return launch_one<T, D, RT, 2, 2>(a, batch, s);
+      case 4 * 16 + 1: return launch_one<T, D, RT, 4, 1>(a, batch, s);
+      case 4 * 16 + 2: return launch_one<T, D, RT, 4, 2>(a, batch, s);
+      case 4 * 16 + 4: return launch_one<T, D, RT, 4, 4>(a, batch, s);
+      case 8 * 16 + 2: return launch_one<T, D, RT, 8, 2>(a, batch, s);
+      case 8 * 16 + 4: return launch_one<T, D, RT, 8, 4>(a, batch, s);
+      case 8 * 16 + 8: return launch_one<T, D, RT, 8, 8>(a, batch, s);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
 template <typename T, int D>
 hipError_t launch_rank(const ScoreArgs& a, int batch, hipStream_t s) {
   switch (a.r) {
+    case 1: return launch_tpl<T, D, 1>(a, batch, s);
     case 2: return launch_tpl<T, D, 2>(a, batch, s);
     case 4: return launch_tpl<T, D, 4>(a, batch, s);
     case 8: return launch_tpl<T, D, 8>(a, batch, s);

@@ -61,7 +61,7 @@ struct ScoreMfma<float, D> {
 };
 
 // ---------------------------------------------------------------------------
-// LDS-staged variant for bf16 summaries with rank 2, 4 or 8 and G * P >= 64.
+// LDS-staged variant for bf16 summaries with rank 1, 2, 4 or 8 and G * P >= 64.
 //
 // Each wave keeps a ring of NS record slots in LDS and fills them with
 // direct global->LDS loads (global_load_lds_dwordx4, non-temporal), so NS-1
@@ -274,15 +274,17 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
 #pragma unroll
       for (int tt = 0; tt < TPL; ++tt) {
         const int tok = u + lph * tt;
-        uint32_t cw[RT / 2];
+        uint32_t cw[RT > 1 ? RT / 2 : 1];
         if constexpr (RT == 8) {
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cb + tok * 16);
           cw[0] = v[0]; cw[1] = v[1]; cw[2] = v[2]; cw[3] = v[3];
         } else if constexpr (RT == 4) {
           const u32x2_t v = *reinterpret_cast<const u32x2_t*>(cb + tok * 8);
           cw[0] = v[0]; cw[1] = v[1];
-        } else {
+        } else if constexpr (RT == 2) {
           cw[0] = *reinterpret_cast<const uint32_t*>(cb + tok * 4);
+        } else {
+          cw[0] = *reinterpret_cast<const uint16_t*>(cb + tok * 2);  // one coefficient, low half
         }
         float sacc = 0.f;
 #pragma unroll

@@ -76,7 +76,7 @@ def _uniform(batch, t):
     return tuple([int(t)] * batch)
 
 
-# The five workload shapes the path is measured and checked on.
+# The workload shapes the path is measured and checked on.
 WORKLOADS = {
     # tiny fp32 case: 64 full pages of 16 + an 8-token partial page
     "tiny_f32": Workload("tiny_f32", 1, 1, 4, 64, 16, _uniform(1, 1032), 4, 8, "f32", "f32",
@@ -87,6 +87,10 @@ WORKLOADS = {
     # headline: 128K, batch 8, AR(1) centroids
     "llama8b_128k_b8": Workload("llama8b_128k_b8", 8, 8, 4, 128, 64, _uniform(8, 131072), 8, 32,
                                 "bf16", "bf16", centroid_std=0.5, ar_rho=0.99, n_needles=16),
+    # the headline shape with the pages' default 16-token pages (the same
+    # 2048-token budget is k = 128 pages; rank swept by the caller)
+    "llama8b_128k_b8_p16": Workload("llama8b_128k_b8_p16", 8, 8, 4, 128, 16, _uniform(8, 131072), 8, 128,
+                                    "bf16", "bf16", centroid_std=0.5, ar_rho=0.99, n_needles=16),
     # long-context stress: 512K, batch 1 (rank swept by the caller)
     "llama8b_512k": Workload("llama8b_512k", 1, 8, 4, 128, 64, _uniform(1, 524288), 4, 32,
                              "bf16", "bf16", centroid_std=0.5, n_needles=8),

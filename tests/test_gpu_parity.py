@@ -522,6 +522,61 @@ def test_stress_512k_sampled(rank):
 
 
 # --------------------------------------------------------------------------
+# the headline shape with 16-token pages (k = 128 pages), r in {1, 2, 4, 8}:
+# the whole step on GPU-built summaries, sampled units against the oracle
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("rank", [1, 2, 4, 8])
+def test_p16_rank_sweep_sampled(rank):
+    wl = W["llama8b_128k_b8_p16"].with_(rank=rank)
+    cfg = _cfg(wl)
+    d = synth.generate(wl, 0, gg.DEV)
+    ids = d["block_table"].reshape(-1).contiguous()
+    pool = L.summary_pool_for(cfg, wl.num_blocks, gg.DEV)
+    L.locks_build_summaries(cfg, d["k_pool"], wl.num_blocks, ids, ids.numel(), pool)
+    hs = gg.gpu_scores(wl, cfg, d, pool)
+    sel, out, lse = gg.gpu_decode_step(wl, cfg, d, pool)
+    torch.cuda.synchronize()
+    bt_c = d["block_table"].cpu()
+    q_c = d["q"].cpu()
+    out_c, sel_c = gg.f64(out.cpu()), sel.cpu()
+    G, P = wl.group, wl.page_size
+    for (b, h) in ((0, 2), (5, 7)):
+        T, J, Jc = gg.lens(wl, b)
+        idx = bt_c[b, :Jc].long().to(gg.DEV)
+        rec = pool[idx, h].cpu()
+        mu, vt, cf = (gg.f64(x) for x in L.split_records(cfg, rec))
+        qg = gg.f64(q_c[b, h * G:(h + 1) * G])
+        s_o = oracle.page_scores(qg, mu, vt, cf, wl.softmax_scale)
+        assert gg.mixed_violation(gg.f64(hs[b, h * G:(h + 1) * G, :Jc].cpu()), s_o) <= 1.0
+        sel_o, sigma_o = gg.oracle_unit_select(wl, b, s_o)
+        gg.check_selection(wl, b, sel_c[b, h].tolist(), sel_o.tolist(), sigma_o)
+        ks, vs = [], []
+        for j in sel_c[b, h].tolist():
+            if j < 0:
+                continue
+            nv = min(P, T - j * P)
+            blk = int(bt_c[b, j])
+            ks.append(gg.f64(d["k_pool"][blk, h, :nv].cpu()))
+            vs.append(gg.f64(d["v_pool"][blk, h, :nv].cpu()))
+        o_ref, _ = oracle.attend(qg, np.concatenate(ks), np.concatenate(vs), wl.softmax_scale)
+        assert np.max(np.abs(out_c[b, h * G:(h + 1) * G] - o_ref)) <= gg.out_tol(wl)
+    # build: sampled pages, Eckart-Young residual against the oracle's spectrum
+    rng = np.random.default_rng(10 + rank)
+    sample = [(int(bt_c[b, j]), int(h)) for b, j, h in zip(rng.integers(0, 8, 6), rng.integers(0, 8192, 6),
+                                                            rng.integers(0, 8, 6))]
+    keys = np.stack([gg.f64(d["k_pool"][blk, h].cpu()) for blk, h in sample])
+    _, _, _, ev, _ = oracle.build_pages(keys, rank)
+    recs = pool[torch.tensor([x for x, _ in sample], device=gg.DEV), torch.tensor([y for _, y in sample], device=gg.DEV)]
+    _, vt_g, _ = L.split_records(cfg, recs.cpu())
+    for i in range(len(sample)):
+        D = keys[i] - keys[i].mean(0)
+        vt = gg.f64(vt_g[i])
+        tau = float(np.sum(np.clip(ev[i, rank:], 0, None)))
+        resid = float(np.linalg.norm(D - D @ vt.T @ vt) ** 2)
+        assert resid <= tau + 2e-2 * float(np.sum(np.clip(ev[i], 0, None)))
+
+
+# --------------------------------------------------------------------------
 # whole decode step (score/select then decode on one workspace) vs the oracle
 # and the stages
 # --------------------------------------------------------------------------
