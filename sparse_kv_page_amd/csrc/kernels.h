@@ -15,7 +15,7 @@ struct ScoreArgs {
   int64_t num_blocks;
   int64_t rec_elems;          // elements per record
   int Hkv, G, P, r, max_pages;
-  int ppw;                    // pages per wave (<= 64)
+  int ppw;                    // pages per wave, set by the launcher (<= 128 LDS-staged, else <= 64)
   float scale;
 };
 

@@ -211,11 +211,12 @@ int cached_waves(const void* fn) {
   return waves;
 }
 
-// pages per wave and grid for one round of `waves` resident waves
-dim3 score_grid(ScoreArgs& a, int batch, int waves) {
+// pages per wave (at most max_ppw) and grid for one round of `waves`
+// resident waves
+dim3 score_grid(ScoreArgs& a, int batch, int waves, int max_ppw) {
   const int64_t total = (int64_t)batch * a.Hkv * a.max_pages;
   int64_t ppw = (total + waves - 1) / waves;
-  ppw = ppw < 1 ? 1 : (ppw > 64 ? 64 : ppw);
+  ppw = ppw < 1 ? 1 : (ppw > max_ppw ? max_ppw : ppw);
   a.ppw = (int)ppw;
   const int waves_per_unit = (int)((a.max_pages + ppw - 1) / ppw);
   return dim3((waves_per_unit + kScoreWaves - 1) / kScoreWaves, a.Hkv, batch);
@@ -227,7 +228,7 @@ struct LdsTag {};
 template <int D, int RT, int GQ, int P>
 hipError_t launch_lds(ScoreArgs a, int batch, hipStream_t stream) {
   const void* fn = reinterpret_cast<const void*>(&page_score_lds_kernel<D, RT, GQ, P>);
-  const dim3 grid = score_grid(a, batch, cached_waves<LdsTag<D, RT, GQ, P>>(fn));
+  const dim3 grid = score_grid(a, batch, cached_waves<LdsTag<D, RT, GQ, P>>(fn), kScoreMaxPpw);
   hipLaunchKernelGGL((page_score_lds_kernel<D, RT, GQ, P>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -241,7 +242,7 @@ hipError_t launch_one(ScoreArgs a, int batch, hipStream_t stream) {
       reinterpret_cast<const void*>(&page_score_kernel<T, D, RT, GQ, TPL>));
   // one round of resident waves; a wave keeps its block ids in one VGPR, so
   // at most 64 pages per wave
-  const dim3 grid = score_grid(a, batch, waves);
+  const dim3 grid = score_grid(a, batch, waves, 64);
   hipLaunchKernelGGL((page_score_kernel<T, D, RT, GQ, TPL>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -11,6 +11,7 @@
 namespace locks {
 
 constexpr int kScoreWaves = 4;
+constexpr int kScoreMaxPpw = 128;  // pages per wave of the LDS-staged scorer (block ids in two VGPRs)
 
 template <typename T, int D>
 struct ScoreMfma;
@@ -133,7 +134,7 @@ struct LdsRec {
   static constexpr int kRowChunks = kE * D / 16;            // 16-byte chunks per row
   static constexpr int kHeadChunks = kHeadBytes / 16;
   static constexpr int kBudget = 80 * 1024;                 // LDS bytes per workgroup
-  static constexpr int kExtra = 4 * (2 * G * 16 + 64 * G) * 4; // w and score staging of 4 waves
+  static constexpr int kExtra = 4 * (2 * G * 16 + kScoreMaxPpw * G) * 4;  // w and score staging of 4 waves
   static constexpr int kNs0 = (kBudget - kExtra) / (4 * kBytes);
   static constexpr int kNs = kNs0 < 2 ? 2 : (kNs0 > 8 ? 8 : kNs0);
   static_assert(kBytes % 16 == 0, "records are whole 16-byte chunks");
@@ -150,11 +151,11 @@ struct alignas(16) ScoreLds {
   using R = LdsRec<D, RT, P, GQ>;
   uint8_t slots[kScoreWaves][R::kNs][R::kBytes];
   float wbuf[kScoreWaves][2][GQ][16];
-  float sbuf[kScoreWaves][64][GQ];
+  float sbuf[kScoreWaves][kScoreMaxPpw][GQ];
 };
 
 // One wave scores pages [p0, p0 + min(ppw, Jc - p0)) of the unit (b, h) for
-// all G heads (ppw <= 64, p0 wave-uniform).
+// all G heads (ppw <= kScoreMaxPpw, p0 wave-uniform).
 template <int D, int RT, int GQ, int P>
 __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h, int p0, int ppw,
                                                ScoreLds<D, RT, GQ, P>& L) {
@@ -177,7 +178,9 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
   // block ids are loaded before the length is known (entries up to max_pages
   // are addressable), so the two loads are in flight together
   const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+  // lane l holds the block ids of pages l and 64 + l of the range
   int my_bid = lane < ppw && p0 + lane < a.max_pages ? bt_row[p0 + lane] : -1;
+  int my_bid2 = lane + 64 < ppw && p0 + 64 + lane < a.max_pages ? bt_row[p0 + 64 + lane] : -1;
   const int T_b = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.max_pages, P));
   const int Jc = T_b / P;
   if (p0 >= Jc) return;
@@ -192,6 +195,12 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
   // below assume only record loads are pending)
   wait_vm_const<0>();
   my_bid = __builtin_amdgcn_mov_dpp(my_bid, 0xE4, 0xf, 0xf, false);  // identity; orders the use after the wait
+  my_bid2 = __builtin_amdgcn_mov_dpp(my_bid2, 0xE4, 0xf, 0xf, false);
+  auto bid_at = [&](int t) {  // t wave-uniform
+    const int b0 = __builtin_amdgcn_readlane(my_bid, t & 63);
+    const int b1 = __builtin_amdgcn_readlane(my_bid2, t & 63);
+    return t < 64 ? b0 : b1;
+  };
   const int g = lane / lph;
   const int u = lane - g * lph;
   const float zscale = a.scale * kLog2e;
@@ -217,7 +226,7 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
   }
 
   auto issue = [&](int t, int slot) {
-    const int bid = __builtin_amdgcn_readlane(my_bid, t);
+    const int bid = bid_at(t);
     const uint8_t* rec = pool + (int64_t)(bid_ok(bid) ? bid : 0) * blk_stride;
     const uint32_t dst = lds_addr(&slots[wave][slot][0]);
 #pragma unroll
@@ -313,7 +322,7 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
     if (u == 0) {
 #pragma unroll
       for (int p = 0; p < NPG; ++p) {
-        const int bid = __builtin_amdgcn_readlane(my_bid, t + p);
+        const int bid = bid_at(t + p);
         const float sc = qmu[p] * a.scale + (mx[p] + log2_fast(sm[p])) * kLn2;
         sbuf[wave][t + p][g] = bid_ok(bid) ? sc : -INFINITY;
       }
@@ -341,6 +350,10 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
   if (lane < np) {
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) out[(int64_t)gg * a.max_pages + lane] = sbuf[wave][lane][gg];
+  }
+  if (lane + 64 < np) {
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) out[(int64_t)gg * a.max_pages + lane + 64] = sbuf[wave][lane + 64][gg];
   }
 }
 
