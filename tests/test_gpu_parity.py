@@ -209,10 +209,13 @@ def test_build_parity(wl, npages):
     assert checked >= max(1, len(pages) // 4)
 
 
-def test_full_rank_reconstruction_equals_exact_lse():
-    """r = P - 1 >= rank(D): the GPU-built summaries reproduce the exact page LSE
-    ([Locks] Thm. 1(i), eta = 0) and the selection equals the exact-LSE set."""
-    wl = TINY.with_(rank=15, noise=0.2)
+@pytest.mark.parametrize("rank,noise", [(15, 0.2), (5, 0.0)], ids=["r15_noisy", "r5_noise_free"])
+def test_full_rank_reconstruction_equals_exact_lse(rank, noise):
+    """r >= rank(D): the GPU-built summaries reproduce the exact page LSE
+    ([Locks] Thm. 1(i), eta = 0) and the selection equals the exact-LSE set.
+    r = P - 1 covers any page; r = 5 covers the noise-free keys of the tiny
+    workload, whose centred pages have rank 4."""
+    wl = TINY.with_(rank=rank, noise=noise)
     cfg = _cfg(wl)
     data, g = gg.make_inputs(wl, seed=6)
     pool = gg.gpu_build(wl, cfg, g)
