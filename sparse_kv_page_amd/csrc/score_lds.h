@@ -12,6 +12,7 @@ namespace locks {
 
 constexpr int kScoreWaves = 4;
 constexpr int kScoreMaxPpw = 128;  // pages per wave of the LDS-staged scorer (block ids in two VGPRs)
+constexpr int kScorePagesPerIter = 4;  // at most this many pages scored together (interleaved chains)
 
 template <typename T, int D>
 struct ScoreMfma;
@@ -134,7 +135,7 @@ struct LdsRec {
   static constexpr int kRowChunks = kE * D / 16;            // 16-byte chunks per row
   static constexpr int kHeadChunks = kHeadBytes / 16;
   static constexpr int kBudget = 80 * 1024;                 // LDS bytes per workgroup
-  static constexpr int kExtra = 4 * (2 * G * 16 + kScoreMaxPpw * G) * 4;  // w and score staging of 4 waves
+  static constexpr int kExtra = 4 * (kScorePagesPerIter * G * 16 + kScoreMaxPpw * G) * 4;  // w and score staging of 4 waves
   static constexpr int kNs0 = (kBudget - kExtra) / (4 * kBytes);
   static constexpr int kNs = kNs0 < 2 ? 2 : (kNs0 > 8 ? 8 : kNs0);
   static_assert(kBytes % 16 == 0, "records are whole 16-byte chunks");
@@ -150,7 +151,7 @@ template <int D, int RT, int GQ, int P>
 struct alignas(16) ScoreLds {
   using R = LdsRec<D, RT, P, GQ>;
   uint8_t slots[kScoreWaves][R::kNs][R::kBytes];
-  float wbuf[kScoreWaves][2][GQ][16];
+  float wbuf[kScoreWaves][kScorePagesPerIter][GQ][16];
   float sbuf[kScoreWaves][kScoreMaxPpw][GQ];
 };
 
@@ -238,14 +239,16 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
   const int npre = np < NS ? np : NS;
   for (int t = 0; t < npre; ++t) issue(t, t);
 
-  // Two pages per iteration: their dependent chains (LDS reads -> MFMA ->
+  // Several pages per iteration: their dependent chains (LDS reads -> MFMA ->
   // transpose through LDS -> logits -> DPP reductions) interleave, which hides
-  // the chain latency the two resident waves per SIMD cannot.
+  // the chain latency the two resident waves per SIMD cannot (4 pages measured
+  // faster than 2 or 3 at the headline shape).
   auto score_pages = [&](auto npg_tag, int t, int s0) {
     constexpr int NPG = decltype(npg_tag)::value;
     const uint8_t* rec[NPG];
     rec[0] = &slots[wave][s0][0];
-    if constexpr (NPG == 2) rec[1] = &slots[wave][s0 + 1 == NS ? 0 : s0 + 1][0];
+#pragma unroll
+    for (int p = 1; p < NPG; ++p) rec[p] = &slots[wave][(s0 + p) % NS][0];
 
     // ---- A: w_g and q_g . mu ----
     typename M::Op av[NPG][M::kSteps];
@@ -331,18 +334,22 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
 
   int slot = 0;
   int t = 0;
-  for (; t + 1 < np; t += 2) {
-    wait_vm_pages<R::kInstr, NS - 1>(min(np, t + NS) - (t + 2));  // records issued after page t+1
-    score_pages(std::integral_constant<int, 2>{}, t, slot);
-    // every read of these two slots has been consumed; refill them
-    const int s1 = slot + 1 == NS ? 0 : slot + 1;
-    if (t + NS < np) issue(t + NS, slot);
-    if (t + 1 + NS < np) issue(t + 1 + NS, s1);
-    slot = s1 + 1 == NS ? 0 : s1 + 1;
+  // one slot beyond an iteration's pages stays in flight across iterations
+  constexpr int KI = NS - 1 < kScorePagesPerIter ? (NS - 1 < 1 ? 1 : NS - 1) : kScorePagesPerIter;
+  for (; t + KI - 1 < np; t += KI) {
+    wait_vm_pages<R::kInstr, NS - 1>(min(np, t + NS) - (t + KI));  // records issued after page t+KI-1
+    score_pages(std::integral_constant<int, KI>{}, t, slot);
+    // every read of these slots has been consumed; refill them
+#pragma unroll
+    for (int p = 0; p < KI; ++p)
+      if (t + p + NS < np) issue(t + p + NS, (slot + p) % NS);
+    slot = (slot + KI) % NS;
   }
-  if (t < np) {
-    wait_vm_pages<R::kInstr, NS - 1>(0);
+  // the last pages one at a time (all issued already: t + NS >= np here)
+  for (; t < np; ++t) {
+    wait_vm_pages<R::kInstr, NS - 1>(min(np, t + NS) - (t + 1));
     score_pages(std::integral_constant<int, 1>{}, t, slot);
+    slot = slot + 1 == NS ? 0 : slot + 1;
   }
   wave_lds_sync();
   // coalesced store of the wave's scores: lane t writes page p0 + t of each head
