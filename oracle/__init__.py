@@ -9,7 +9,8 @@ listed per function below (a gather by block table, widening to float64).
 Formulas follow "Locks: Page-Local Compact Key Summaries for Efficient
 Long-Context Decoding" (arXiv 2607.24555): §2 Eq. (1) exact page LSE, §3-§4
 summary fit, §4 Eq. (2) reconstructed page LSE, §4 share-average combine and
-selection, §2 restricted attention.
+selection, §2 restricted attention, §4 / App. C.7 quantized ("i4") summary
+storage.
 """
 from __future__ import annotations
 
@@ -53,6 +54,7 @@ def lib():
         L.lo_combine.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp, _dp]
         L.lo_select.argtypes = [ctypes.c_int] * 3 + [_dp, _ip]
         L.lo_attend.argtypes = [ctypes.c_int] * 3 + [_dp] * 3 + [ctypes.c_double, _dp, _dp]
+        L.lo_quantize_summaries.argtypes = [ctypes.c_int] * 4 + [_dp] * 3 + [_ip] * 3 + [_dp] * 3
         _lib = L
     return _lib
 
@@ -99,6 +101,40 @@ def round_bf16(x) -> np.ndarray:
     out = np.empty_like(a)
     lib().lo_round_bf16(_p(a), a.size, _p(out))
     return out
+
+
+# --------------------------------------------------------------------------
+# Quantized summary storage ([Locks] §4 "i4" variants, App. C.7)
+# --------------------------------------------------------------------------
+def quantize_summaries(mu, vt, coef):
+    """Full-precision (mu [n][d], vt [n][r][d], coef [n][P][r]) -> int4/int8 codes and
+    bf16 scales: dict(mu_code [n][d], vt_code [n][r][d], coef_code [n][P][r] (int32),
+    mu_scale [n], vt_scale [n][r], coef_scale [n][P] (float64 holding bf16 values)).
+
+    One symmetric scale per basis vector (4-bit codes in [-7, 7]), per token's
+    coefficient row and for the centroid (8-bit codes in [-127, 127]); scale =
+    bf16(max|x| / L), code = round-half-even(x / scale), decided in fp32."""
+    mu = _f64(mu); vt = _f64(vt); coef = _f64(coef)
+    n, r, d = vt.shape
+    P = coef.shape[1]
+    out = dict(mu_code=np.zeros((n, d), np.int32), vt_code=np.zeros((n, r, d), np.int32),
+               coef_code=np.zeros((n, P, r), np.int32), mu_scale=np.zeros(n),
+               vt_scale=np.zeros((n, r)), coef_scale=np.zeros((n, P)))
+    ip = lambda a: a.ctypes.data_as(_ip)
+    _check(lib().lo_quantize_summaries(n, d, P, r, _p(mu), _p(vt), _p(coef), ip(out["mu_code"]),
+                                       ip(out["vt_code"]), ip(out["coef_code"]),
+                                       _p(out["mu_scale"]), _p(out["vt_scale"]),
+                                       _p(out["coef_scale"])), "quantize_summaries")
+    return out
+
+
+def dequantize_summaries(qs):
+    """Stored values of quantized summaries: code * scale of its group, in float64.
+    Returns (mu [n][d], vt [n][r][d], coef [n][P][r])."""
+    mu = qs["mu_code"] * qs["mu_scale"][:, None]
+    vt = qs["vt_code"] * qs["vt_scale"][:, :, None]
+    coef = qs["coef_code"] * qs["coef_scale"][:, :, None]
+    return mu.astype(np.float64), vt.astype(np.float64), coef.astype(np.float64)
 
 
 # --------------------------------------------------------------------------

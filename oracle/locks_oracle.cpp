@@ -333,4 +333,64 @@ int lo_attend(int G, int d, int n_tok, const double* q, const double* keys,
   return 0;
 }
 
+
+// Quantized summary storage, [Locks] §4 (the "i4" variants) and App. C.7:
+// the basis V_j in 4-bit integers, the centroid mu_j and the coefficients
+// C_j in 8-bit integers, with bfloat16 scales. The pages give the widths and
+// the byte count only (d*r/2 + B*r + d bytes before scales; 818 / 490 / 326
+// bytes with scales at B = 16, d = 128, r = 8 / 4 / 2). Reading taken here:
+//   * symmetric codes, one scale per group, the groups being each basis
+//     vector (d entries), each token's coefficient row (r entries) and the
+//     centroid (d entries): r + B + 1 scales, the count that reproduces the
+//     printed totals;
+//   * scale = bf16(max|x| / L) with L = 7 (4-bit) or 127 (8-bit), code =
+//     round-half-even(x / scale), clamped to [-L, L]; a group of zeros has
+//     scale 0 and codes 0;
+//   * the code is an integer decided by floating point, so it is decided in
+//     fp32, the precision of the GPU build: x is first rounded to fp32 and the
+//     maximum, the division by L and the division by the scale are fp32
+//     operations (each correctly rounded).
+// The three parts are quantized independently from the full-precision fit.
+static void quantize_group(const double* x, long n, long stride, int L, int* code, long cstride,
+                           double* scale) {
+  float amax = 0.0f;
+  for (long i = 0; i < n; ++i) amax = std::max(amax, std::fabs((float)x[i * stride]));
+  const float s32 = amax / (float)L;
+  double sb = 0.0;
+  const double s64 = (double)s32;
+  lo_round_bf16(&s64, 1, &sb);
+  *scale = sb;
+  const float sf = (float)sb;  // a bf16 value, exact in fp32
+  for (long i = 0; i < n; ++i) {
+    int c = 0;
+    if (sf > 0.0f) {
+      const float t = (float)x[i * stride] / sf;
+      c = (int)std::nearbyint(t);  // ties to even in the default rounding mode
+      c = std::min(L, std::max(-L, c));
+    }
+    code[i * cstride] = c;
+  }
+}
+
+// n_pages summaries (mu [n][d], vt [n][r][d], coef [n][P][r], full precision)
+// -> signed codes of the same shapes and scales mu_scale [n], vt_scale [n][r]
+// (one per basis vector), coef_scale [n][P] (one per token).
+int lo_quantize_summaries(int n_pages, int d, int P, int r, const double* mu, const double* vt,
+                          const double* coef, int* mu_code, int* vt_code, int* coef_code,
+                          double* mu_scale, double* vt_scale, double* coef_scale) {
+  if (n_pages < 0 || d < 1 || P < 1 || r < 1) return -1;
+  for (int j = 0; j < n_pages; ++j) {
+    quantize_group(mu + (size_t)j * d, d, 1, 127, mu_code + (size_t)j * d, 1, mu_scale + j);
+    for (int rho = 0; rho < r; ++rho) {
+      const size_t o = ((size_t)j * r + rho) * d;
+      quantize_group(vt + o, d, 1, 7, vt_code + o, 1, vt_scale + (size_t)j * r + rho);
+    }
+    for (int i = 0; i < P; ++i) {
+      const size_t o = ((size_t)j * P + i) * r;
+      quantize_group(coef + o, r, 1, 127, coef_code + o, 1, coef_scale + (size_t)j * P + i);
+    }
+  }
+  return 0;
+}
+
 }  // extern "C"

@@ -377,3 +377,125 @@ def test_round_bf16_matches_torch_cast():
     ref = torch.tensor(x).to(torch.bfloat16).to(torch.float64).numpy()
     got = oracle.round_bf16(x.astype(np.float64))
     np.testing.assert_array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------
+# Quantized summary storage ([Locks] §4 "i4" variants, App. C.7)
+# --------------------------------------------------------------------------
+def _quantize_one_group(x, L):
+    """Quantize a single group through the oracle by placing it where that
+    group width lives: L = 7 -> one basis vector, L = 127 -> the centroid."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.size
+    if L == 7:
+        qs = oracle.quantize_summaries(np.zeros((1, n)), x[None, None, :], np.zeros((1, 1, 1)))
+        return qs["vt_scale"][0, 0], qs["vt_code"][0, 0]
+    qs = oracle.quantize_summaries(x[None, :], np.zeros((1, 1, n)), np.zeros((1, 1, 1)))
+    return qs["mu_scale"][0], qs["mu_code"][0]
+
+
+@pytest.mark.parametrize("case", _golden("quantize_worked.json")["groups"], ids=lambda c: c["name"])
+def test_quantize_worked_examples(case):
+    scale, codes = _quantize_one_group(case["x"], case["L"])
+    assert scale == case["scale"]
+    assert codes.tolist() == case["codes"]
+
+
+def test_quantize_coefficient_rows_use_their_own_scale():
+    # the coefficient group is a token's row of r values: the hand-worked row
+    # as token 1 of a page, next to a token whose row is 64x smaller
+    row = [-2.54, 0.01, 1.0]
+    coef = np.array([[[x / 64 for x in row], row]])
+    qs = oracle.quantize_summaries(np.zeros((1, 4)), np.zeros((1, 3, 4)), coef)
+    assert qs["coef_scale"][0, 1] == 0.02001953125
+    assert qs["coef_code"][0, 1].tolist() == [-127, 0, 50]
+    assert qs["coef_scale"][0, 0] == 0.02001953125 / 64  # a power of two apart: same codes
+    assert qs["coef_code"][0, 0].tolist() == [-127, 0, 50]
+
+
+@pytest.mark.parametrize("case", _golden("byte_model.json")["summaries_with_scales"],
+                         ids=lambda c: f"r{c['r']}")
+def test_quantized_byte_model(case):
+    """Bits of the stored codes and scales equal the pages' byte counts."""
+    rng = np.random.default_rng(case["r"])
+    B, d, r = case["B"], case["d"], case["r"]
+    keys = _page(rng, B, d, 6)[None]
+    mu, vt, cf, _, _ = oracle.build_pages(keys, r)
+    qs = oracle.quantize_summaries(mu, vt, cf)
+    assert np.abs(qs["vt_code"]).max() <= 7        # fits a signed 4-bit field
+    assert np.abs(qs["mu_code"]).max() <= 127      # fits a signed 8-bit field
+    assert np.abs(qs["coef_code"]).max() <= 127
+    n_scales = qs["mu_scale"].size + qs["vt_scale"].size + qs["coef_scale"].size
+    bits = 4 * qs["vt_code"].size + 8 * (qs["mu_code"].size + qs["coef_code"].size) + 16 * n_scales
+    assert bits % 8 == 0
+    assert bits // 8 == case["bytes"]
+    kv = _golden("byte_model.json")["kv_page_bytes"]["bytes"]
+    assert round(case["bytes"] / kv, 3) == case["alpha"]
+
+
+def _fitted(seed, n=6, P=16, d=64, r=4):
+    rng = np.random.default_rng(seed)
+    keys = np.stack([_page(rng, P, d, 6) for _ in range(n)])
+    return oracle.build_pages(keys, r)[:3]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_quantize_roundtrip_bound(seed):
+    """No code is ever clamped (bf16(amax/L) is within 2^-9 of amax/L), so every
+    stored value is within half a step of the fitted one, and the group's
+    largest entry maps to +-L."""
+    mu, vt, cf = _fitted(seed)
+    qs = oracle.quantize_summaries(mu, vt, cf)
+    dmu, dvt, dcf = oracle.dequantize_summaries(qs)
+    for x, y, s, L, code in ((mu, dmu, qs["mu_scale"][:, None], 127, qs["mu_code"]),
+                             (vt, dvt, qs["vt_scale"][:, :, None], 7, qs["vt_code"]),
+                             (cf, dcf, qs["coef_scale"][:, :, None], 127, qs["coef_code"])):
+        assert np.all(np.abs(x - y) <= 0.5 * s * (1 + 1e-6) + 1e-7 * np.abs(x))
+        assert np.all(np.abs(code).max(axis=-1) == L)
+
+
+def test_quantize_grid_values_roundtrip_exactly():
+    """Values already on the grid (integer codes times a bf16 scale, largest
+    code +-L, a different scale per group) come back exactly, so the quantized
+    page score equals the unquantized one."""
+    rng = np.random.default_rng(7)
+    n, P, d, r = 3, 16, 64, 4
+
+    def grid(shape, L):
+        c = rng.integers(-L, L + 1, size=shape)
+        c[..., 0] = L * rng.choice([-1, 1], size=shape[:-1])
+        s = oracle.round_bf16(2.0 ** rng.uniform(-9, 2, size=shape[:-1]))
+        return c, s
+
+    mc, ms = grid((n, d), 127)
+    vc, vs = grid((n, r, d), 7)
+    cc, cs = grid((n, P, r), 127)
+    mu, vt, cf = mc * ms[:, None], vc * vs[:, :, None], cc * cs[:, :, None]
+    qs = oracle.quantize_summaries(mu, vt, cf)
+    assert np.array_equal(qs["mu_code"], mc) and np.array_equal(qs["mu_scale"], ms)
+    assert np.array_equal(qs["vt_code"], vc) and np.array_equal(qs["vt_scale"], vs)
+    assert np.array_equal(qs["coef_code"], cc) and np.array_equal(qs["coef_scale"], cs)
+    dmu, dvt, dcf = oracle.dequantize_summaries(qs)
+    q = rng.standard_normal((4, d))
+    np.testing.assert_array_equal(oracle.page_scores(q, dmu, dvt, dcf, d ** -0.5),
+                                  oracle.page_scores(q, mu, vt, cf, d ** -0.5))
+
+
+def test_quantized_score_within_lipschitz_bound():
+    """Log-sum-exp moves by at most the largest logit change, so the quantized
+    page score differs from the fitted one by at most
+    scale * (|q.(mu'-mu)| + max_i |q.(V'c'_i - V c_i)|), evaluated here on the
+    reconstructed keys rather than through V^T q."""
+    mu, vt, cf = _fitted(3)
+    dmu, dvt, dcf = oracle.dequantize_summaries(oracle.quantize_summaries(mu, vt, cf))
+    d = mu.shape[1]
+    sc = d ** -0.5
+    q = np.random.default_rng(4).standard_normal((4, d))
+    s0 = oracle.page_scores(q, mu, vt, cf, sc)
+    s1 = oracle.page_scores(q, dmu, dvt, dcf, sc)
+    rec0 = np.einsum("nrd,npr->npd", vt, cf)    # V c_i, per page and token
+    rec1 = np.einsum("nrd,npr->npd", dvt, dcf)
+    for g in range(q.shape[0]):
+        bound = sc * (np.abs((dmu - mu) @ q[g]) + np.abs((rec1 - rec0) @ q[g]).max(axis=1))
+        assert np.all(np.abs(s1[g] - s0[g]) <= bound * (1 + 1e-9) + 1e-12)
+        assert np.any(s1[g] != s0[g])
