@@ -19,6 +19,8 @@
  * - Return value: LOCKS_OK (0) or a negative status (see below). A non-OK
  *   status means nothing was enqueued, except LOCKS_E_HIP, which reports a
  *   launch failure from the HIP runtime.
+ * - num_blocks >= 1 for every call with work that reads a paged pool (an id
+ *   outside the pool still issues its loads at block 0, result discarded).
  * - Data-dependent checks are done on the device: a block id outside
  *   [0, num_blocks) is skipped (its page scores -inf and is never selected;
  *   in decode the slot contributes nothing), a negative sequence length counts
@@ -38,6 +40,21 @@
  *                    ascending, padded with -1
  * A sequence with T tokens has J = ceil(T/P) pages; the first floor(T/P) are
  * complete. Page J-1 is the current page (partial when P does not divide T).
+ *
+ * LOCKS_I4 summary records ([Locks] §4 "i4" storage, App. C.7 byte model),
+ * in this byte order:
+ *   V codes     r rows of d/2 bytes: basis vector rho as 4-bit fields n in
+ *               1..15, value s_V[rho] * (n - 8)
+ *   mu codes    2 rows of d/2 bytes: the high, then the low 4 bits of the
+ *               centroid's 8-bit codes b in 1..255, value s_mu * (b - 128)
+ *   C codes     P rows of r bytes: token i's codes b, value s_C[i] * (b - 128)
+ *   scales      1 + r + P bf16: s_mu, s_V[0..r-1], s_C[0..P-1]
+ *   padding     zero bytes up to a multiple of 16
+ *   In a row of 4-bit fields, element a (0 <= a < d) lives in the 32-bit
+ *   little-endian word w = ((a % 32) / 8) * (d / 32) + a / 32, at bits
+ *   4m .. 4m+3 with m = e/2 for even e = a % 8 and m = 4 + (e-1)/2 for odd e.
+ *   Size: ((r + 2) d/2 + P r + 2 (1 + r + P)) rounded up to 16 bytes, i.e. the
+ *   pages' d r/2 + P r + d bytes before scales plus 2 (r + P + 1) of scales.
  */
 #ifndef LOCKS_H
 #define LOCKS_H
@@ -59,7 +76,10 @@ enum {
   LOCKS_E_HIP = -4           /* the HIP runtime reported a launch error          */
 };
 
-typedef enum { LOCKS_BF16 = 0, LOCKS_F32 = 1 } locks_dtype_t;
+/* LOCKS_I4 is a summary_dtype only: the quantized summary storage of [Locks]
+ * §4 and App. C.7 (4-bit basis, 8-bit centroid and coefficients, bf16
+ * scales), layout below. */
+typedef enum { LOCKS_BF16 = 0, LOCKS_F32 = 1, LOCKS_I4 = 2 } locks_dtype_t;
 
 typedef struct locks_config {
   int32_t head_dim;      /* d: 64 or 128                                          */
@@ -69,7 +89,8 @@ typedef struct locks_config {
   int32_t num_kv_heads;  /* H_kv >= 1; G = H_q / H_kv must be 1, 2, 4 or 8        */
   int32_t budget_pages;  /* k = ceil(b / P) page slots per (sequence, KV head), >= 2 */
   int32_t kv_dtype;      /* locks_dtype_t of q, K, V and the attention output     */
-  int32_t summary_dtype; /* locks_dtype_t of the summary records; must equal kv_dtype */
+  int32_t summary_dtype; /* locks_dtype_t of the summary records: kv_dtype, or
+                            LOCKS_I4 with kv_dtype LOCKS_BF16 and rank 1, 2, 4 or 8 */
   float softmax_scale;   /* logit scale, normally 1/sqrt(d); finite and > 0       */
 } locks_config_t;
 
@@ -79,7 +100,8 @@ const char* locks_status_string(int status);
 /* Library ABI version (this header: 1). */
 int locks_version(void);
 
-/* Bytes of one summary record, e*(d + r*d + P*r); 0 when cfg is invalid or
+/* Bytes of one summary record: e*(d + r*d + P*r) for bf16 / fp32 records,
+ * the LOCKS_I4 size below for quantized ones; 0 when cfg is invalid or
  * unsupported. [Locks] §4: a page stores its centroid mu_j, its basis V_j and
  * its per-token coefficients C_j. */
 size_t locks_summary_record_bytes(const locks_config_t* cfg);
@@ -103,7 +125,10 @@ int locks_workspace_size(const locks_config_t* cfg, int32_t batch, int32_t max_p
  *     V  = top-r eigenvectors of H = D^T D (orthonormal, d x r),
  *     C  = D V  (P x r),
  * and store (mu, V^T, C) rounded to summary_dtype (round-to-nearest-even)
- * into the record of (block, h) in summary_pool. Keys are read as stored;
+ * into the record of (block, h) in summary_pool. For LOCKS_I4 each group (the
+ * centroid, each basis vector, each token's coefficient row) is quantized
+ * symmetrically: scale = bf16(max|x| / L) with L = 127 (8-bit) or 7 (4-bit),
+ * code = round-half-even(x / scale) in fp32, scale 0 for an all-zero group. Keys are read as stored;
  * the fit is computed in fp32 (Gram matrix on the matrix cores, subspace
  * iteration with a Rayleigh-Ritz step). Within an eigenvalue cluster any
  * orthonormal basis of the subspace is an equally valid result; each basis
@@ -118,8 +143,9 @@ int locks_build_summaries(const locks_config_t* cfg, const void* k_pool, int64_t
  * and complete page j < floor(T_b / P), with mu, V, C the summary of
  * block_table[b][j] for KV head g / G,
  *     head_scores[b][g][j] = (q.mu) * scale + log sum_i exp(((V^T q).c_i) * scale)
- * computed from the stored summary values in fp32. Entries j >= floor(T_b/P)
- * are left untouched. head_scores: [batch][H_q][max_pages] fp32. */
+ * computed from the stored summary values in fp32 (for LOCKS_I4, the values
+ * code * scale). Entries j >= floor(T_b/P) are left untouched. head_scores:
+ * [batch][H_q][max_pages] fp32. */
 int locks_page_score(const locks_config_t* cfg, const void* q, const void* summary_pool,
                      int64_t num_blocks, const int32_t* block_table, const int32_t* seq_lens,
                      int32_t batch, int32_t max_pages, float* head_scores, hipStream_t stream);

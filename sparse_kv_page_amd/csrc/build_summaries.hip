@@ -28,7 +28,11 @@
 //     sign-fixed so its largest-magnitude entry is positive (lowest index on
 //     ties).
 //  5. C = D V in fp32 from the unrounded V; mu, V, C are rounded to the
-//     summary dtype independently.
+//     summary dtype independently. Quantized ("i4") records, [Locks] §4 and
+//     App. C.7: per group (the centroid, each basis vector, each token's
+//     coefficient row) scale = bf16(max|x| / L), L = 127 for the 8-bit
+//     centroid and coefficients and 7 for the 4-bit basis, and code =
+//     round-half-even(x / scale), all in fp32 (correctly rounded division).
 #include "common.h"
 #include "kernels.h"
 
@@ -78,7 +82,7 @@ struct GramOp<float> {
 
 }  // namespace
 
-template <typename T, int D>
+template <typename T, int D, bool I4>
 __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
   constexpr int NT = D / 16;          // row tiles of H
   constexpr int RTW = NT / 4;         // row tiles per wave
@@ -435,6 +439,61 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
   __syncthreads();
 
   // ---- 5. C = D V and the record ----
+  if constexpr (I4) {
+    float* Cs = &X[0][0];      // C [P][r]; X is free from here on
+    float* sq = &Mp[0][0][0];  // scales: centroid, basis vectors, tokens
+    for (int e = tid; e < P * r; e += 256) {
+      const int i = e / r, rho = e - i * r;
+      float s = 0.f;
+      for (int d0 = 0; d0 < D; ++d0) s = fmaf(Elem<T>::load(&kt[d0 * KT_STRIDE + i]) - mu[d0], Y[d0][rho], s);
+      Cs[e] = s;
+    }
+    __syncthreads();
+    // group scales: the waves take the centroid and the basis vectors, the
+    // first P threads their token's coefficient row
+    for (int gi = wave; gi < 1 + r; gi += 4) {
+      float m = 0.f;
+      for (int row = lane; row < D; row += 64) m = fmaxf(m, fabsf(gi == 0 ? mu[row] : Y[row][gi - 1]));
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      if (lane == 0) sq[gi] = bf16_to_f32(f32_to_bf16(m / (gi == 0 ? 127.f : 7.f)));
+    }
+    if (tid < P) {
+      float m = 0.f;
+      for (int rho = 0; rho < r; ++rho) m = fmaxf(m, fabsf(Cs[tid * r + rho]));
+      sq[1 + r + tid] = bf16_to_f32(f32_to_bf16(m / 127.f));
+    }
+    __syncthreads();
+    auto code = [](float x, float s, float L) -> int {
+      if (!(s > 0.f)) return 0;
+      return (int)fminf(fmaxf(__builtin_rintf(x / s), -L), L);
+    };
+    uint8_t* rec = a.sum_pool + ((int64_t)blk * a.Hkv + h) * a.rec_bytes;
+    constexpr int WPR = D / 8;  // 32-bit words per nibble row
+    for (int t = tid; t < (r + 2) * WPR; t += 256) {
+      const int row = t / WPR, wi = t - row * WPR;
+      const int kg = wi / (D / 32), st = wi - kg * (D / 32);
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int el = st * 32 + kg * 8 + e;
+        uint32_t nib;
+        if (row < r) {
+          nib = (uint32_t)(code(Y[el][row], sq[1 + row], 7.f) + 8);
+        } else {
+          const uint32_t byte = (uint32_t)(code(mu[el], sq[0], 127.f) + 128);
+          nib = row == r ? byte >> 4 : byte & 15u;
+        }
+        word |= nib << (4 * ((e & 1) ? 4 + (e >> 1) : (e >> 1)));
+      }
+      *reinterpret_cast<uint32_t*>(rec + row * (D / 2) + wi * 4) = word;
+    }
+    uint8_t* crec = rec + (r + 2) * (D / 2);
+    for (int e = tid; e < P * r; e += 256) crec[e] = (uint8_t)(code(Cs[e], sq[1 + r + e / r], 127.f) + 128);
+    bf16_t* srec = reinterpret_cast<bf16_t*>(crec + P * r);
+    for (int t = tid; t < 1 + r + P; t += 256) srec[t] = f32_to_bf16(sq[t]);
+    for (int t = (r + 2) * (D / 2) + P * r + 2 * (1 + r + P) + tid; t < a.rec_bytes; t += 256) rec[t] = 0;
+    return;
+  }
   T* rec = reinterpret_cast<T*>(a.sum_pool) + ((int64_t)blk * a.Hkv + h) * a.rec_elems;
   for (int d0 = tid; d0 < D; d0 += 256) rec[d0] = Elem<T>::from_f32(mu[d0]);
   for (int e = tid; e < r * D; e += 256) {
@@ -454,14 +513,17 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
   }
 }
 
-hipError_t launch_build(const BuildArgs& a, int dtype, int D, hipStream_t stream) {
+hipError_t launch_build(const BuildArgs& a, int dtype, int D, bool i4, hipStream_t stream) {
   dim3 grid(a.n, a.Hkv);
-  if (dtype == 0) {
-    if (D == 64) hipLaunchKernelGGL((build_kernel<bf16_t, 64>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((build_kernel<bf16_t, 128>), grid, dim3(256), 0, stream, a);
+  if (dtype == 0 && i4) {
+    if (D == 64) hipLaunchKernelGGL((build_kernel<bf16_t, 64, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((build_kernel<bf16_t, 128, true>), grid, dim3(256), 0, stream, a);
+  } else if (dtype == 0) {
+    if (D == 64) hipLaunchKernelGGL((build_kernel<bf16_t, 64, false>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((build_kernel<bf16_t, 128, false>), grid, dim3(256), 0, stream, a);
   } else {
-    if (D == 64) hipLaunchKernelGGL((build_kernel<float, 64>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((build_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+    if (D == 64) hipLaunchKernelGGL((build_kernel<float, 64, false>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((build_kernel<float, 128, false>), grid, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }

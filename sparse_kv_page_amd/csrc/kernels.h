@@ -51,14 +51,33 @@ struct BuildArgs {
   const int32_t* block_ids;   // [n]
   uint8_t* sum_pool;          // [blocks][Hkv][record]
   int64_t num_blocks;
-  int64_t rec_elems;
+  int64_t rec_elems;          // elements per record (bf16 / fp32 records)
+  int64_t rec_bytes;          // bytes per record
   int Hkv, P, r, n;
 };
+
+// Quantized ("i4") summary record of one (block, KV head), bytes:
+//   r + 2 nibble rows of d/2 bytes: the basis vectors' 4-bit codes (excess 8),
+//     then the high and the low nibbles of the centroid's 8-bit codes
+//     (excess 128); element a of a row lives in 32-bit word
+//     (a % 32) / 8 * (d / 32) + a / 32, nibble e / 2 (even e) or 4 + e / 2
+//     (odd e), e = a % 8
+//   P rows of r bytes: the coefficient codes (excess 128)
+//   1 + r + P bf16 scales: centroid, basis vectors, tokens
+//   zero padding to a multiple of 16 bytes
+constexpr int i4_head_bytes(int d, int r) { return (r + 2) * (d / 2); }
+constexpr int i4_scale_offset(int d, int r, int P) { return i4_head_bytes(d, r) + P * r; }
+constexpr int i4_record_bytes(int d, int r, int P) {
+  return (i4_scale_offset(d, r, P) + 2 * (1 + r + P) + 15) / 16 * 16;
+}
 
 hipError_t launch_page_score(const ScoreArgs& a, int dtype, int D, int batch, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s);
 hipError_t launch_sparse_decode(const DecodeArgs& a, int dtype, int D, int batch, hipStream_t s);
 int decode_pages_per_split(int page_size);
-hipError_t launch_build(const BuildArgs& a, int dtype, int D, hipStream_t s);
+// dtype: 0 bf16, 1 fp32 keys; i4: write quantized records (bf16 keys only)
+hipError_t launch_build(const BuildArgs& a, int dtype, int D, bool i4, hipStream_t s);
+// page scores from quantized records (bf16 q)
+hipError_t launch_page_score_i4(const ScoreArgs& a, int D, int batch, hipStream_t s);
 
 }  // namespace locks

@@ -24,7 +24,8 @@ int check_config(const locks_config_t* c) {
     return LOCKS_E_INVALID_ARG;
   if (!std::isfinite(c->softmax_scale) || !(c->softmax_scale > 0.f)) return LOCKS_E_INVALID_ARG;
   if (c->kv_dtype != LOCKS_BF16 && c->kv_dtype != LOCKS_F32) return LOCKS_E_INVALID_ARG;
-  if (c->summary_dtype != LOCKS_BF16 && c->summary_dtype != LOCKS_F32) return LOCKS_E_INVALID_ARG;
+  if (c->summary_dtype != LOCKS_BF16 && c->summary_dtype != LOCKS_F32 && c->summary_dtype != LOCKS_I4)
+    return LOCKS_E_INVALID_ARG;
   if (c->num_q_heads % c->num_kv_heads != 0) return LOCKS_E_INVALID_ARG;
   const int G = c->num_q_heads / c->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return LOCKS_E_UNSUPPORTED;
@@ -32,7 +33,13 @@ int check_config(const locks_config_t* c) {
   if (c->page_size != 16 && c->page_size != 32 && c->page_size != 64) return LOCKS_E_UNSUPPORTED;
   if (c->rank > 15 || c->rank > c->page_size - 1) return LOCKS_E_UNSUPPORTED;
   if (c->budget_pages > kMaxK) return LOCKS_E_UNSUPPORTED;
-  if (c->summary_dtype != c->kv_dtype) return LOCKS_E_UNSUPPORTED;
+  if (c->summary_dtype == LOCKS_I4) {
+    // quantized records: bf16 queries on the bf16 matrix cores, ranks 1/2/4/8
+    if (c->kv_dtype != LOCKS_BF16) return LOCKS_E_UNSUPPORTED;
+    if (c->rank != 1 && c->rank != 2 && c->rank != 4 && c->rank != 8) return LOCKS_E_UNSUPPORTED;
+  } else if (c->summary_dtype != c->kv_dtype) {
+    return LOCKS_E_UNSUPPORTED;
+  }
   return LOCKS_OK;
 }
 
@@ -47,6 +54,11 @@ int check_batch(int32_t batch, int32_t max_pages) {
 
 int64_t rec_elems(const locks_config_t* c) {
   return (int64_t)c->head_dim * (1 + c->rank) + (int64_t)c->page_size * c->rank;
+}
+
+int64_t rec_bytes(const locks_config_t* c) {
+  if (c->summary_dtype == LOCKS_I4) return locks::i4_record_bytes(c->head_dim, c->rank, c->page_size);
+  return rec_elems(c) * elem_bytes(c->summary_dtype);
 }
 
 // Workspace layout, shared by every entry point that takes a workspace:
@@ -167,7 +179,7 @@ int locks_version(void) { return 1; }
 
 size_t locks_summary_record_bytes(const locks_config_t* cfg) {
   if (check_config(cfg) != LOCKS_OK) return 0;
-  return (size_t)rec_elems(cfg) * elem_bytes(cfg->summary_dtype);
+  return (size_t)rec_bytes(cfg);
 }
 
 int locks_workspace_size(const locks_config_t* cfg, int32_t batch, int32_t max_pages, size_t* bytes) {
@@ -197,11 +209,12 @@ int locks_build_summaries(const locks_config_t* cfg, const void* k_pool, int64_t
   a.sum_pool = static_cast<uint8_t*>(summary_pool);
   a.num_blocks = num_blocks;
   a.rec_elems = rec_elems(cfg);
+  a.rec_bytes = rec_bytes(cfg);
   a.Hkv = cfg->num_kv_heads;
   a.P = cfg->page_size;
   a.r = cfg->rank;
   a.n = n_ids;
-  return hip_status(locks::launch_build(a, cfg->kv_dtype, cfg->head_dim, stream));
+  return hip_status(locks::launch_build(a, cfg->kv_dtype, cfg->head_dim, cfg->summary_dtype == LOCKS_I4, stream));
 }
 
 int locks_page_score(const locks_config_t* cfg, const void* q, const void* summary_pool,
@@ -213,8 +226,10 @@ int locks_page_score(const locks_config_t* cfg, const void* q, const void* summa
   if (st != LOCKS_OK) return st;
   if (num_blocks < 0) return LOCKS_E_INVALID_ARG;
   if (batch == 0) return LOCKS_OK;
+  if (num_blocks == 0) return LOCKS_E_INVALID_ARG;  // an empty pool cannot be read
   if (!q || !summary_pool || !block_table || !seq_lens || !head_scores) return LOCKS_E_INVALID_ARG;
   locks::ScoreArgs a = score_args(cfg, q, summary_pool, num_blocks, block_table, seq_lens, max_pages, head_scores);
+  if (cfg->summary_dtype == LOCKS_I4) return hip_status(locks::launch_page_score_i4(a, cfg->head_dim, batch, stream));
   return hip_status(locks::launch_page_score(a, cfg->kv_dtype, cfg->head_dim, batch, stream));
 }
 
@@ -241,6 +256,7 @@ int locks_score_select(const locks_config_t* cfg, const void* q, const void* sum
   if (st != LOCKS_OK) return st;
   if (num_blocks < 0) return LOCKS_E_INVALID_ARG;
   if (batch == 0) return LOCKS_OK;
+  if (num_blocks == 0) return LOCKS_E_INVALID_ARG;  // an empty pool cannot be read
   if (!q || !summary_pool || !block_table || !seq_lens || !selected) return LOCKS_E_INVALID_ARG;
   if (!ws || ws_bytes < score_ws_bytes(cfg, batch, max_pages)) return LOCKS_E_WORKSPACE;
   uint8_t* region = static_cast<uint8_t*>(ws) + ctl_bytes(cfg, batch);
@@ -264,6 +280,7 @@ int locks_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_
   if (st != LOCKS_OK) return st;
   if (num_blocks < 0) return LOCKS_E_INVALID_ARG;
   if (batch == 0) return LOCKS_OK;
+  if (num_blocks == 0) return LOCKS_E_INVALID_ARG;  // an empty pool cannot be read
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !selected || !out)
     return LOCKS_E_INVALID_ARG;
   if (!ws || ws_bytes < decode_ws_bytes(cfg, batch)) return LOCKS_E_WORKSPACE;
@@ -286,6 +303,7 @@ int locks_decode_step(const locks_config_t* cfg, const void* q, const void* summ
   if (st != LOCKS_OK) return st;
   if (num_blocks < 0) return LOCKS_E_INVALID_ARG;
   if (batch == 0) return LOCKS_OK;
+  if (num_blocks == 0) return LOCKS_E_INVALID_ARG;  // an empty pool cannot be read
   if (!q || !summary_pool || !k_pool || !v_pool || !block_table || !seq_lens || !selected || !out)
     return LOCKS_E_INVALID_ARG;
   if (!ws || ws_bytes < score_ws_bytes(cfg, batch, max_pages) || ws_bytes < decode_ws_bytes(cfg, batch))

@@ -1,0 +1,371 @@
+// (a2) Page scoring on quantized ("i4") summaries: [Locks] §4 Eq. (2)
+// evaluated on the stored values of the i4 storage (§4, App. C.7: 4-bit
+// basis, 8-bit centroid and coefficients, bf16 scales; the record layout is
+// described next to i4_record_bytes):
+//   s_g(j) = s_mu (mu_code . q_g) * scale
+//          + log sum_i exp( s_C[i] sum_rho C_code[i][rho] s_V[rho] (V_code[rho] . q_g) * scale )
+//
+// The wave structure is the bf16 LDS-staged scorer's: a ring of record
+// slots per wave filled by direct global->LDS loads (16-byte chunks of the
+// nibble rows XOR-swizzled by row), several pages per iteration, scores
+// staged in LDS and stored coalesced. What differs is the operand decode:
+//  * MFMA A operand from 4-bit fields. A 32-bit word holds 8 consecutive
+//    elements, element e at nibble e/2 (even e) or 4 + e/2 (odd e), so
+//      ((w >> 4j) << 3) & 0x00780078 | 0x41804180
+//    is the exact bf16 pair (16 + field(2j), 16 + field(2j+1)): two
+//    instructions per pair. The MFMA against q then gives
+//    A = sum_a (16 + field_a) q_a, and one MFMA per wave against the
+//    constant operand 16 gives A16 = 16 sum_a q_a, which removes the offset
+//    and the excess of the codes:
+//      basis rows (field = code + 8):       code . q = A - 1.5 A16
+//      centroid (byte = code + 128 = 16 hi + lo, hi and lo in two rows):
+//                                            code . q = 16 A_hi + A_lo - 25 A16
+//  * coefficient bytes are excess 128, one conversion instruction each, and
+//    sum_rho (b_rho - 128) w_rho = sum_rho b_rho w_rho - 128 sum_rho w_rho.
+#include "common.h"
+#include "kernels.h"
+#include "score_lds.h"
+
+#include <atomic>
+#include <type_traits>
+
+namespace locks {
+
+constexpr int kI4MaxPpw = 64;        // pages per wave (block ids in one VGPR)
+constexpr int kI4Budget = 40 * 1024;  // LDS bytes per workgroup: 4 workgroups per CU
+
+template <int D, int RT, int P, int G>
+struct I4Rec {
+  static constexpr int kRowBytes = D / 2;
+  static constexpr int kHeadBytes = i4_head_bytes(D, RT);
+  static constexpr int kScaleOff = i4_scale_offset(D, RT, P);
+  static constexpr int kBytes = i4_record_bytes(D, RT, P);
+  static constexpr int kChunks = kBytes / 16;
+  static constexpr int kInstr = (kChunks + 63) / 64;         // DMA instructions per record
+  static constexpr int kTail = kChunks - (kInstr - 1) * 64;  // lanes of the last one
+  static constexpr int kRowChunks = kRowBytes / 16;          // 4 (d = 128) or 2 (d = 64)
+  static constexpr int kHeadChunks = kHeadBytes / 16;
+  static constexpr int kExtra = 4 * (kScorePagesPerIter * G * 16 + kI4MaxPpw * G) * 4;
+  static constexpr int kNs0 = (kI4Budget - kExtra) / (4 * kBytes);
+  static constexpr int kNs = kNs0 < 2 ? 2 : (kNs0 > 8 ? 8 : kNs0);
+  static_assert(kBytes % 16 == 0 && kHeadBytes % 16 == 0, "whole 16-byte chunks");
+  // LDS chunk x holds global chunk swz(x) (an involution inside each nibble row)
+  static __device__ __forceinline__ int swz(int x) {
+    if (x >= kHeadChunks) return x;
+    const int row = x / kRowChunks;
+    return row * kRowChunks + ((x % kRowChunks) ^ (row % kRowChunks));
+  }
+};
+
+template <int D, int RT, int GQ, int P>
+struct alignas(16) ScoreI4Lds {
+  using R = I4Rec<D, RT, P, GQ>;
+  uint8_t slots[kScoreWaves][R::kNs][R::kBytes];
+  float wbuf[kScoreWaves][kScorePagesPerIter][GQ][16];
+  float sbuf[kScoreWaves][kI4MaxPpw][GQ];
+};
+
+// bf16 pairs (16 + field) of the 8 nibbles of w, in element order
+__device__ __forceinline__ bf16x8_t nibbles_to_bf16(uint32_t w) {
+  constexpr uint32_t kMask = 0x00780078u, kBias = 0x41804180u;
+  const u32x4_t v = {((w << 3) & kMask) | kBias, ((w >> 1) & kMask) | kBias, ((w >> 5) & kMask) | kBias,
+                     ((w >> 9) & kMask) | kBias};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// One wave scores pages [p0, p0 + min(ppw, Jc - p0)) of the unit (b, h) for
+// all G heads (ppw <= kI4MaxPpw, p0 wave-uniform).
+template <int D, int RT, int GQ, int P>
+__device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, int p0, int ppw,
+                                              ScoreI4Lds<D, RT, GQ, P>& L) {
+  using M = ScoreMfma<bf16_t, D>;
+  using R = I4Rec<D, RT, P, GQ>;
+  constexpr int G = GQ;
+  constexpr int lph = 64 / G;                    // lanes per head
+  constexpr bool kPartial = P < lph;             // lanes u >= P hold no token
+  constexpr int TPL = kPartial ? 1 : P / lph;    // tokens per lane
+  constexpr int NS = R::kNs;
+  constexpr int kSteps = M::kSteps;
+  constexpr int kWVec = (RT + 2 + 3) / 4;
+  constexpr int kSW = (RT + 2) / 2;              // dwords holding s_mu, s_V[0..RT-1]
+  auto& slots = L.slots;
+  auto& wbuf = L.wbuf;
+  auto& sbuf = L.sbuf;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int Hq = a.Hkv * G;
+  if (p0 >= a.max_pages) return;
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+  int my_bid = lane < ppw && p0 + lane < a.max_pages ? bt_row[p0 + lane] : -1;
+  const int T_b = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.max_pages, P));
+  const int Jc = T_b / P;
+  if (p0 >= Jc) return;
+  const int np = min(ppw, Jc - p0);
+
+  const int n = lane & 15;
+  const int kg = lane >> 4;
+  typename M::Op qb[kSteps];
+  M::load_b(qb, reinterpret_cast<const bf16_t*>(a.q) + ((int64_t)b * Hq + (int64_t)h * G + (n < G ? n : 0)) * D,
+            n < G, kg);
+  // settle the ordinary loads before the record loads start (the wait counts
+  // below assume only record loads are pending)
+  wait_vm_const<0>();
+  my_bid = __builtin_amdgcn_mov_dpp(my_bid, 0xE4, 0xf, 0xf, false);  // identity; orders the use after the wait
+  auto bid_at = [&](int t) { return __builtin_amdgcn_readlane(my_bid, t); };  // t wave-uniform, < 64
+  const int g = lane / lph;
+  const int u = lane - g * lph;
+  const float zscale = a.scale * kLog2e;
+
+  // A16 = 16 sum_a q_g[a] for the lane's head g: one MFMA against the constant 16
+  float a16;
+  {
+    typename M::Op cop[kSteps];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) cop[s] = nibbles_to_bf16(0u);
+    const f32x4_t c16 = M::product(cop, qb);
+    if (n < G && kg == 0) wbuf[wave][0][n][0] = c16[0];
+    wave_lds_sync();
+    a16 = wbuf[wave][0][g][0];
+    wave_lds_sync();
+  }
+
+  auto bid_ok = [&](int bid) { return bid >= 0 && (int64_t)bid < a.num_blocks; };
+  const uint8_t* pool = a.sum_pool + (int64_t)h * R::kBytes;
+  const int64_t blk_stride = (int64_t)a.Hkv * R::kBytes;
+
+  int src_off[R::kInstr];
+#pragma unroll
+  for (int j = 0; j < R::kInstr; ++j) {
+    const int x = 64 * j + lane;
+    src_off[j] = (x < R::kChunks ? R::swz(x) : 0) * 16;
+  }
+  // A operand: lane (n, kg) reads record row n (rows past the centroid's two
+  // read row 0; their MFMA output rows are never used) at its k groups
+  const int arow = n < RT + 2 ? n : 0;
+  int a_off;
+  if constexpr (D == 128) a_off = (arow * R::kRowChunks + (kg ^ (arow % R::kRowChunks))) * 16;
+  else a_off = (arow * R::kRowChunks + ((kg >> 1) ^ (arow % R::kRowChunks))) * 16 + (kg & 1) * 8;
+
+  auto issue = [&](int t, int slot) {
+    const int bid = bid_at(t);
+    const uint8_t* rec = pool + (int64_t)(bid_ok(bid) ? bid : 0) * blk_stride;
+    const uint32_t dst = lds_addr(&slots[wave][slot][0]);
+#pragma unroll
+    for (int j = 0; j < R::kInstr; ++j) {
+      if (j < R::kInstr - 1 || lane < R::kTail) dma16(rec + src_off[j], dst + j * 1024);
+    }
+  };
+
+  const int npre = np < NS ? np : NS;
+  for (int t = 0; t < npre; ++t) issue(t, t);
+
+  auto score_pages = [&](auto npg_tag, int t, int s0) {
+    constexpr int NPG = decltype(npg_tag)::value;
+    const uint8_t* rec[NPG];
+    rec[0] = &slots[wave][s0][0];
+#pragma unroll
+    for (int p = 1; p < NPG; ++p) rec[p] = &slots[wave][(s0 + p) % NS][0];
+
+    // ---- A: code . q for the basis rows and the centroid's nibble rows ----
+    typename M::Op av[NPG][kSteps];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      if constexpr (D == 128) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(rec[p] + a_off);
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) av[p][s] = nibbles_to_bf16(w[s]);
+      } else {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(rec[p] + a_off);
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) av[p][s] = nibbles_to_bf16(w[s]);
+      }
+    }
+    f32x4_t acc[NPG];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) acc[p] = M::product(av[p], qb);
+    if (n < G) {
+#pragma unroll
+      for (int p = 0; p < NPG; ++p) *reinterpret_cast<f32x4_t*>(&wbuf[wave][p][n][kg * 4]) = acc[p];
+    }
+    wave_lds_sync();
+    float ws[NPG][RT], wsum[NPG], qmu[NPG];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      float w[kWVec * 4];
+#pragma unroll
+      for (int v = 0; v < kWVec; ++v) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&wbuf[wave][p][g][v * 4]);
+        w[4 * v] = x[0]; w[4 * v + 1] = x[1]; w[4 * v + 2] = x[2]; w[4 * v + 3] = x[3];
+      }
+      uint32_t sw[kSW];
+#pragma unroll
+      for (int i = 0; i < kSW; ++i) sw[i] = *reinterpret_cast<const uint32_t*>(rec[p] + R::kScaleOff + 4 * i);
+      auto sc = [&](int k) { return (k & 1) ? bf16_hi(sw[k >> 1]) : bf16_lo(sw[k >> 1]); };
+      qmu[p] = sc(0) * (16.f * w[RT] + w[RT + 1] - 25.f * a16);
+      wsum[p] = 0.f;
+#pragma unroll
+      for (int rho = 0; rho < RT; ++rho) {
+        ws[p][rho] = (w[rho] - 1.5f * a16) * sc(1 + rho) * zscale;
+        wsum[p] += ws[p][rho];
+      }
+    }
+
+    // ---- B: logits of the lane's tokens u, u + lph, ... ----
+    float z[NPG][TPL];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      const uint8_t* cb = rec[p] + R::kHeadBytes;
+      const uint8_t* tsc = rec[p] + R::kScaleOff + 2 * (1 + RT);
+#pragma unroll
+      for (int tt = 0; tt < TPL; ++tt) {
+        int tok = u + lph * tt;
+        if constexpr (kPartial) tok = tok < P ? tok : 0;
+        uint32_t cw[(RT + 3) / 4];
+        if constexpr (RT == 8) {
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(cb + tok * 8);
+          cw[0] = v[0]; cw[1] = v[1];
+        } else if constexpr (RT == 4) {
+          cw[0] = *reinterpret_cast<const uint32_t*>(cb + tok * 4);
+        } else if constexpr (RT == 2) {
+          cw[0] = *reinterpret_cast<const uint16_t*>(cb + tok * 2);
+        } else {
+          cw[0] = cb[tok];
+        }
+        float sacc = 0.f;
+#pragma unroll
+        for (int rho = 0; rho < RT; ++rho)
+          sacc = fmaf(ws[p][rho], (float)((cw[rho >> 2] >> (8 * (rho & 3))) & 0xffu), sacc);
+        const float st = bf16_to_f32(*reinterpret_cast<const bf16_t*>(tsc + 2 * tok));
+        float zz = st * fmaf(-128.f, wsum[p], sacc);
+        if constexpr (kPartial) zz = u < P ? zz : -INFINITY;
+        z[p][tt] = zz;
+      }
+    }
+    float mx[NPG], sm[NPG];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      mx[p] = z[p][0];
+#pragma unroll
+      for (int tt = 1; tt < TPL; ++tt) mx[p] = fmaxf(mx[p], z[p][tt]);
+    }
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) mx[p] = group_max<lph>(mx[p]);
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      sm[p] = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < TPL; ++tt) sm[p] += exp2_fast(z[p][tt] - mx[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) sm[p] = group_sum<lph>(sm[p]);
+    if (u == 0) {
+#pragma unroll
+      for (int p = 0; p < NPG; ++p) {
+        const int bid = bid_at(t + p);
+        const float s = qmu[p] * a.scale + (mx[p] + log2_fast(sm[p])) * kLn2;
+        sbuf[wave][t + p][g] = bid_ok(bid) ? s : -INFINITY;
+      }
+    }
+  };
+
+  int slot = 0;
+  int t = 0;
+  constexpr int KI = NS - 1 < kScorePagesPerIter ? (NS - 1 < 1 ? 1 : NS - 1) : kScorePagesPerIter;
+  for (; t + KI - 1 < np; t += KI) {
+    wait_vm_pages<R::kInstr, NS - 1>(min(np, t + NS) - (t + KI));  // records issued after page t+KI-1
+    score_pages(std::integral_constant<int, KI>{}, t, slot);
+#pragma unroll
+    for (int p = 0; p < KI; ++p)
+      if (t + p + NS < np) issue(t + p + NS, (slot + p) % NS);
+    slot = (slot + KI) % NS;
+  }
+  for (; t < np; ++t) {
+    wait_vm_pages<R::kInstr, NS - 1>(min(np, t + NS) - (t + 1));
+    score_pages(std::integral_constant<int, 1>{}, t, slot);
+    slot = slot + 1 == NS ? 0 : slot + 1;
+  }
+  wave_lds_sync();
+  float* out = a.scores + ((int64_t)b * Hq + (int64_t)h * G) * a.max_pages + p0;
+  if (lane < np) {
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) out[(int64_t)gg * a.max_pages + lane] = sbuf[wave][lane][gg];
+  }
+}
+
+template <int D, int RT, int GQ, int P>
+__global__ __launch_bounds__(256, 4) void page_score_i4_kernel(ScoreArgs a) {
+  __shared__ ScoreI4Lds<D, RT, GQ, P> lds;
+  const int wave = threadIdx.x >> 6;
+  const int p0 = __builtin_amdgcn_readfirstlane((blockIdx.x * kScoreWaves + wave) * a.ppw);
+  score_wave_i4<D, RT, GQ, P>(a, blockIdx.z, blockIdx.y, p0, a.ppw, lds);
+}
+
+namespace {
+
+template <int D, int RT, int GQ, int P>
+hipError_t launch_i4(ScoreArgs a, int batch, hipStream_t stream) {
+  static_assert(sizeof(ScoreI4Lds<D, RT, GQ, P>) <= kI4Budget, "LDS budget");
+  static std::atomic<int> cached{0};
+  int waves = cached.load(std::memory_order_relaxed);
+  if (waves == 0) {
+    int dev = 0, cus = 0, blocks = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, reinterpret_cast<const void*>(&page_score_i4_kernel<D, RT, GQ, P>), 256, 0) != hipSuccess ||
+        blocks <= 0)
+      blocks = 1;
+    waves = cus * blocks * kScoreWaves;
+    cached.store(waves, std::memory_order_relaxed);
+  }
+  // pages per wave for one round of resident waves, at most kI4MaxPpw
+  const int64_t total = (int64_t)batch * a.Hkv * a.max_pages;
+  int64_t ppw = (total + waves - 1) / waves;
+  ppw = ppw < 1 ? 1 : (ppw > kI4MaxPpw ? kI4MaxPpw : ppw);
+  a.ppw = (int)ppw;
+  const int waves_per_unit = (int)((a.max_pages + ppw - 1) / ppw);
+  const dim3 grid((waves_per_unit + kScoreWaves - 1) / kScoreWaves, a.Hkv, batch);
+  hipLaunchKernelGGL((page_score_i4_kernel<D, RT, GQ, P>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int RT, int GQ>
+hipError_t launch_i4_p(const ScoreArgs& a, int batch, hipStream_t s) {
+  switch (a.P) {
+    case 16: return launch_i4<D, RT, GQ, 16>(a, batch, s);
+    case 32: return launch_i4<D, RT, GQ, 32>(a, batch, s);
+    case 64: return launch_i4<D, RT, GQ, 64>(a, batch, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D, int RT>
+hipError_t launch_i4_g(const ScoreArgs& a, int batch, hipStream_t s) {
+  switch (a.G) {
+    case 1: return launch_i4_p<D, RT, 1>(a, batch, s);
+    case 2: return launch_i4_p<D, RT, 2>(a, batch, s);
+    case 4: return launch_i4_p<D, RT, 4>(a, batch, s);
+    case 8: return launch_i4_p<D, RT, 8>(a, batch, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_i4_r(const ScoreArgs& a, int batch, hipStream_t s) {
+  switch (a.r) {
+    case 1: return launch_i4_g<D, 1>(a, batch, s);
+    case 2: return launch_i4_g<D, 2>(a, batch, s);
+    case 4: return launch_i4_g<D, 4>(a, batch, s);
+    case 8: return launch_i4_g<D, 8>(a, batch, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_page_score_i4(const ScoreArgs& a, int D, int batch, hipStream_t stream) {
+  return D == 64 ? launch_i4_r<64>(a, batch, stream) : launch_i4_r<128>(a, batch, stream);
+}
+
+}  // namespace locks

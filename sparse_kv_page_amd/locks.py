@@ -22,6 +22,7 @@ LOCKS_E_WORKSPACE = -3
 LOCKS_E_HIP = -4
 LOCKS_BF16 = 0
 LOCKS_F32 = 1
+LOCKS_I4 = 2  # summary dtype only: 4-bit basis, 8-bit centroid and coefficients, bf16 scales
 
 # every exported entry point declared in include/locks.h
 EXPORTED = ("locks_status_string", "locks_version", "locks_summary_record_bytes",
@@ -46,7 +47,7 @@ class Config(ctypes.Structure):
 
 def make_config(head_dim, page_size, rank, num_q_heads, num_kv_heads, budget_pages,
                 kv_dtype="bf16", summary_dtype=None, softmax_scale=None) -> Config:
-    dt = {"bf16": LOCKS_BF16, "f32": LOCKS_F32}
+    dt = {"bf16": LOCKS_BF16, "f32": LOCKS_F32, "i4": LOCKS_I4}
     sd = summary_dtype or kv_dtype
     scale = softmax_scale if softmax_scale is not None else head_dim ** -0.5
     return Config(head_dim, page_size, rank, num_q_heads, num_kv_heads, budget_pages,
@@ -188,17 +189,22 @@ def locks_decode_step(cfg, q, summary_pool, k_pool, v_pool, num_blocks, block_ta
 # Convenience layer over torch tensors (allocation of outputs / workspace)
 # --------------------------------------------------------------------------
 def summary_pool_for(cfg: Config, num_blocks: int, device) -> torch.Tensor:
-    """Empty summary pool [blocks][H_kv][record elements] in the summary dtype."""
+    """Empty summary pool [blocks][H_kv][record elements] in the summary dtype
+    (uint8 bytes for LOCKS_I4 records)."""
     rb = locks_summary_record_bytes(cfg)
     if rb == 0:
         raise LocksError("locks_summary_record_bytes", LOCKS_E_UNSUPPORTED, "bad config")
+    if cfg.summary_dtype == LOCKS_I4:
+        return torch.empty((num_blocks, cfg.num_kv_heads, rb), dtype=torch.uint8, device=device)
     dt = torch.bfloat16 if cfg.summary_dtype == LOCKS_BF16 else torch.float32
     el = rb // (2 if dt == torch.bfloat16 else 4)
     return torch.empty((num_blocks, cfg.num_kv_heads, el), dtype=dt, device=device)
 
 
 def split_records(cfg: Config, pool: torch.Tensor):
-    """Views (mu [..][d], vt [..][r][d], coef [..][P][r]) of a summary pool."""
+    """Views (mu [..][d], vt [..][r][d], coef [..][P][r]) of a bf16 / fp32 summary pool."""
+    if cfg.summary_dtype == LOCKS_I4:
+        raise ValueError("LOCKS_I4 records hold packed codes, not element views")
     d, r, P = cfg.head_dim, cfg.rank, cfg.page_size
     mu = pool[..., :d]
     vt = pool[..., d:d + r * d].unflatten(-1, (r, d))

@@ -43,7 +43,7 @@ class Workload:
     rank: int
     budget_pages: int
     kv_dtype: str            # "bf16" or "f32"
-    summary_dtype: str       # "bf16" or "f32"
+    summary_dtype: str       # "bf16", "f32" or "i4" (quantized records)
     centroid_std: float = 0.5
     ar_rho: float = 0.0
     basis_var: tuple = (4.0, 2.0, 1.0, 0.5, 0.25, 0.125)
@@ -200,3 +200,29 @@ def random_summaries(wl: Workload, seed: int = 0, device="cpu"):
     coef = torch.randn((n, H, P, r), generator=g, device=dev, dtype=f32) * sd
     dt = torch_dtype(wl.summary_dtype)
     return mu.to(dt), v.transpose(-1, -2).contiguous().to(dt), coef.to(dt)
+
+
+def random_i4_codes(wl: Workload, seed: int = 0, device="cpu"):
+    """Random quantized summary records (codes and scales, not fits) for every
+    (block, KV head): 4-bit basis codes uniform in [-7, 7], 8-bit centroid and
+    coefficient codes uniform in [-127, 127], scales log-uniform and cast to
+    bf16 (basis 0.02-0.07, centroid 0.004-0.016, coefficients 0.004-0.05).
+    Returns a dict of tensors: mu_code [blocks][Hkv][d], vt_code [..][r][d],
+    coef_code [..][P][r] (int32) and mu_scale [blocks][Hkv], vt_scale [..][r],
+    coef_scale [..][P] (float32 holding bf16 values)."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed) + 104729)
+    n, H, d, P, r = wl.num_blocks, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.rank
+    i32 = torch.int32
+
+    def codes(shape, L):
+        return torch.randint(-L, L + 1, shape, generator=g, device=dev, dtype=i32)
+
+    def scales(shape, lo, hi):
+        u = torch.rand(shape, generator=g, device=dev, dtype=torch.float32)
+        return torch.exp(math.log(lo) + u * (math.log(hi) - math.log(lo))).to(torch.bfloat16).float()
+
+    return dict(mu_code=codes((n, H, d), 127), vt_code=codes((n, H, r, d), 7),
+                coef_code=codes((n, H, P, r), 127), mu_scale=scales((n, H), 0.004, 0.016),
+                vt_scale=scales((n, H, r), 0.02, 0.07), coef_scale=scales((n, H, P), 0.004, 0.05))

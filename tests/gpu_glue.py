@@ -223,3 +223,92 @@ def gpu_decode_step(wl, cfg, g, pool, ws=None):
     L.locks_decode_step(cfg, g["q"], pool, g["k_pool"], g["v_pool"], wl.num_blocks, g["block_table"],
                         g["seq_lens"], wl.batch, wl.max_pages, sel, out, lse, ws, nbytes)
     return sel, out, lse
+
+
+# --------------------------------------------------------------------------
+# quantized (LOCKS_I4) records: packing from codes and scales, written from
+# the record layout that include/locks.h states (test side; no arithmetic of
+# the method, only bit placement)
+# --------------------------------------------------------------------------
+def i4_record_bytes(d, r, P):
+    raw = (r + 2) * d // 2 + P * r + 2 * (1 + r + P)
+    return (raw + 15) // 16 * 16
+
+
+def _nibble_slots(d):
+    """(word index, bit offset) of element a of a row of d 4-bit fields."""
+    a = np.arange(d)
+    e = a % 8
+    word = (a % 32) // 8 * (d // 32) + a // 32
+    m = np.where(e % 2 == 0, e // 2, 4 + (e - 1) // 2)
+    return word, 4 * m
+
+
+def _bf16_bits(x):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    assert torch.equal(t.float(), torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))), \
+        "scales must be bf16 values"
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def pack_i4(qs, d, r, P):
+    """Codes/scales (leading dims [...]) -> uint8 records [...][record bytes]."""
+    lead = qs["mu_code"].shape[:-1]
+    n = int(np.prod(lead)) if lead else 1
+    mu_c = np.asarray(qs["mu_code"]).reshape(n, d)
+    vt_c = np.asarray(qs["vt_code"]).reshape(n, r, d)
+    cf_c = np.asarray(qs["coef_code"]).reshape(n, P, r)
+    assert np.abs(vt_c).max(initial=0) <= 7 and np.abs(mu_c).max(initial=0) <= 127
+    assert np.abs(cf_c).max(initial=0) <= 127
+    word, shift = _nibble_slots(d)
+    mu_b = (mu_c + 128).astype(np.uint32)
+    fields = np.concatenate([(vt_c + 8).astype(np.uint32), (mu_b >> 4)[:, None], (mu_b & 15)[:, None]], axis=1)
+    words = np.zeros((n, r + 2, d // 8), np.uint32)
+    for a in range(d):
+        words[:, :, word[a]] |= fields[:, :, a] << np.uint32(shift[a])
+    out = np.zeros((n, i4_record_bytes(d, r, P)), np.uint8)
+    hb = (r + 2) * d // 2
+    out[:, :hb] = words.astype("<u4").view(np.uint8).reshape(n, hb)
+    out[:, hb:hb + P * r] = (cf_c + 128).astype(np.uint8).reshape(n, P * r)
+    sc = np.concatenate([np.asarray(qs["mu_scale"]).reshape(n, 1), np.asarray(qs["vt_scale"]).reshape(n, r),
+                         np.asarray(qs["coef_scale"]).reshape(n, P)], axis=1)
+    out[:, hb + P * r:hb + P * r + 2 * (1 + r + P)] = _bf16_bits(sc).astype("<u2").view(np.uint8).reshape(n, -1)
+    return out.reshape(tuple(lead) + (out.shape[-1],))
+
+
+def unpack_i4(rec, d, r, P):
+    """uint8 records [...][bytes] -> codes (int) and scales (float64) as in
+    oracle.quantize_summaries, plus the padding bytes."""
+    rec = np.asarray(rec, dtype=np.uint8)
+    lead = rec.shape[:-1]
+    n = int(np.prod(lead)) if lead else 1
+    rec = rec.reshape(n, -1)
+    hb = (r + 2) * d // 2
+    words = np.ascontiguousarray(rec[:, :hb]).view("<u4").reshape(n, r + 2, d // 8)
+    word, shift = _nibble_slots(d)
+    fields = np.stack([(words[:, :, word[a]] >> np.uint32(shift[a])) & np.uint32(15) for a in range(d)], axis=-1)
+    fields = fields.astype(np.int64)
+    mu_b = fields[:, r] * 16 + fields[:, r + 1]
+    coef_b = rec[:, hb:hb + P * r].astype(np.int64).reshape(n, P, r)
+    sb = np.ascontiguousarray(rec[:, hb + P * r:hb + P * r + 2 * (1 + r + P)]).view("<u2").reshape(n, 1 + r + P)
+    sc = torch.from_numpy(sb.astype(np.int16)).view(torch.bfloat16).double().numpy()
+    res = dict(mu_code=mu_b - 128, vt_code=fields[:, :r] - 8, coef_code=coef_b - 128,
+               mu_scale=sc[:, 0], vt_scale=sc[:, 1:1 + r], coef_scale=sc[:, 1 + r:],
+               padding=rec[:, hb + P * r + 2 * (1 + r + P):])
+    return {k: v.reshape(tuple(lead) + v.shape[1:]) for k, v in res.items()}
+
+
+def i4_pool_from_codes(wl, cfg, qs, device=DEV):
+    """Device pool [blocks][Hkv][record bytes] from codes/scales over every (block, head)."""
+    qs = {k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in qs.items()}
+    rec = pack_i4(qs, wl.head_dim, wl.rank, wl.page_size)
+    assert rec.shape[-1] == L.locks_summary_record_bytes(cfg)
+    return torch.from_numpy(rec).to(device)
+
+
+def i4_unit_summaries(wl, qs, bt, b, h, n):
+    """Dequantized (mu, vt, coef) of the first n pages of unit (b, h), by the oracle."""
+    idx = np.asarray(bt[b, :n], dtype=np.int64)
+    sub = {k: (v.cpu().numpy() if torch.is_tensor(v) else np.asarray(v))[idx, h] for k, v in qs.items()
+           if k != "padding"}
+    return oracle.dequantize_summaries(sub)

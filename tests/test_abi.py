@@ -56,6 +56,56 @@ def test_record_bytes(d, P, r, dt, expect):
     assert expect % 16 == 0  # every record stays 16-byte aligned
 
 
+@pytest.mark.parametrize("r,pages_bytes", [(8, 818), (4, 490), (2, 326)])
+def test_i4_record_bytes_follow_the_byte_model(r, pages_bytes):
+    """[Locks] App. C.7: 818 / 490 / 326 B per page at B = 16, d = 128 with scales;
+    records are that payload padded to 16 bytes."""
+    cfg = _cfg(head_dim=128, page_size=16, rank=r, summary_dtype="i4")
+    assert L.locks_summary_record_bytes(cfg) == (pages_bytes + 15) // 16 * 16
+
+
+@pytest.mark.parametrize("d,P,r", [(128, 64, 8), (128, 64, 1), (64, 32, 2), (64, 16, 4)])
+def test_i4_record_bytes_layout(d, P, r):
+    cfg = _cfg(head_dim=d, page_size=P, rank=r, summary_dtype="i4")
+    payload = d * r // 2 + P * r + d + 2 * (r + P + 1)
+    assert L.locks_summary_record_bytes(cfg) == (payload + 15) // 16 * 16
+
+
+def test_i4_packer_places_fields_as_the_header_states():
+    """The test-side packer against hand-placed words: d = 64, so a row is 8
+    words and element a sits in word ((a % 32) // 8) * 2 + a // 32 at nibble
+    a % 8 // 2 (even) or 4 + (a % 8 - 1) // 2 (odd)."""
+    import numpy as np
+    from tests import gpu_glue as gg
+    d, r, P = 64, 1, 16
+    vt = np.zeros((1, r, d), np.int64)
+    # field = code + 8; choose codes so fields are 1 .. 7 at a few elements, 8 (code 0) elsewhere
+    for a, f in [(0, 1), (1, 2), (7, 3), (8, 4), (32, 5), (63, 6), (33, 7)]:
+        vt[0, 0, a] = f - 8
+    qs = dict(mu_code=np.zeros((1, d), np.int64), vt_code=vt, coef_code=np.zeros((1, P, r), np.int64),
+              mu_scale=np.ones(1), vt_scale=np.ones((1, r)), coef_scale=np.ones((1, P)))
+    rec = gg.pack_i4(qs, d, r, P)[0]
+    words = rec[:d // 2].view("<u4")
+    base = 0x88888888
+    expect = [base] * 8
+    def put(w, m, f):
+        expect[w] = (expect[w] & ~(0xF << (4 * m))) | (f << (4 * m))
+    put(0, 0, 1)   # a = 0: word 0, nibble 0
+    put(0, 4, 2)   # a = 1: word 0, nibble 4
+    put(0, 7, 3)   # a = 7: word 0, nibble 7
+    put(2, 0, 4)   # a = 8: word 2, nibble 0
+    put(1, 0, 5)   # a = 32: word 1, nibble 0
+    put(1, 4, 7)   # a = 33: word 1, nibble 4
+    put(7, 7, 6)   # a = 63: word 7, nibble 7
+    assert [int(x) for x in words] == expect
+    # centroid code 0 is byte 128: high nibble 8, low nibble 0
+    assert all(int(x) == 0x88888888 for x in rec[d // 2:d].view("<u4"))
+    assert all(int(x) == 0 for x in rec[d:3 * d // 2].view("<u4"))
+    # coefficient code 0 is byte 128; scales 1.0 are bf16 0x3F80
+    assert all(int(x) == 128 for x in rec[3 * d // 2:3 * d // 2 + P * r])
+    assert all(int(x) == 0x3F80 for x in rec[3 * d // 2 + P * r:3 * d // 2 + P * r + 2 * (1 + r + P)].view("<u2"))
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), L.LOCKS_E_UNSUPPORTED),
     (dict(page_size=48), L.LOCKS_E_UNSUPPORTED),
@@ -71,6 +121,10 @@ def test_record_bytes(d, P, r, dt, expect):
     (dict(softmax_scale=float("nan")), L.LOCKS_E_INVALID_ARG),
     (dict(kv_dtype=7), L.LOCKS_E_INVALID_ARG),
     (dict(kv_dtype="bf16", summary_dtype="f32"), L.LOCKS_E_UNSUPPORTED),
+    (dict(kv_dtype="f32", summary_dtype="i4"), L.LOCKS_E_UNSUPPORTED),     # i4 needs bf16 queries
+    (dict(summary_dtype="i4", rank=3), L.LOCKS_E_UNSUPPORTED),             # i4 ranks: 1, 2, 4, 8
+    (dict(summary_dtype="i4", rank=16), L.LOCKS_E_UNSUPPORTED),
+    (dict(summary_dtype=3), L.LOCKS_E_INVALID_ARG),
 ])
 def test_config_errors(kw, status):
     cfg = _cfg(**kw)
@@ -122,6 +176,13 @@ def test_null_pointers_and_sizes():
         lambda: L.locks_decode_step(cfg, fake, fake, fake, fake, 10, fake, fake, 1, 4, None, fake,
                                     None, fake, 1 << 30, stream=0),
         lambda: L.locks_decode_step(cfg, fake, fake, fake, fake, -1, fake, fake, 1, 4, fake, fake,
+                                    None, fake, 1 << 30, stream=0),
+        # an empty pool cannot be read: every call that reads one wants num_blocks >= 1
+        lambda: L.locks_page_score(cfg, fake, fake, 0, fake, fake, 1, 4, fake, stream=0),
+        lambda: L.locks_score_select(cfg, fake, fake, 0, fake, fake, 1, 4, fake, fake, 1 << 30, stream=0),
+        lambda: L.locks_sparse_decode(cfg, fake, fake, fake, 0, fake, fake, fake, 1, 4, fake,
+                                      None, fake, 1 << 30, stream=0),
+        lambda: L.locks_decode_step(cfg, fake, fake, fake, fake, 0, fake, fake, 1, 4, fake, fake,
                                     None, fake, 1 << 30, stream=0),
     ]
     for c in cases:
