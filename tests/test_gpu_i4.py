@@ -274,6 +274,6 @@ def test_i4_full_size_sampled(name, rank):
                       wl.page_size)
     # (blk, h)-keyed views of the sampled records and keys
     rec = {k: {(blk, h): v[pos[blk], h] for blk, h in sample} for k, v in un.items()}
-    keys = {"k_pool": {(blk, h): d["k_pool"][blk, h].cpu() for blk, h in sample}}
+    keys = {"k_pool": {(blk, h): d["k_pool"][blk, h].cpu() for blk, h in sample}, "block_table": None}
     n_basis, _ = _check_build(wl, rec, keys, sample)
     assert n_basis >= len(sample)
