@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama8b_128k_b8")
     ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--summary-dtype", choices=("bf16", "f32", "i4"), default=None,
+                    help="summary records (default: the workload's); i4 = 4-bit basis, 8-bit "
+                         "centroid and coefficients, bf16 scales, reported as workload <name>_i4")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -53,10 +56,34 @@ def parse():
     return ap.parse_args()
 
 
+def resolve_workload(args):
+    """The named workload with the --rank / --summary-dtype overrides; i4
+    summaries are reported under <name>_i4."""
+    from sparse_kv_page_amd import synth
+    wl = synth.WORKLOADS[args.workload]
+    if args.rank is not None:
+        wl = wl.with_(rank=args.rank)
+    if args.summary_dtype is not None and args.summary_dtype != wl.summary_dtype:
+        wl = wl.with_(summary_dtype=args.summary_dtype, name=f"{wl.name}_{args.summary_dtype}")
+    return wl
+
+
+def bench_flags(args):
+    """The command-line flags that select the workload (for the recorded commands)."""
+    f = []
+    if args.workload != "llama8b_128k_b8":
+        f.append(f"--workload {args.workload}")
+    if args.rank is not None:
+        f.append(f"--rank {args.rank}")
+    if args.summary_dtype is not None:
+        f.append(f"--summary-dtype {args.summary_dtype}")
+    return (" " + " ".join(f)) if f else ""
+
+
 def main():
     args = parse()
     if args.summarize_profiles:
-        summarize_profiles(args.workload, *args.summarize_profiles)
+        summarize_profiles(resolve_workload(args), bench_flags(args), *args.summarize_profiles)
         return
     if args.full_step:
         if args.gpus != 1:
@@ -78,9 +105,7 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda"
-    wl = synth.WORKLOADS[args.workload]
-    if args.rank is not None:
-        wl = wl.with_(rank=args.rank)
+    wl = resolve_workload(args)
     cfg = L.config_for(wl)
     B, Hkv, Hq, d, P, r, k = (wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim,
                               wl.page_size, wl.rank, wl.budget_pages)
@@ -227,8 +252,8 @@ def main():
         "hbm_roofline_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": step_bytes,
         "step_achieved_GBps": round(step_gbs, 1),
-        "roofline": roofline("page_score", wl.name, summary_bytes, stage_us["page_score"]),
-        "sparse_decode_roofline": roofline("sparse_decode", wl.name, kv_bytes, stage_us["sparse_decode"]),
+        "roofline": roofline("page_score", wl, summary_bytes, stage_us["page_score"]),
+        "sparse_decode_roofline": roofline("sparse_decode", wl, kv_bytes, stage_us["sparse_decode"]),
         "staged_step_us": round(staged_ms * 1e3, 3),
         "stages_us": {n: round(v, 3) for n, v in stage_us.items()},
         "step_with_build_us": round(step_ms * 1e3 + stage_us["build_step"], 3),
@@ -391,8 +416,12 @@ def full_step(args):
 def algorithmic_bytes(wl, rec_bytes):
     """Bytes the method must move per step: the summary record of every
     complete page and the K/V rows of every attended token (sink, top-(k-2)
-    and the current page's valid tokens; all tokens when J <= k)."""
+    and the current page's valid tokens; all tokens when J <= k). A quantized
+    record counts the pages' byte model, d r/2 + P r + d + 2 (r + P + 1), not
+    the library's 16-byte padding."""
     P, k, d, Hkv = wl.page_size, wl.budget_pages, wl.head_dim, wl.num_kv_heads
+    if wl.summary_dtype == "i4":
+        rec_bytes = d * wl.rank // 2 + P * wl.rank + d + 2 * (wl.rank + P + 1)
     ekv = 2 if wl.kv_dtype == "bf16" else 4
     summary_bytes = kv_bytes = 0
     for T in wl.seq_lens:
@@ -407,16 +436,16 @@ def algorithmic_bytes(wl, rec_bytes):
 PROFILE_CMDS = {
     "stats": ("export TMPDIR=/tmp && cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv \\\n"
               "    -d $R/gpurun_out/prof_stats -o locks -- python3 -u $R/bench.py --steps 20 --warmup 5 "
-              "--no-cpu-baseline"),
+              "--no-cpu-baseline{flags}"),
     "fetch": ("export TMPDIR=/tmp && cd /tmp && timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE \\\n"
               "    --kernel-include-regex 'locks::|copyBuffer' --output-format csv -d $R/gpurun_out/prof_fetch "
               "-o fetch \\\n    -- python3 -u $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
-              "--copy-calibration 256"),
-    "summarize": ("python bench.py --summarize-profiles gpurun_out/prof_stats gpurun_out/prof_fetch "
+              "--copy-calibration 256{flags}"),
+    "summarize": ("python bench.py{flags} --summarize-profiles gpurun_out/prof_stats gpurun_out/prof_fetch "
                   "gpurun_out/prof_write"),
 }
 
-KERNEL_PATTERNS = (("page_score", ("page_score_lds_kernel", "page_score_kernel")),
+KERNEL_PATTERNS = (("page_score", ("page_score_lds_kernel", "page_score_kernel", "page_score_i4_kernel")),
                    ("select", ("select_kernel",)),
                    ("sparse_decode", ("sparse_decode_kernel",)),
                    ("build", ("build_kernel",)))
@@ -438,7 +467,7 @@ def _kernel_key(name):
     return None
 
 
-def summarize_profiles(workload, stats_dir, fetch_dir, write_dir):
+def summarize_profiles(wl, flags, stats_dir, fetch_dir, write_dir):
     """Write profiles/traffic_<workload>.json, profiles/decode_step_kernels_<workload>.md and
     profiles/memory_traffic_<workload>.md from rocprofv3 CSV output (kernel stats, one
     FETCH_SIZE pass, one WRITE_SIZE pass, each pass ending with plain 256 MiB copies)."""
@@ -448,7 +477,7 @@ def summarize_profiles(workload, stats_dir, fetch_dir, write_dir):
     from sparse_kv_page_amd import locks as L
     from sparse_kv_page_amd import synth
 
-    wl = synth.WORKLOADS[workload]
+    workload = wl.name
     cfg = L.config_for(wl)
     summary_bytes, kv_bytes = algorithmic_bytes(wl, L.locks_summary_record_bytes(cfg))
     alg = {"page_score": summary_bytes, "sparse_decode": kv_bytes}
@@ -502,7 +531,7 @@ def summarize_profiles(workload, stats_dir, fetch_dir, write_dir):
         a = alg.get(key)
         avg = next((v[1] for n, v in stats.items() if n == name), None)
         rec["kernels"][key] = {
-            "symbol": name, "source_sha1": _sha1([os.path.join(csrc, x) for x in KERNEL_SOURCES[key]]),
+            "symbol": name, "source_sha1": _sha1([os.path.join(csrc, x) for x in kernel_sources(key, wl)]),
             "fetch_kib": round(fetch[name], 1), "write_kib": round(write[name], 1),
             "hbm_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": a,
             "avg_duration_ns": round(avg * 1e3, 1) if avg else None, "calls": calls[name]}
@@ -528,15 +557,15 @@ def summarize_profiles(workload, stats_dir, fetch_dir, write_dir):
     with open(os.path.join(here, "profiles", f"decode_step_kernels_{workload}.md"), "w") as f:
         f.write(f"# Decode-step kernels, {workload}\n\nWorkload: {shape}; MI355X (gfx950), one GPU, "
                 f"ROCm 7.2.\n\nCommand (repository root on the GPU box = `R`):\n\n    "
-                + PROFILE_CMDS["stats"].replace("\n", "\n    ") +
-                "\n\nThen, without a GPU:\n\n    " + PROFILE_CMDS["summarize"] +
+                + PROFILE_CMDS["stats"].format(flags=flags).replace("\n", "\n    ") +
+                "\n\nThen, without a GPU:\n\n    " + PROFILE_CMDS["summarize"].format(flags=flags) +
                 "\n\n| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|\n" +
                 "\n".join(rows_s) + "\n\n" + "\n".join(rates) + "\n")
     with open(os.path.join(here, "profiles", f"memory_traffic_{workload}.md"), "w") as f:
         f.write(f"# Memory traffic of the decode-step kernels, {workload}\n\nSame workload as "
                 f"decode_step_kernels_{workload}.md. Two counter passes, one counter each, followed by "
                 f"three plain 256 MiB device copies used as the calibration:\n\n    "
-                + PROFILE_CMDS["fetch"].replace("\n", "\n    ") +
+                + PROFILE_CMDS["fetch"].format(flags=flags).replace("\n", "\n    ") +
                 "\n    (the same with --pmc WRITE_SIZE, -d $R/gpurun_out/prof_write -o write)\n\n"
                 f"Calibration: a 256 MiB copy reads FETCH_SIZE = {fetch_copy:.1f} KiB and WRITE_SIZE = "
                 f"{write_copy:.1f} KiB, so FETCH_SIZE is scaled by {fs:.6f} and WRITE_SIZE by {wsc:.6f}.\n\n"
@@ -551,9 +580,16 @@ def summarize_profiles(workload, stats_dir, fetch_dir, write_dir):
 # reported only while these files are unchanged)
 KERNEL_SOURCES = {
     "page_score": ("page_score.hip", "score_lds.h", "common.h", "kernels.h"),
+    "page_score_i4": ("page_score_i4.hip", "score_lds.h", "common.h", "kernels.h"),
     "select": ("select.hip", "select_unit.h", "common.h", "kernels.h"),
     "sparse_decode": ("sparse_decode.hip", "decode_split.h", "common.h", "kernels.h"),
 }
+
+
+def kernel_sources(kernel, wl):
+    if kernel == "page_score" and wl.summary_dtype == "i4":
+        return KERNEL_SOURCES["page_score_i4"]
+    return KERNEL_SOURCES.get(kernel)
 
 
 def _sha1(paths):
@@ -565,7 +601,7 @@ def _sha1(paths):
     return h.hexdigest()
 
 
-def roofline(kernel, workload, alg_bytes, avg_us):
+def roofline(kernel, wl, alg_bytes, avg_us):
     """Roofline record of one kernel: algorithmic bytes per launch over its
     average launch time (HIP events in the timed region), against the HBM
     peak. `traffic` is the measured memory traffic per launch from the
@@ -577,14 +613,14 @@ def roofline(kernel, workload, alg_bytes, avg_us):
            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
            "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(avg_us, 3)}
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(here, "profiles", f"traffic_{wl.name}.json")
     if os.path.exists(path):
         with open(path) as f:
             tr = json.load(f)
         k = tr.get("kernels", {}).get(kernel)
         csrc = os.path.join(here, "sparse_kv_page_amd", "csrc")
-        if k and kernel in KERNEL_SOURCES:
-            cur = _sha1([os.path.join(csrc, f) for f in KERNEL_SOURCES[kernel]])
+        if k and kernel_sources(kernel, wl):
+            cur = _sha1([os.path.join(csrc, f) for f in kernel_sources(kernel, wl)])
             if cur == k.get("source_sha1"):
                 rec["traffic"] = int(k["hbm_bytes_per_launch"])
                 rec["traffic_over_algorithmic"] = round(k["hbm_bytes_per_launch"] / alg_bytes, 4)
@@ -610,16 +646,31 @@ def cpu_baseline(wl, cfg, data, seconds):
     to32 = lambda t: t.to("cpu", torch.float32).numpy()
     kp = to32(data["k_pool"][used.to(data["k_pool"].device)])
     vp = to32(data["v_pool"][used.to(data["v_pool"].device)])
-    # records indexed by the local block ids (one per (page, KV head) of the sample)
-    mu, vt, cf = synth.random_summaries(sub.with_(extra_blocks=0), seed=1, device="cpu")
-    assert mu.shape[0] == used.numel()
-    mu, vt, cf = (x.double().numpy() for x in (mu, vt, cf))
+    # records indexed by the local block ids (one per (page, KV head) of the sample);
+    # quantized records are dequantized by the oracle inside the timed loop
+    if wl.summary_dtype == "i4":
+        codes = synth.random_i4_codes(sub.with_(extra_blocks=0), seed=1, device="cpu")
+        codes = {kk: v.reshape((-1,) + tuple(v.shape[2:])).numpy() for kk, v in codes.items()}
+        shape = (used.numel(), wl.num_kv_heads)
+
+        def summaries():
+            m, v, c = oracle.dequantize_summaries(codes)
+            return (x.reshape(shape + x.shape[1:]) for x in (m, v, c))
+    else:
+        recs = synth.random_summaries(sub.with_(extra_blocks=0), seed=1, device="cpu")
+        recs = [x.double().numpy() for x in recs]
+
+        def summaries():
+            return recs
     q = data["q"][:nseq].to("cpu", torch.float64).numpy()
     threads = oracle.default_threads()
+    mu, vt, cf = summaries()
+    assert mu.shape[0] == used.numel()
     oracle.decode_step(q, mu, vt, cf, kp, vp, bt_local, list(sub.seq_lens), wl.page_size,
                        wl.budget_pages, wl.softmax_scale, threads=threads)  # warm (loads lib)
     reps, t0 = 0, time.perf_counter()
     while True:
+        mu, vt, cf = summaries()
         oracle.decode_step(q, mu, vt, cf, kp, vp, bt_local, list(sub.seq_lens), wl.page_size,
                            wl.budget_pages, wl.softmax_scale, threads=threads)
         reps += 1
