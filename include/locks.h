@@ -48,7 +48,7 @@
  *   mu codes    2 rows of d/2 bytes: the high, then the low 4 bits of the
  *               centroid's 8-bit codes b in 1..255, value s_mu * (b - 128)
  *   C codes     P rows of r bytes: token i's codes b, value s_C[i] * (b - 128)
- *   scales      1 + r + P bf16: s_mu, s_V[0..r-1], s_C[0..P-1]
+ *   scales      r + 1 + P bf16: s_V[0..r-1], s_mu, s_C[0..P-1]
  *   padding     zero bytes up to a multiple of 16
  *   In a row of 4-bit fields, element a (0 <= a < d) lives in the 32-bit
  *   little-endian word w = ((a % 32) / 8) * (d / 32) + a / 32, at bits

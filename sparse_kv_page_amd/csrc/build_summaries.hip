@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
   // ---- 5. C = D V and the record ----
   if constexpr (I4) {
     float* Cs = &X[0][0];      // C [P][r]; X is free from here on
-    float* sq = &Mp[0][0][0];  // scales: centroid, basis vectors, tokens
+    float* sq = &Mp[0][0][0];  // scales in record order: basis vectors, centroid, tokens
     for (int e = tid; e < P * r; e += 256) {
       const int i = e / r, rho = e - i * r;
       float s = 0.f;
@@ -449,18 +449,18 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
       Cs[e] = s;
     }
     __syncthreads();
-    // group scales: the waves take the centroid and the basis vectors, the
+    // group scales: the waves take the basis vectors and the centroid, the
     // first P threads their token's coefficient row
-    for (int gi = wave; gi < 1 + r; gi += 4) {
+    for (int gi = wave; gi < r + 1; gi += 4) {
       float m = 0.f;
-      for (int row = lane; row < D; row += 64) m = fmaxf(m, fabsf(gi == 0 ? mu[row] : Y[row][gi - 1]));
+      for (int row = lane; row < D; row += 64) m = fmaxf(m, fabsf(gi == r ? mu[row] : Y[row][gi]));
       for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      if (lane == 0) sq[gi] = bf16_to_f32(f32_to_bf16(m / (gi == 0 ? 127.f : 7.f)));
+      if (lane == 0) sq[gi] = bf16_to_f32(f32_to_bf16(m / (gi == r ? 127.f : 7.f)));
     }
     if (tid < P) {
       float m = 0.f;
       for (int rho = 0; rho < r; ++rho) m = fmaxf(m, fabsf(Cs[tid * r + rho]));
-      sq[1 + r + tid] = bf16_to_f32(f32_to_bf16(m / 127.f));
+      sq[r + 1 + tid] = bf16_to_f32(f32_to_bf16(m / 127.f));
     }
     __syncthreads();
     auto code = [](float x, float s, float L) -> int {
@@ -478,9 +478,9 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
         const int el = st * 32 + kg * 8 + e;
         uint32_t nib;
         if (row < r) {
-          nib = (uint32_t)(code(Y[el][row], sq[1 + row], 7.f) + 8);
+          nib = (uint32_t)(code(Y[el][row], sq[row], 7.f) + 8);
         } else {
-          const uint32_t byte = (uint32_t)(code(mu[el], sq[0], 127.f) + 128);
+          const uint32_t byte = (uint32_t)(code(mu[el], sq[r], 127.f) + 128);
           nib = row == r ? byte >> 4 : byte & 15u;
         }
         word |= nib << (4 * ((e & 1) ? 4 + (e >> 1) : (e >> 1)));
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
       *reinterpret_cast<uint32_t*>(rec + row * (D / 2) + wi * 4) = word;
     }
     uint8_t* crec = rec + (r + 2) * (D / 2);
-    for (int e = tid; e < P * r; e += 256) crec[e] = (uint8_t)(code(Cs[e], sq[1 + r + e / r], 127.f) + 128);
+    for (int e = tid; e < P * r; e += 256) crec[e] = (uint8_t)(code(Cs[e], sq[r + 1 + e / r], 127.f) + 128);
     bf16_t* srec = reinterpret_cast<bf16_t*>(crec + P * r);
     for (int t = tid; t < 1 + r + P; t += 256) srec[t] = f32_to_bf16(sq[t]);
     for (int t = (r + 2) * (D / 2) + P * r + 2 * (1 + r + P) + tid; t < a.rec_bytes; t += 256) rec[t] = 0;

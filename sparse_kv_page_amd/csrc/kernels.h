@@ -63,7 +63,7 @@ struct BuildArgs {
 //     (a % 32) / 8 * (d / 32) + a / 32, nibble e / 2 (even e) or 4 + e / 2
 //     (odd e), e = a % 8
 //   P rows of r bytes: the coefficient codes (excess 128)
-//   1 + r + P bf16 scales: centroid, basis vectors, tokens
+//   r + 1 + P bf16 scales: basis vectors, centroid, tokens
 //   zero padding to a multiple of 16 bytes
 constexpr int i4_head_bytes(int d, int r) { return (r + 2) * (d / 2); }
 constexpr int i4_scale_offset(int d, int r, int P) { return i4_head_bytes(d, r) + P * r; }

@@ -16,7 +16,8 @@
 //    instructions per pair. The MFMA against q then gives
 //    A = sum_a (16 + field_a) q_a, and one MFMA per wave against the
 //    constant operand 16 gives A16 = 16 sum_a q_a, which removes the offset
-//    and the excess of the codes:
+//    and the excess of the codes (applied in the MFMA output layout, where
+//    each lane scales its own four rows):
 //      basis rows (field = code + 8):       code . q = A - 1.5 A16
 //      centroid (byte = code + 128 = 16 hi + lo, hi and lo in two rows):
 //                                            code . q = 16 A_hi + A_lo - 25 A16
@@ -31,8 +32,11 @@
 
 namespace locks {
 
-constexpr int kI4MaxPpw = 64;        // pages per wave (block ids in one VGPR)
+constexpr int kI4MaxPpw = 64;        // pages per wave (block ids in one VGPR; 128 measured slower:
+                                      // the larger score staging leaves fewer ring slots)
 constexpr int kI4Budget = 40 * 1024;  // LDS bytes per workgroup: 4 workgroups per CU
+constexpr int kI4PagesPerIter = kScorePagesPerIter;  // at most this many pages scored together
+constexpr int kI4MaxNs = 8;           // ring slots per wave
 
 template <int D, int RT, int P, int G>
 struct I4Rec {
@@ -45,9 +49,9 @@ struct I4Rec {
   static constexpr int kTail = kChunks - (kInstr - 1) * 64;  // lanes of the last one
   static constexpr int kRowChunks = kRowBytes / 16;          // 4 (d = 128) or 2 (d = 64)
   static constexpr int kHeadChunks = kHeadBytes / 16;
-  static constexpr int kExtra = 4 * (kScorePagesPerIter * G * 16 + kI4MaxPpw * G) * 4;
+  static constexpr int kExtra = 4 * (kI4PagesPerIter * G * 16 + kI4MaxPpw * G) * 4;
   static constexpr int kNs0 = (kI4Budget - kExtra) / (4 * kBytes);
-  static constexpr int kNs = kNs0 < 2 ? 2 : (kNs0 > 8 ? 8 : kNs0);
+  static constexpr int kNs = kNs0 < 2 ? 2 : (kNs0 > kI4MaxNs ? kI4MaxNs : kNs0);
   static_assert(kBytes % 16 == 0 && kHeadBytes % 16 == 0, "whole 16-byte chunks");
   // LDS chunk x holds global chunk swz(x) (an involution inside each nibble row)
   static __device__ __forceinline__ int swz(int x) {
@@ -61,15 +65,25 @@ template <int D, int RT, int GQ, int P>
 struct alignas(16) ScoreI4Lds {
   using R = I4Rec<D, RT, P, GQ>;
   uint8_t slots[kScoreWaves][R::kNs][R::kBytes];
-  float wbuf[kScoreWaves][kScorePagesPerIter][GQ][16];
+  float wbuf[kScoreWaves][kI4PagesPerIter][GQ][16];
   float sbuf[kScoreWaves][kI4MaxPpw][GQ];
 };
 
-// bf16 pairs (16 + field) of the 8 nibbles of w, in element order
-__device__ __forceinline__ bf16x8_t nibbles_to_bf16(uint32_t w) {
-  constexpr uint32_t kMask = 0x00780078u, kBias = 0x41804180u;
-  const u32x4_t v = {((w << 3) & kMask) | kBias, ((w >> 1) & kMask) | kBias, ((w >> 5) & kMask) | kBias,
-                     ((w >> 9) & kMask) | kBias};
+constexpr uint32_t kNibMask = 0x00780078u;  // one nibble at mantissa bits 3..6 of each bf16 half
+constexpr uint32_t kNibBias = 0x41804180u;  // bf16 16.0 in both halves
+
+// (x & m) | b in one instruction; m and b are held in VGPRs (a VOP3 takes no
+// literal here, and the compiler would otherwise split it into two)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t b) {
+  uint32_t r;
+  __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(b));
+  return r;
+}
+
+// bf16 pairs (16 + field) of the 8 nibbles of w, in element order; m, b =
+// kNibMask, kNibBias in VGPRs
+__device__ __forceinline__ bf16x8_t nibbles_to_bf16(uint32_t w, uint32_t m, uint32_t b) {
+  const u32x4_t v = {and_or(w << 3, m, b), and_or(w >> 1, m, b), and_or(w >> 5, m, b), and_or(w >> 9, m, b)};
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
@@ -86,8 +100,8 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   constexpr int TPL = kPartial ? 1 : P / lph;    // tokens per lane
   constexpr int NS = R::kNs;
   constexpr int kSteps = M::kSteps;
-  constexpr int kWVec = (RT + 2 + 3) / 4;
-  constexpr int kSW = (RT + 2) / 2;              // dwords holding s_mu, s_V[0..RT-1]
+  constexpr int kWVec = (RT + 1 + 3) / 4;        // scaled basis rows and the centroid term
+  constexpr int kCi = RT % 4;                    // the centroid's rows RT, RT + 1 sit in lane group RT / 4
   auto& slots = L.slots;
   auto& wbuf = L.wbuf;
   auto& sbuf = L.sbuf;
@@ -117,17 +131,17 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   const int u = lane - g * lph;
   const float zscale = a.scale * kLog2e;
 
-  // A16 = 16 sum_a q_g[a] for the lane's head g: one MFMA against the constant 16
+  uint32_t nib_m, nib_b;  // the decode constants, in VGPRs
+  __asm__("v_mov_b32 %0, %1" : "=v"(nib_m) : "i"(kNibMask));
+  __asm__("v_mov_b32 %0, %1" : "=v"(nib_b) : "i"(kNibBias));
+  // A16 = 16 sum_a q_n[a] for the lane's MFMA column n: one MFMA against the
+  // constant 16 (every output row holds it)
   float a16;
   {
     typename M::Op cop[kSteps];
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) cop[s] = nibbles_to_bf16(0u);
-    const f32x4_t c16 = M::product(cop, qb);
-    if (n < G && kg == 0) wbuf[wave][0][n][0] = c16[0];
-    wave_lds_sync();
-    a16 = wbuf[wave][0][g][0];
-    wave_lds_sync();
+    for (int s = 0; s < kSteps; ++s) cop[s] = nibbles_to_bf16(0u, nib_m, nib_b);
+    a16 = M::product(cop, qb)[0];
   }
 
   auto bid_ok = [&](int bid) { return bid >= 0 && (int64_t)bid < a.num_blocks; };
@@ -174,19 +188,35 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
       if constexpr (D == 128) {
         const u32x4_t w = *reinterpret_cast<const u32x4_t*>(rec[p] + a_off);
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) av[p][s] = nibbles_to_bf16(w[s]);
+        for (int s = 0; s < kSteps; ++s) av[p][s] = nibbles_to_bf16(w[s], nib_m, nib_b);
       } else {
         const u32x2_t w = *reinterpret_cast<const u32x2_t*>(rec[p] + a_off);
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) av[p][s] = nibbles_to_bf16(w[s]);
+        for (int s = 0; s < kSteps; ++s) av[p][s] = nibbles_to_bf16(w[s], nib_m, nib_b);
       }
     }
     f32x4_t acc[NPG];
 #pragma unroll
     for (int p = 0; p < NPG; ++p) acc[p] = M::product(av[p], qb);
-    if (n < G) {
+    // Lane (n, kg) holds rows 4kg .. 4kg+3 of head n; it scales them where
+    // they are (scales s_V[4kg .. 4kg+3], or s_mu at index RT, in one 8-byte
+    // read):
+    //   basis row rho < RT:   (A - 1.5 A16) s_V[rho] * scale * log2(e)
+    //   row RT (centroid):    (16 A_hi + A_lo - 25 A16) s_mu * scale
+    // then the G heads' rows go through LDS to the lanes that own the head.
 #pragma unroll
-      for (int p = 0; p < NPG; ++p) *reinterpret_cast<f32x4_t*>(&wbuf[wave][p][n][kg * 4]) = acc[p];
+    for (int p = 0; p < NPG; ++p) {
+      const u32x2_t sv = *reinterpret_cast<const u32x2_t*>(rec[p] + R::kScaleOff + 8 * kg);
+      f32x4_t o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sz = ((i & 1) ? bf16_hi(sv[i >> 1]) : bf16_lo(sv[i >> 1])) * zscale;
+        o[i] = fmaf(acc[p][i], sz, -1.5f * a16 * sz);
+      }
+      const float smu = (kCi & 1) ? bf16_hi(sv[kCi >> 1]) : bf16_lo(sv[kCi >> 1]);
+      const float cent = (16.f * acc[p][kCi] + acc[p][kCi + 1] - 25.f * a16) * smu * a.scale;
+      if (kg == RT / 4) o[kCi] = cent;
+      if (n < G) *reinterpret_cast<f32x4_t*>(&wbuf[wave][p][n][kg * 4]) = o;
     }
     wave_lds_sync();
     float ws[NPG][RT], wsum[NPG], qmu[NPG];
@@ -198,17 +228,14 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
         const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&wbuf[wave][p][g][v * 4]);
         w[4 * v] = x[0]; w[4 * v + 1] = x[1]; w[4 * v + 2] = x[2]; w[4 * v + 3] = x[3];
       }
-      uint32_t sw[kSW];
-#pragma unroll
-      for (int i = 0; i < kSW; ++i) sw[i] = *reinterpret_cast<const uint32_t*>(rec[p] + R::kScaleOff + 4 * i);
-      auto sc = [&](int k) { return (k & 1) ? bf16_hi(sw[k >> 1]) : bf16_lo(sw[k >> 1]); };
-      qmu[p] = sc(0) * (16.f * w[RT] + w[RT + 1] - 25.f * a16);
-      wsum[p] = 0.f;
+      qmu[p] = w[RT];
+      float sum = 0.f;
 #pragma unroll
       for (int rho = 0; rho < RT; ++rho) {
-        ws[p][rho] = (w[rho] - 1.5f * a16) * sc(1 + rho) * zscale;
-        wsum[p] += ws[p][rho];
+        ws[p][rho] = w[rho];
+        sum += w[rho];
       }
+      wsum[p] = -128.f * sum;
     }
 
     // ---- B: logits of the lane's tokens u, u + lph, ... ----
@@ -216,7 +243,7 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
 #pragma unroll
     for (int p = 0; p < NPG; ++p) {
       const uint8_t* cb = rec[p] + R::kHeadBytes;
-      const uint8_t* tsc = rec[p] + R::kScaleOff + 2 * (1 + RT);
+      const uint8_t* tsc = rec[p] + R::kScaleOff + 2 * (RT + 1);
 #pragma unroll
       for (int tt = 0; tt < TPL; ++tt) {
         int tok = u + lph * tt;
@@ -232,12 +259,12 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
         } else {
           cw[0] = cb[tok];
         }
-        float sacc = 0.f;
+        float sacc = wsum[p];  // holds -128 sum_rho w_rho: the codes' excess
 #pragma unroll
         for (int rho = 0; rho < RT; ++rho)
           sacc = fmaf(ws[p][rho], (float)((cw[rho >> 2] >> (8 * (rho & 3))) & 0xffu), sacc);
         const float st = bf16_to_f32(*reinterpret_cast<const bf16_t*>(tsc + 2 * tok));
-        float zz = st * fmaf(-128.f, wsum[p], sacc);
+        float zz = st * sacc;
         if constexpr (kPartial) zz = u < P ? zz : -INFINITY;
         z[p][tt] = zz;
       }
@@ -263,7 +290,7 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
 #pragma unroll
       for (int p = 0; p < NPG; ++p) {
         const int bid = bid_at(t + p);
-        const float s = qmu[p] * a.scale + (mx[p] + log2_fast(sm[p])) * kLn2;
+        const float s = qmu[p] + (mx[p] + log2_fast(sm[p])) * kLn2;
         sbuf[wave][t + p][g] = bid_ok(bid) ? s : -INFINITY;
       }
     }
@@ -271,7 +298,7 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
 
   int slot = 0;
   int t = 0;
-  constexpr int KI = NS - 1 < kScorePagesPerIter ? (NS - 1 < 1 ? 1 : NS - 1) : kScorePagesPerIter;
+  constexpr int KI = NS - 1 < kI4PagesPerIter ? (NS - 1 < 1 ? 1 : NS - 1) : kI4PagesPerIter;
   for (; t + KI - 1 < np; t += KI) {
     wait_vm_pages<R::kInstr, NS - 1>(min(np, t + NS) - (t + KI));  // records issued after page t+KI-1
     score_pages(std::integral_constant<int, KI>{}, t, slot);

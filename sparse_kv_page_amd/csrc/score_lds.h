@@ -110,7 +110,8 @@ __device__ __forceinline__ void wait_vm_const() {
 
 template <int STEP, int MAXN>
 __device__ __forceinline__ void wait_vm_pages(int pages) {
-  // pages in 0 .. MAXN; the immediate must be a constant, hence the switch
+  // pages in 0 .. MAXN (<= 11, STEP * MAXN <= 63); the immediate must be a constant, hence the switch
+  static_assert(MAXN <= 11 && STEP * MAXN <= 63, "vmcnt range");
   switch (pages) {
     case 0: wait_vm_const<0>(); break;
     case 1: if constexpr (MAXN >= 1) wait_vm_const<1 * STEP>(); break;
@@ -119,7 +120,11 @@ __device__ __forceinline__ void wait_vm_pages(int pages) {
     case 4: if constexpr (MAXN >= 4) wait_vm_const<4 * STEP>(); break;
     case 5: if constexpr (MAXN >= 5) wait_vm_const<5 * STEP>(); break;
     case 6: if constexpr (MAXN >= 6) wait_vm_const<6 * STEP>(); break;
-    default: if constexpr (MAXN >= 7) wait_vm_const<7 * STEP>(); break;
+    case 7: if constexpr (MAXN >= 7) wait_vm_const<7 * STEP>(); break;
+    case 8: if constexpr (MAXN >= 8) wait_vm_const<8 * STEP>(); break;
+    case 9: if constexpr (MAXN >= 9) wait_vm_const<9 * STEP>(); break;
+    case 10: if constexpr (MAXN >= 10) wait_vm_const<10 * STEP>(); break;
+    default: if constexpr (MAXN >= 11) wait_vm_const<11 * STEP>(); break;
   }
   compiler_fence();
 }

@@ -270,7 +270,7 @@ def pack_i4(qs, d, r, P):
     hb = (r + 2) * d // 2
     out[:, :hb] = words.astype("<u4").view(np.uint8).reshape(n, hb)
     out[:, hb:hb + P * r] = (cf_c + 128).astype(np.uint8).reshape(n, P * r)
-    sc = np.concatenate([np.asarray(qs["mu_scale"]).reshape(n, 1), np.asarray(qs["vt_scale"]).reshape(n, r),
+    sc = np.concatenate([np.asarray(qs["vt_scale"]).reshape(n, r), np.asarray(qs["mu_scale"]).reshape(n, 1),
                          np.asarray(qs["coef_scale"]).reshape(n, P)], axis=1)
     out[:, hb + P * r:hb + P * r + 2 * (1 + r + P)] = _bf16_bits(sc).astype("<u2").view(np.uint8).reshape(n, -1)
     return out.reshape(tuple(lead) + (out.shape[-1],))
@@ -293,7 +293,7 @@ def unpack_i4(rec, d, r, P):
     sb = np.ascontiguousarray(rec[:, hb + P * r:hb + P * r + 2 * (1 + r + P)]).view("<u2").reshape(n, 1 + r + P)
     sc = torch.from_numpy(sb.astype(np.int16)).view(torch.bfloat16).double().numpy()
     res = dict(mu_code=mu_b - 128, vt_code=fields[:, :r] - 8, coef_code=coef_b - 128,
-               mu_scale=sc[:, 0], vt_scale=sc[:, 1:1 + r], coef_scale=sc[:, 1 + r:],
+               mu_scale=sc[:, r], vt_scale=sc[:, :r], coef_scale=sc[:, r + 1:],
                padding=rec[:, hb + P * r + 2 * (1 + r + P):])
     return {k: v.reshape(tuple(lead) + v.shape[1:]) for k, v in res.items()}
 
