@@ -8,8 +8,10 @@ namespace locks {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecTile = 16;
-constexpr int kDecTilesPerWave = 2;
-constexpr int kDecTilesPerWg = kDecWaves * kDecTilesPerWave;
+// 16-token tiles per wave: 4 (8 pages of 64 per workgroup, 2 workgroups per
+// CU) when the grid still fills the chip, else 2 (more, smaller splits)
+constexpr int kDecTilesPerWaveLarge = 4;
+constexpr int kDecTilesPerWaveSmall = 2;
 
 namespace dec_detail {
 
@@ -72,9 +74,9 @@ struct alignas(16) DecodeLds {
 };
 
 
-// One split (workgroup of 4 waves) of the unit (b, h); `splits` splits per
-// unit.
-template <typename T, int D, int GQ>
+// One split (workgroup of 4 waves, TPW tiles each) of the unit (b, h);
+// `splits` splits per unit.
+template <typename T, int D, int GQ, int TPW>
 __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int h, int b, int splits,
                                              DecodeLds<D, GQ>& lds) {
   using namespace dec_detail;
@@ -121,18 +123,18 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
   }
 
   // ---- locate this wave's tiles (scalar loads), then issue every K/V load ----
-  int ntok[kDecTilesPerWave];
-  int64_t tile_off[kDecTilesPerWave];
-  int jsel[kDecTilesPerWave];
+  int ntok[TPW];
+  int64_t tile_off[TPW];
+  int jsel[TPW];
   const int slot_end = min((split + 1) * a.pages_per_split, a.k);
 #pragma unroll
-  for (int i = 0; i < kDecTilesPerWave; ++i) {
+  for (int i = 0; i < TPW; ++i) {
     const int ti = wave_u + kDecWaves * i;
     const int slot = split * a.pages_per_split + ti / tiles_per_page;
     jsel[i] = slot < slot_end ? sel[slot] : -1;
   }
 #pragma unroll
-  for (int i = 0; i < kDecTilesPerWave; ++i) {
+  for (int i = 0; i < TPW; ++i) {
     const int ti = wave_u + kDecWaves * i;
     const int sub = ti % tiles_per_page;
     const int j = jsel[i];
@@ -153,11 +155,11 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
   // past the valid tokens reads the tile's first row) so that no load sits
   // inside a branch; K rows past ntok only reach S rows that are masked to
   // -inf, and V rows past ntok are zeroed below.
-  typename Q::Op ka[kDecTilesPerWave][Q::kSteps];
-  VRow<T> vr[kDecTilesPerWave][kColPasses][4];
+  typename Q::Op ka[TPW][Q::kSteps];
+  VRow<T> vr[TPW][kColPasses][4];
   const int cc = c_ok ? c : 0;
 #pragma unroll
-  for (int i = 0; i < kDecTilesPerWave; ++i) {
+  for (int i = 0; i < TPW; ++i) {
     const T* kt = kp + tile_off[i];
     const T* vt = vp + tile_off[i];
     const int krow = n < ntok[i] ? n : 0;
@@ -172,7 +174,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
       }
   }
 #pragma unroll
-  for (int i = 0; i < kDecTilesPerWave; ++i) {
+  for (int i = 0; i < TPW; ++i) {
     if (ntok[i] < kDecTile || !c_ok) {
 #pragma unroll
       for (int cp = 0; cp < kColPasses; ++cp)
@@ -193,7 +195,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
       for (int e = 0; e < 8; ++e) o[cp][g][e] = 0.f;
 
 #pragma unroll
-  for (int i = 0; i < kDecTilesPerWave; ++i) {
+  for (int i = 0; i < TPW; ++i) {
     if (ntok[i] == 0) continue;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

@@ -74,7 +74,11 @@ constexpr int i4_record_bytes(int d, int r, int P) {
 hipError_t launch_page_score(const ScoreArgs& a, int dtype, int D, int batch, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s);
 hipError_t launch_sparse_decode(const DecodeArgs& a, int dtype, int D, int batch, hipStream_t s);
-int decode_pages_per_split(int page_size);
+int decode_pages_per_split(int page_size, int tiles_per_wave);
+// tiles per wave for `units` (sequence, KV head) units of k pages
+int decode_tiles_per_wave(int64_t units, int k, int page_size, bool f32);
+// the most splits any launch uses (the workspace is sized for it)
+int decode_max_splits(int k, int page_size);
 // dtype: 0 bf16, 1 fp32 keys; i4: write quantized records (bf16 keys only)
 hipError_t launch_build(const BuildArgs& a, int dtype, int D, bool i4, hipStream_t s);
 // page scores from quantized records (bf16 q)

@@ -80,15 +80,22 @@ size_t score_ws_bytes(const locks_config_t* c, int32_t batch, int32_t max_pages)
   return ctl_bytes(c, batch) + align_up(scores) + align_up(sigma);
 }
 
-int decode_pages_per_split(const locks_config_t* c) { return locks::decode_pages_per_split(c->page_size); }
+// pages per split of a launch over `batch` sequences
+int decode_pages_per_split(const locks_config_t* c, int32_t batch) {
+  const int tpw = locks::decode_tiles_per_wave((int64_t)batch * c->num_kv_heads, c->budget_pages, c->page_size,
+                                                c->kv_dtype == LOCKS_F32);
+  return locks::decode_pages_per_split(c->page_size, tpw);
+}
 
-int decode_splits(const locks_config_t* c) {
-  const int pps = decode_pages_per_split(c);
+int decode_splits(const locks_config_t* c, int32_t batch) {
+  const int pps = decode_pages_per_split(c, batch);
   return (c->budget_pages + pps - 1) / pps;
 }
 
+// sized for the most splits any batch uses, so a workspace sized for one
+// batch serves every smaller batch
 size_t decode_ws_bytes(const locks_config_t* c, int32_t batch) {
-  const size_t rows = (size_t)batch * c->num_q_heads * decode_splits(c);
+  const size_t rows = (size_t)batch * c->num_q_heads * locks::decode_max_splits(c->budget_pages, c->page_size);
   return ctl_bytes(c, batch) + align_up(rows * c->head_dim * sizeof(float)) +
          align_up(rows * sizeof(float));
 }
@@ -134,7 +141,7 @@ locks::SelectArgs select_args(const locks_config_t* cfg, const float* head_score
 
 locks::DecodeArgs decode_args(const locks_config_t* cfg, const void* q, const void* k_pool, const void* v_pool,
                               int64_t num_blocks, const int32_t* block_table, const int32_t* seq_lens,
-                              const int32_t* selected, int32_t max_pages, void* out, float* lse,
+                              const int32_t* selected, int32_t batch, int32_t max_pages, void* out, float* lse,
                               int32_t* counters, float* part_o, float* part_lse) {
   locks::DecodeArgs a{};
   a.q = q;
@@ -154,8 +161,8 @@ locks::DecodeArgs decode_args(const locks_config_t* cfg, const void* q, const vo
   a.P = cfg->page_size;
   a.k = cfg->budget_pages;
   a.max_pages = max_pages;
-  a.pages_per_split = decode_pages_per_split(cfg);
-  a.splits = decode_splits(cfg);
+  a.pages_per_split = decode_pages_per_split(cfg, batch);
+  a.splits = decode_splits(cfg, batch);
   a.scale = cfg->softmax_scale;
   return a;
 }
@@ -284,10 +291,11 @@ int locks_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !selected || !out)
     return LOCKS_E_INVALID_ARG;
   if (!ws || ws_bytes < decode_ws_bytes(cfg, batch)) return LOCKS_E_WORKSPACE;
-  const size_t rows = (size_t)batch * cfg->num_q_heads * decode_splits(cfg);
+  // partial rows laid out for the most splits any batch uses (the workspace layout)
+  const size_t rows = (size_t)batch * cfg->num_q_heads * locks::decode_max_splits(cfg->budget_pages, cfg->page_size);
   uint8_t* region = static_cast<uint8_t*>(ws) + ctl_bytes(cfg, batch);
   locks::DecodeArgs a = decode_args(cfg, q, k_pool, v_pool, num_blocks, block_table, seq_lens, selected,
-                                    max_pages, out, lse, static_cast<int32_t*>(ws),
+                                    batch, max_pages, out, lse, static_cast<int32_t*>(ws),
                                     reinterpret_cast<float*>(region),
                                     reinterpret_cast<float*>(region + align_up(rows * cfg->head_dim * sizeof(float))));
   return hip_status(locks::launch_sparse_decode(a, cfg->kv_dtype, cfg->head_dim, batch, stream));

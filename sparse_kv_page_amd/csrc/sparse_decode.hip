@@ -4,7 +4,7 @@
 //
 // Split-K: a workgroup takes `pages_per_split` consecutive slots of one
 // (sequence, KV head)'s selected list, cut into 16-token tiles; its 4 waves
-// take the tiles in turn (kDecTilesPerWave each), with every K and V load of
+// take the tiles in turn (TPW each), with every K and V load of
 // a wave issued up front (non-temporal: the tiles are read once per step).
 // Per tile, for all G query heads of the group:
 //   S = K q^T on the matrix cores (16 tokens x 16 head columns, G used),
@@ -22,20 +22,52 @@
 
 namespace locks {
 
-// bf16 with G <= 4: 4 workgroups (16 waves) per CU, so the whole grid of the
-// common shapes is resident at once; G = 8 and fp32 need more registers.
-template <typename T, int D, int GQ>
-__global__ __launch_bounds__(256, (sizeof(T) == 2 && GQ <= 4) ? 4 : 2) void sparse_decode_kernel(DecodeArgs a) {
+// Two tiles per wave, bf16, G <= 4: 4 workgroups (16 waves) per CU, so the
+// whole grid of the common shapes is resident at once; four tiles per wave,
+// G = 8 and fp32 need more registers (2 workgroups per CU).
+template <typename T, int D, int GQ, int TPW>
+__global__ __launch_bounds__(256, (sizeof(T) == 2 && GQ <= 4 && TPW <= 2) ? 4 : 2) void sparse_decode_kernel(
+    DecodeArgs a) {
   __shared__ DecodeLds<D, GQ> lds;
-  decode_split<T, D, GQ>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x, lds);
+  decode_split<T, D, GQ, TPW>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x, lds);
 }
 
-int decode_pages_per_split(int page_size) { return kDecTilesPerWg * kDecTile / page_size; }
+int decode_pages_per_split(int page_size, int tiles_per_wave) {
+  return kDecWaves * tiles_per_wave * kDecTile / page_size;
+}
+
+// Four tiles per wave halve the splits (a shorter merge) while the grid
+// still holds at least 512 workgroups (two per CU); smaller grids and fp32
+// (whose four-tile kernel spills) keep two.
+int decode_tiles_per_wave(int64_t units, int k, int page_size, bool f32) {
+  if (f32) return kDecTilesPerWaveSmall;
+  const int pps = decode_pages_per_split(page_size, kDecTilesPerWaveLarge);
+  const int64_t wgs = units * ((k + pps - 1) / pps);
+  return wgs >= 512 ? kDecTilesPerWaveLarge : kDecTilesPerWaveSmall;
+}
+
+int decode_max_splits(int k, int page_size) {
+  const int pps = decode_pages_per_split(page_size, kDecTilesPerWaveSmall);
+  return (k + pps - 1) / pps;
+}
+
+namespace {
+template <typename T, int D, int G>
+void launch_tpw(const DecodeArgs& a, dim3 grid, hipStream_t stream, bool large) {
+  if constexpr (sizeof(T) == 2) {
+    if (large) {
+      hipLaunchKernelGGL((sparse_decode_kernel<T, D, G, kDecTilesPerWaveLarge>), grid, dim3(256), 0, stream, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((sparse_decode_kernel<T, D, G, kDecTilesPerWaveSmall>), grid, dim3(256), 0, stream, a);
+}
+}  // namespace
 
 hipError_t launch_sparse_decode(const DecodeArgs& a, int dtype, int D, int batch, hipStream_t stream) {
   dim3 grid(a.splits, a.Hkv, batch);
-#define LAUNCH(T, DD, GG) \
-  hipLaunchKernelGGL((sparse_decode_kernel<T, DD, GG>), grid, dim3(256), 0, stream, a)
+  const bool large = dtype == 0 && a.pages_per_split * a.P == kDecWaves * kDecTilesPerWaveLarge * kDecTile;
+#define LAUNCH(T, DD, GG) launch_tpw<T, DD, GG>(a, grid, stream, large)
 #define LAUNCH_G(T, DD)                  \
   switch (a.G) {                         \
     case 1: LAUNCH(T, DD, 1); break;     \
