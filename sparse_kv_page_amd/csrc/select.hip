@@ -28,12 +28,25 @@ namespace locks {
 
 constexpr int kSelLdsKeys = 16384;  // sigma keys kept in LDS up to this many pages
 
-// NT threads, NPT register pages per thread (0: loop over global memory)
-template <int NT, int NPT>
+// NT threads, NPT register pages per thread (0: loop over global memory), GQ
+// query heads per KV head
+template <int NT, int NPT, int GQ>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   __shared__ SelectLds<NT, kSelLdsKeys> lds;
-  select_unit<NT, NPT, kSelLdsKeys>(a, blockIdx.y, blockIdx.x, lds);
+  select_unit<NT, NPT, kSelLdsKeys, GQ>(a, blockIdx.y, blockIdx.x, lds);
 }
+
+namespace {
+template <int NT, int NPT>
+void launch_g(const SelectArgs& a, dim3 grid, hipStream_t stream) {
+  switch (a.G) {
+    case 1: hipLaunchKernelGGL((select_kernel<NT, NPT, 1>), grid, dim3(NT), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((select_kernel<NT, NPT, 2>), grid, dim3(NT), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((select_kernel<NT, NPT, 4>), grid, dim3(NT), 0, stream, a); break;
+    default: hipLaunchKernelGGL((select_kernel<NT, NPT, 8>), grid, dim3(NT), 0, stream, a); break;
+  }
+}
+}  // namespace
 
 // Up to 2048 pages, 512 threads with 4 pages each: the selection is a chain
 // of block-wide steps, and a smaller block shortens every barrier (measured
@@ -41,11 +54,11 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t stream) {
   dim3 grid(a.Hkv, batch);
   if (a.max_pages <= 512 * 4)
-    hipLaunchKernelGGL((select_kernel<512, 4>), grid, dim3(512), 0, stream, a);
+    launch_g<512, 4>(a, grid, stream);
   else if (a.max_pages <= 1024 * 8)
-    hipLaunchKernelGGL((select_kernel<1024, 8>), grid, dim3(1024), 0, stream, a);
+    launch_g<1024, 8>(a, grid, stream);
   else
-    hipLaunchKernelGGL((select_kernel<1024, 0>), grid, dim3(1024), 0, stream, a);
+    launch_g<1024, 0>(a, grid, stream);
   return hipGetLastError();
 }
 

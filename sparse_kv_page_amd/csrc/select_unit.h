@@ -88,11 +88,12 @@ struct alignas(16) SelectLds {
   int pick_s[3];
 };
 
-// Combine and selection of the unit (b, h) by a workgroup of NT threads.
-// NPT > 0 keeps pages tid, tid + NT, ... (NPT of them, max_pages <= NT * NPT)
-// in registers; NPT = 0 loops over global memory. KEYS: page keys kept in LDS
-// (longer contexts keep them in the sigma buffer).
-template <int NT, int NPT, int KEYS>
+// Combine and selection of the unit (b, h) by a workgroup of NT threads for
+// GQ query heads per KV head (a compile-time count: the per-head loops are
+// straight-line code). NPT > 0 keeps pages tid, tid + NT, ... (NPT of them,
+// max_pages <= NT * NPT) in registers; NPT = 0 loops over global memory.
+// KEYS: page keys kept in LDS (longer contexts keep them in the sigma buffer).
+template <int NT, int NPT, int KEYS, int GQ>
 __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, SelectLds<NT, KEYS>& L) {
   using namespace sel_detail;
   constexpr int kSelThreads = NT;
@@ -110,18 +111,19 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int P = a.P, G = a.G, k = a.k;
+  const int P = a.P, k = a.k;
+  constexpr int G = GQ;
   const float* srow = a.scores + ((int64_t)b * a.Hkv * G + (int64_t)h * G) * a.max_pages;
   // the register path loads its scores before the length is known (pages up
   // to max_pages are addressable), so both loads are in flight together
   constexpr int kRegs = NPT > 0 ? NPT : 1;
-  float sc[kRegs][8];
+  float sc[kRegs][GQ];
   if constexpr (NPT > 0) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int j = tid + kSelThreads * i;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) sc[i][g] = (g < G && j < a.max_pages) ? srow[(int64_t)g * a.max_pages + j] : 0.f;
+      for (int g = 0; g < GQ; ++g) sc[i][g] = (g < G && j < a.max_pages) ? srow[(int64_t)g * a.max_pages + j] : 0.f;
     }
   }
   const int T = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.max_pages, P));
@@ -144,15 +146,15 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   // ---- per-head normaliser log Z_g: block max, then block sum of
   // 2^(s - max); each reduction is DPP inside the waves, one LDS exchange and
   // one barrier, with every thread combining the wave results itself ----
-  float mx[8];
+  float mx[GQ];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) mx[g] = -INFINITY;
+  for (int g = 0; g < GQ; ++g) mx[g] = -INFINITY;
   if constexpr (NPT > 0) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int j = tid + kSelThreads * i;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
+      for (int g = 0; g < GQ; ++g) {
         if (!(g < G && j < Jc)) sc[i][g] = -INFINITY;
         mx[g] = fmaxf(mx[g], sc[i][g]);
       }
@@ -160,11 +162,11 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   } else {
     for (int j = tid; j < Jc; j += kSelThreads)
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
+      for (int g = 0; g < GQ; ++g)
         if (g < G) mx[g] = fmaxf(mx[g], srow[(int64_t)g * a.max_pages + j]);
   }
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
+  for (int g = 0; g < GQ; ++g) {
     if (g < G) {
       const float r = wave_max(mx[g]);
       if (lane == 0) red_m[wave][g] = r;
@@ -172,7 +174,7 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   }
   __syncthreads();
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
+  for (int g = 0; g < GQ; ++g) {
     if (g < G) {
       float r = red_m[0][g];
 #pragma unroll
@@ -180,32 +182,32 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
       mx[g] = r;
     }
   }
-  float sm[8];
+  float sm[GQ];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) sm[g] = 0.f;
+  for (int g = 0; g < GQ; ++g) sm[g] = 0.f;
   if constexpr (NPT > 0) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i)
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
+      for (int g = 0; g < GQ; ++g)
         if (g < G && mx[g] > -INFINITY) sm[g] += exp2_fast((sc[i][g] - mx[g]) * kLog2e);
   } else {
     for (int j = tid; j < Jc; j += kSelThreads)
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
+      for (int g = 0; g < GQ; ++g)
         if (g < G && mx[g] > -INFINITY) sm[g] += exp2_fast((srow[(int64_t)g * a.max_pages + j] - mx[g]) * kLog2e);
   }
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
+  for (int g = 0; g < GQ; ++g) {
     if (g < G) {
       const float r = wave_sum(sm[g]);
       if (lane == 0) red_s[wave][g] = r;
     }
   }
   __syncthreads();
-  float lz[8];
+  float lz[GQ];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
+  for (int g = 0; g < GQ; ++g) {
     lz[g] = -INFINITY;
     if (g < G && mx[g] > -INFINITY) {
       float r = red_s[0][g];
@@ -219,10 +221,10 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   const float log2G = log2_fast((float)G);
   uint32_t kmax = 0u, kmin = 0xffffffffu;
   auto sigma_key = [&](int j, const float* sv) {
-    float tg[8];
+    float tg[GQ];
     float m = -INFINITY;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = 0; g < GQ; ++g) {
       tg[g] = -INFINITY;
       if (g < G && lz[g] > -INFINITY) {
         tg[g] = (sv[g] - lz[g]) * kLog2e;
@@ -231,7 +233,7 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     }
     float s = 0.f;
 #pragma unroll
-    for (int g = 0; g < 8; ++g)
+    for (int g = 0; g < GQ; ++g)
       if (g < G && m > -INFINITY) s += exp2_fast(tg[g] - m);
     const float sigma = m > -INFINITY ? (m + log2_fast(s) - log2G) * kLn2 : -INFINITY;
     const uint32_t key = float_key(sigma);
@@ -254,9 +256,9 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     }
   } else {
     for (int j = tid; j < Jc; j += kSelThreads) {
-      float sv[8];
+      float sv[GQ];
 #pragma unroll
-      for (int g = 0; g < 8; ++g) sv[g] = g < G ? srow[(int64_t)g * a.max_pages + j] : 0.f;
+      for (int g = 0; g < GQ; ++g) sv[g] = g < G ? srow[(int64_t)g * a.max_pages + j] : 0.f;
       sigma_key(j, sv);
     }
   }
