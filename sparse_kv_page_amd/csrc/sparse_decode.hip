@@ -3,9 +3,10 @@
 // uses the original K/V.
 //
 // Split-K: a workgroup takes `pages_per_split` consecutive slots of one
-// (sequence, KV head)'s selected list, cut into 16-token tiles; its 4 waves
-// take the tiles in turn (TPW each), with every K and V load of
-// a wave issued up front (non-temporal: the tiles are read once per step).
+// (sequence, KV head)'s selected list, cut into 16-token tiles; its 8 waves
+// take the tiles in turn (TPW each), a wave loading its next tile while it
+// computes the current one (non-temporal loads: the tiles are read once per
+// step).
 // Per tile, for all G query heads of the group:
 //   S = K q^T on the matrix cores (16 tokens x 16 head columns, G used),
 //   online softmax in base 2 (running max / sum per head),
@@ -22,11 +23,11 @@
 
 namespace locks {
 
-// Two tiles per wave, bf16, G <= 4: 4 workgroups (16 waves) per CU, so the
-// whole grid of the common shapes is resident at once; four tiles per wave,
-// G = 8 and fp32 need more registers (2 workgroups per CU).
+// Register budget: two tiles per wave with bf16 and G <= 4 fits 4 waves per
+// SIMD; four tiles per wave, G = 8 and fp32 take more registers. An 8-wave
+// workgroup per CU holds every workgroup of the headline-like grids.
 template <typename T, int D, int GQ, int TPW>
-__global__ __launch_bounds__(256, (sizeof(T) == 2 && GQ <= 4 && TPW <= 2) ? 4 : 2) void sparse_decode_kernel(
+__global__ __launch_bounds__(kDecThreads, (sizeof(T) == 2 && GQ <= 4 && TPW <= 2) ? 4 : 2) void sparse_decode_kernel(
     DecodeArgs a) {
   __shared__ DecodeLds<D, GQ> lds;
   decode_split<T, D, GQ, TPW>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x, lds);
@@ -37,13 +38,13 @@ int decode_pages_per_split(int page_size, int tiles_per_wave) {
 }
 
 // Four tiles per wave halve the splits (a shorter merge) while the grid
-// still holds at least 512 workgroups (two per CU); smaller grids and fp32
+// still holds at least 256 workgroups (one per CU); smaller grids and fp32
 // (whose four-tile kernel spills) keep two.
 int decode_tiles_per_wave(int64_t units, int k, int page_size, bool f32) {
   if (f32) return kDecTilesPerWaveSmall;
   const int pps = decode_pages_per_split(page_size, kDecTilesPerWaveLarge);
   const int64_t wgs = units * ((k + pps - 1) / pps);
-  return wgs >= 512 ? kDecTilesPerWaveLarge : kDecTilesPerWaveSmall;
+  return wgs >= 256 ? kDecTilesPerWaveLarge : kDecTilesPerWaveSmall;
 }
 
 int decode_max_splits(int k, int page_size) {
@@ -56,11 +57,11 @@ template <typename T, int D, int G>
 void launch_tpw(const DecodeArgs& a, dim3 grid, hipStream_t stream, bool large) {
   if constexpr (sizeof(T) == 2) {
     if (large) {
-      hipLaunchKernelGGL((sparse_decode_kernel<T, D, G, kDecTilesPerWaveLarge>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((sparse_decode_kernel<T, D, G, kDecTilesPerWaveLarge>), grid, dim3(kDecThreads), 0, stream, a);
       return;
     }
   }
-  hipLaunchKernelGGL((sparse_decode_kernel<T, D, G, kDecTilesPerWaveSmall>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((sparse_decode_kernel<T, D, G, kDecTilesPerWaveSmall>), grid, dim3(kDecThreads), 0, stream, a);
 }
 }  // namespace
 
