@@ -284,13 +284,13 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
     for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, mm[w][g]);
     float L = 0.f, O = 0.f;
     if (M > -INFINITY) {
+      // branch-free, so the LDS reads of all waves go out together: a wave
+      // without tokens has mm = -inf (weight exp2(-inf) = 0) and o = 0
 #pragma unroll
       for (int w = 0; w < kDecWaves; ++w) {
-        if (mm[w][g] > -INFINITY) {
-          const float cw = exp2_fast(mm[w][g] - M);
-          L += cw * ml[w][g];
-          O += cw * (mo[w][0][g][e] + mo[w][1][g][e] + mo[w][2][g][e] + mo[w][3][g][e]);
-        }
+        const float cw = exp2_fast(mm[w][g] - M);
+        L = fmaf(cw, ml[w][g], L);
+        O = fmaf(cw, (mo[w][0][g][e] + mo[w][1][g][e]) + (mo[w][2][g][e] + mo[w][3][g][e]), O);
       }
     }
     __hip_atomic_store(&part_o[x], L > 0.f ? O / L : 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
