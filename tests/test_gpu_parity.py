@@ -86,6 +86,33 @@ def test_select_parity(wl):
     assert ndiff <= 2 * len(refs)
 
 
+@pytest.mark.parametrize("G,lens", [(4, (64 * 10000 + 5, 64 * 6000)), (8, (64 * 3000 + 17, 64 * 2100)),
+                                     (1, (64 * 9000,)), (4, (64 * 5000 + 1, 64 * 40))],
+                         ids=["g4_10000_pages", "g8_3000_pages", "g1_9000_pages", "g4_5000_pages"])
+def test_select_long_context_paths(G, lens):
+    """The selector's long-context kernels (1024 threads with 8 register pages
+    up to 8192 pages, 1024 threads re-reading the scores beyond that) for
+    G in {1, 4, 8}, on seeded random page scores, against the oracle."""
+    wl = synth.Workload("sel_long", len(lens), 2, G, 128, 64, lens, 4, 32, "bf16", "bf16")
+    cfg = _cfg(wl)
+    gen = torch.Generator().manual_seed(31 + G)
+    hs = (torch.randn((wl.batch, wl.num_q_heads, wl.max_pages), generator=gen) * 2.5).float()
+    g = {"seq_lens": torch.tensor(list(lens), dtype=torch.int32, device=gg.DEV)}
+    sel, sig = gg.gpu_select(wl, cfg, g, hs.to(gg.DEV))
+    torch.cuda.synchronize()
+    sel, sig = sel.cpu(), sig.cpu()
+    ndiff = 0
+    for b in range(wl.batch):
+        _, J, Jc = gg.lens(wl, b)
+        for h in range(wl.num_kv_heads):
+            s32 = hs[b, h * G:(h + 1) * G, :Jc].double().numpy()
+            sel_o, sigma_o = gg.oracle_unit_select(wl, b, s32)
+            ndiff += gg.check_selection(wl, b, sel[b, h].tolist(), sel_o.tolist(), sigma_o)
+            if sigma_o is not None:
+                assert gg.mixed_violation(gg.f64(sig[b, h, :Jc]), sigma_o) <= 1.0
+    assert ndiff <= 2 * wl.batch * wl.num_kv_heads
+
+
 def test_select_ties_go_to_lower_page():
     """Equal keys: the lower page id wins (radix select resolves full 64-bit keys)."""
     wl = E2E.with_(batch=1, seq_lens=(64 * 40,), budget_pages=6)
