@@ -16,6 +16,7 @@ struct ScoreArgs {
   int64_t rec_elems;          // elements per record
   int Hkv, G, P, r, max_pages;
   int ppw;                    // pages per wave, set by the launcher (<= 128 LDS-staged, else <= 64)
+  int head_major;             // LDS-staged scorer: a workgroup's waves take adjacent KV heads
   float scale;
 };
 

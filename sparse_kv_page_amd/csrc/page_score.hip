@@ -178,11 +178,16 @@ __global__ __launch_bounds__(256) void page_score_kernel(ScoreArgs a) {
 
 // LDS-staged variant (bf16 records, rank 1/2/4/8, G * P >= 64): see score_lds.h.
 template <int D, int RT, int GQ, int P>
-__global__ __launch_bounds__(256, 2) void page_score_lds_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreLdsWaves * 64, 2) void page_score_lds_kernel(ScoreArgs a) {
   __shared__ ScoreLds<D, RT, GQ, P> lds;
   const int wave = threadIdx.x >> 6;
-  const int p0 = __builtin_amdgcn_readfirstlane((blockIdx.x * kScoreWaves + wave) * a.ppw);
-  score_wave_lds<D, RT, GQ, P>(a, blockIdx.z, blockIdx.y, p0, a.ppw, lds);
+  if (a.head_major) {  // grid (page ranges, H_kv / waves, batch): adjacent heads, same pages
+    const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * kScoreLdsWaves + wave);
+    score_wave_lds<D, RT, GQ, P>(a, blockIdx.z, h, __builtin_amdgcn_readfirstlane(blockIdx.x * a.ppw), a.ppw, lds);
+  } else {  // grid (page ranges / waves, H_kv, batch): consecutive page ranges of one head
+    const int p0 = __builtin_amdgcn_readfirstlane((blockIdx.x * kScoreLdsWaves + wave) * a.ppw);
+    score_wave_lds<D, RT, GQ, P>(a, blockIdx.z, blockIdx.y, p0, a.ppw, lds);
+  }
 }
 
 namespace {
@@ -201,11 +206,11 @@ int resident_waves(const void* fn, int threads) {
 }
 
 template <typename KernelTag>
-int cached_waves(const void* fn) {
+int cached_waves(const void* fn, int threads = 256) {
   static std::atomic<int> cached{0};
   int waves = cached.load(std::memory_order_relaxed);
   if (waves == 0) {
-    waves = resident_waves(fn, 256);
+    waves = resident_waves(fn, threads);
     cached.store(waves, std::memory_order_relaxed);
   }
   return waves;
@@ -228,8 +233,16 @@ struct LdsTag {};
 template <int D, int RT, int GQ, int P>
 hipError_t launch_lds(ScoreArgs a, int batch, hipStream_t stream) {
   const void* fn = reinterpret_cast<const void*>(&page_score_lds_kernel<D, RT, GQ, P>);
-  const dim3 grid = score_grid(a, batch, cached_waves<LdsTag<D, RT, GQ, P>>(fn), kScoreMaxPpw);
-  hipLaunchKernelGGL((page_score_lds_kernel<D, RT, GQ, P>), grid, dim3(256), 0, stream, a);
+  constexpr int kThreads = kScoreLdsWaves * 64;
+  dim3 grid = score_grid(a, batch, cached_waves<LdsTag<D, RT, GQ, P>>(fn, kThreads), kScoreMaxPpw);
+  a.head_major = a.Hkv % kScoreLdsWaves == 0;
+  if (a.head_major) {
+    grid = dim3((a.max_pages + a.ppw - 1) / a.ppw, a.Hkv / kScoreLdsWaves, batch);
+  } else {
+    const int waves_per_unit = (a.max_pages + a.ppw - 1) / a.ppw;
+    grid = dim3((waves_per_unit + kScoreLdsWaves - 1) / kScoreLdsWaves, a.Hkv, batch);
+  }
+  hipLaunchKernelGGL((page_score_lds_kernel<D, RT, GQ, P>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

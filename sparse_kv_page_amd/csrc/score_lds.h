@@ -11,6 +11,11 @@
 namespace locks {
 
 constexpr int kScoreWaves = 4;
+// waves of an LDS-staged scorer workgroup; with H_kv a multiple of it they
+// take adjacent KV heads of the same pages, whose records are adjacent in
+// the pool (a block's heads are stored together), so a workgroup's record
+// loads cover one contiguous run per page
+constexpr int kScoreLdsWaves = 4;
 constexpr int kScoreMaxPpw = 128;  // pages per wave of the LDS-staged scorer (block ids in two VGPRs)
 constexpr int kScorePagesPerIter = 4;  // at most this many pages scored together (interleaved chains)
 
@@ -139,9 +144,9 @@ struct LdsRec {
   static constexpr int kTail = kChunks - (kInstr - 1) * 64; // lanes of the last one
   static constexpr int kRowChunks = kE * D / 16;            // 16-byte chunks per row
   static constexpr int kHeadChunks = kHeadBytes / 16;
-  static constexpr int kBudget = 80 * 1024;                 // LDS bytes per workgroup
-  static constexpr int kExtra = 4 * (kScorePagesPerIter * G * 16 + kScoreMaxPpw * G) * 4;  // w and score staging of 4 waves
-  static constexpr int kNs0 = (kBudget - kExtra) / (4 * kBytes);
+  static constexpr int kBudget = 20 * 1024 * kScoreLdsWaves;  // LDS bytes per workgroup (2 per CU at 4 waves)
+  static constexpr int kExtra = kScoreLdsWaves * (kScorePagesPerIter * G * 16 + kScoreMaxPpw * G) * 4;  // w and score staging
+  static constexpr int kNs0 = (kBudget - kExtra) / (kScoreLdsWaves * kBytes);
   static constexpr int kNs = kNs0 < 2 ? 2 : (kNs0 > 8 ? 8 : kNs0);
   static_assert(kBytes % 16 == 0, "records are whole 16-byte chunks");
   // LDS chunk x holds global chunk swz(x) (an involution inside each row)
@@ -155,9 +160,9 @@ struct LdsRec {
 template <int D, int RT, int GQ, int P>
 struct alignas(16) ScoreLds {
   using R = LdsRec<D, RT, P, GQ>;
-  uint8_t slots[kScoreWaves][R::kNs][R::kBytes];
-  float wbuf[kScoreWaves][kScorePagesPerIter][GQ][16];
-  float sbuf[kScoreWaves][kScoreMaxPpw][GQ];
+  uint8_t slots[kScoreLdsWaves][R::kNs][R::kBytes];
+  float wbuf[kScoreLdsWaves][kScorePagesPerIter][GQ][16];
+  float sbuf[kScoreLdsWaves][kScoreMaxPpw][GQ];
 };
 
 // One wave scores pages [p0, p0 + min(ppw, Jc - p0)) of the unit (b, h) for
