@@ -144,7 +144,10 @@ struct LdsRec {
   static constexpr int kTail = kChunks - (kInstr - 1) * 64; // lanes of the last one
   static constexpr int kRowChunks = kE * D / 16;            // 16-byte chunks per row
   static constexpr int kHeadChunks = kHeadBytes / 16;
-  static constexpr int kBudget = 20 * 1024 * kScoreLdsWaves;  // LDS bytes per workgroup (2 per CU at 4 waves)
+  // LDS bytes per workgroup (2 per CU at 4 waves): 4 ring slots at the
+  // headline shape, measured faster than 5 (fewer record loads in flight)
+  // and than 3
+  static constexpr int kBudget = 17 * 1024 * kScoreLdsWaves;
   static constexpr int kExtra = kScoreLdsWaves * (kScorePagesPerIter * G * 16 + kScoreMaxPpw * G) * 4;  // w and score staging
   static constexpr int kNs0 = (kBudget - kExtra) / (kScoreLdsWaves * kBytes);
   static constexpr int kNs = kNs0 < 2 ? 2 : (kNs0 > 8 ? 8 : kNs0);
