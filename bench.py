@@ -435,8 +435,8 @@ def algorithmic_bytes(wl, rec_bytes):
 
 PROFILE_CMDS = {
     "stats": ("export TMPDIR=/tmp && cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv \\\n"
-              "    -d $R/gpurun_out/prof_stats -o locks -- python3 -u $R/bench.py --steps 20 --warmup 5 "
-              "--no-cpu-baseline{flags}"),
+              "    -d $R/gpurun_out/prof_stats -o locks -- python3 -u $R/bench.py --no-cpu-baseline{flags}\n"
+              "    (bench.py's default steps and warm-up, so the averages match its timed windows)"),
     "fetch": ("export TMPDIR=/tmp && cd /tmp && timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE \\\n"
               "    --kernel-include-regex 'locks::|copyBuffer' --output-format csv -d $R/gpurun_out/prof_fetch "
               "-o fetch \\\n    -- python3 -u $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
