@@ -48,7 +48,7 @@ def parse():
                     help="after the timed steps, run 3 plain device copies of MIB MiB "
                          "(reference dispatches for scaling memory counters)")
     ap.add_argument("--full-step", action="store_true",
-                    help="instead of the headline step: the 32-layer decode step of a 16 x 64K batch "
+                    help="instead of the 128K batch-8 layer step: the 32-layer decode step of a 16 x 64K batch "
                          "with the builds of completing pages interleaved (its own JSON line)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: turn the rocprofv3 outputs of the commands in profiles/*.md into "
@@ -435,14 +435,14 @@ def algorithmic_bytes(wl, rec_bytes):
 
 PROFILE_CMDS = {
     "stats": ("export TMPDIR=/tmp && cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv \\\n"
-              "    -d $R/gpurun_out/prof_stats -o locks -- python3 -u $R/bench.py --no-cpu-baseline{flags}\n"
+              "    -d $OUT/prof_stats -o locks -- python3 -u $R/bench.py --no-cpu-baseline{flags}\n"
               "    (bench.py's default steps and warm-up, so the averages match its timed windows)"),
     "fetch": ("export TMPDIR=/tmp && cd /tmp && timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE \\\n"
-              "    --kernel-include-regex 'locks::|copyBuffer' --output-format csv -d $R/gpurun_out/prof_fetch "
+              "    --kernel-include-regex 'locks::|copyBuffer' --output-format csv -d $OUT/prof_fetch "
               "-o fetch \\\n    -- python3 -u $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
               "--copy-calibration 256{flags}"),
-    "summarize": ("python bench.py{flags} --summarize-profiles gpurun_out/prof_stats gpurun_out/prof_fetch "
-                  "gpurun_out/prof_write"),
+    "summarize": ("python bench.py{flags} --summarize-profiles $OUT/prof_stats $OUT/prof_fetch "
+                  "$OUT/prof_write"),
 }
 
 KERNEL_PATTERNS = (("page_score", ("page_score_lds_kernel", "page_score_kernel", "page_score_i4_kernel")),
@@ -556,7 +556,7 @@ def summarize_profiles(wl, flags, stats_dir, fetch_dir, write_dir):
              f"{wl.kv_dtype} K/V and {wl.summary_dtype} summaries")
     with open(os.path.join(here, "profiles", f"decode_step_kernels_{workload}.md"), "w") as f:
         f.write(f"# Decode-step kernels, {workload}\n\nWorkload: {shape}; MI355X (gfx950), one GPU, "
-                f"ROCm 7.2.\n\nCommand (repository root on the GPU box = `R`):\n\n    "
+                f"ROCm 7.2.\n\nCommand (repository root = `R`, results directory = `OUT`):\n\n    "
                 + PROFILE_CMDS["stats"].format(flags=flags).replace("\n", "\n    ") +
                 "\n\nThen, without a GPU:\n\n    " + PROFILE_CMDS["summarize"].format(flags=flags) +
                 "\n\n| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|\n" +
@@ -566,7 +566,7 @@ def summarize_profiles(wl, flags, stats_dir, fetch_dir, write_dir):
                 f"decode_step_kernels_{workload}.md. Two counter passes, one counter each, followed by "
                 f"three plain 256 MiB device copies used as the calibration:\n\n    "
                 + PROFILE_CMDS["fetch"].format(flags=flags).replace("\n", "\n    ") +
-                "\n    (the same with --pmc WRITE_SIZE, -d $R/gpurun_out/prof_write -o write)\n\n"
+                "\n    (the same with --pmc WRITE_SIZE, -d $OUT/prof_write -o write)\n\n"
                 f"Calibration: a 256 MiB copy reads FETCH_SIZE = {fetch_copy:.1f} KiB and WRITE_SIZE = "
                 f"{write_copy:.1f} KiB, so FETCH_SIZE is scaled by {fs:.6f} and WRITE_SIZE by {wsc:.6f}.\n\n"
                 "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled traffic B/launch | algorithmic B/launch "

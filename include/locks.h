@@ -71,7 +71,7 @@ extern "C" {
 enum {
   LOCKS_OK = 0,
   LOCKS_E_INVALID_ARG = -1,  /* null pointer, negative size, k < 2, bad scale ... */
-  LOCKS_E_UNSUPPORTED = -2,  /* a shape or dtype this build has no kernel for   */
+  LOCKS_E_UNSUPPORTED = -2,  /* a shape or dtype this library has no kernel for */
   LOCKS_E_WORKSPACE = -3,    /* workspace pointer NULL or smaller than required */
   LOCKS_E_HIP = -4           /* the HIP runtime reported a launch error          */
 };

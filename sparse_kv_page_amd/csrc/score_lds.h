@@ -1,6 +1,6 @@
-// Device code of the page scorer shared by the scoring kernel and the fused
-// decode-step kernel: MFMA operand helpers, direct global->LDS record loads
-// and the LDS-staged per-wave scoring of a run of pages, [Locks] §4 Eq. (2).
+// Device code of the page scorer: MFMA operand helpers, direct global->LDS
+// record loads and the LDS-staged per-wave scoring of a run of pages,
+// [Locks] §4 Eq. (2).
 #pragma once
 
 #include "common.h"
@@ -145,7 +145,7 @@ struct LdsRec {
   static constexpr int kRowChunks = kE * D / 16;            // 16-byte chunks per row
   static constexpr int kHeadChunks = kHeadBytes / 16;
   // LDS bytes per workgroup (2 per CU at 4 waves): 4 ring slots at the
-  // headline shape, measured faster than 5 (fewer record loads in flight)
+  // 128K-context batch-8 shape, measured faster than 5 (fewer record loads in flight)
   // and than 3
   static constexpr int kBudget = 17 * 1024 * kScoreLdsWaves;
   static constexpr int kExtra = kScoreLdsWaves * (kScorePagesPerIter * G * 16 + kScoreMaxPpw * G) * 4;  // w and score staging
@@ -255,7 +255,7 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
   // Several pages per iteration: their dependent chains (LDS reads -> MFMA ->
   // transpose through LDS -> logits -> DPP reductions) interleave, which hides
   // the chain latency the two resident waves per SIMD cannot (4 pages measured
-  // faster than 2 or 3 at the headline shape).
+  // faster than 2 or 3 at 128K context, batch 8).
   auto score_pages = [&](auto npg_tag, int t, int s0) {
     constexpr int NPG = decltype(npg_tag)::value;
     const uint8_t* rec[NPG];

@@ -25,7 +25,7 @@ namespace locks {
 
 // Register budget: two tiles per wave with bf16 and G <= 4 fits 4 waves per
 // SIMD; four tiles per wave, G = 8 and fp32 take more registers. An 8-wave
-// workgroup per CU holds every workgroup of the headline-like grids.
+// workgroup per CU holds every workgroup of grids like 128K context at batch 8.
 template <typename T, int D, int GQ, int TPW>
 __global__ __launch_bounds__(kDecThreads, (sizeof(T) == 2 && GQ <= 4 && TPW <= 2) ? 4 : 2) void sparse_decode_kernel(
     DecodeArgs a) {

@@ -84,10 +84,10 @@ WORKLOADS = {
     # Llama-3.1-8B-shaped layer at 32K, batch 1
     "llama8b_32k": Workload("llama8b_32k", 1, 8, 4, 128, 64, _uniform(1, 32768), 4, 32,
                             "bf16", "bf16", centroid_std=0.5, n_needles=8),
-    # headline: 128K, batch 8, AR(1) centroids
+    # 128K context, batch 8, AR(1) centroids
     "llama8b_128k_b8": Workload("llama8b_128k_b8", 8, 8, 4, 128, 64, _uniform(8, 131072), 8, 32,
                                 "bf16", "bf16", centroid_std=0.5, ar_rho=0.99, n_needles=16),
-    # the headline shape with the pages' default 16-token pages (the same
+    # the 128K-context batch-8 shape with the pages' default 16-token pages (the same
     # 2048-token budget is k = 128 pages; rank swept by the caller)
     "llama8b_128k_b8_p16": Workload("llama8b_128k_b8_p16", 8, 8, 4, 128, 16, _uniform(8, 131072), 8, 128,
                                     "bf16", "bf16", centroid_std=0.5, ar_rho=0.99, n_needles=16),

@@ -194,7 +194,7 @@ def test_null_pointers_and_sizes():
 def test_workspace_checks():
     cfg = _cfg()
     need = L.locks_workspace_size(cfg, 8, 2048)
-    # scores (8*32*2048) + sigma (8*8*2048) floats for the headline shape
+    # scores (8*32*2048) + sigma (8*8*2048) floats for 128K context at batch 8
     assert need >= 4 * (8 * 32 * 2048 + 8 * 8 * 2048)
     fake = 1 << 20
     for ws, nbytes in ((None, need), (fake, 16)):

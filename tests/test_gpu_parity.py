@@ -427,9 +427,9 @@ def test_deterministic_repeats():
 
 
 # --------------------------------------------------------------------------
-# headline shape (128K context, batch 8, r = 8): sampled parity at full size
+# 128K context, batch 8, r = 8: sampled parity at full size
 # --------------------------------------------------------------------------
-def test_headline_sampled():
+def test_128k_b8_sampled():
     wl = W["llama8b_128k_b8"]
     cfg = _cfg(wl)
     d = synth.generate(wl, 0, gg.DEV)
@@ -552,7 +552,7 @@ def test_stress_512k_sampled(rank):
 
 
 # --------------------------------------------------------------------------
-# the headline shape with 16-token pages (k = 128 pages), r in {1, 2, 4, 8}:
+# 128K context, batch 8 with 16-token pages (k = 128 pages), r in {1, 2, 4, 8}:
 # the whole step on GPU-built summaries, sampled units against the oracle
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("rank", [1, 2, 4, 8])
