@@ -111,10 +111,11 @@ size_t locks_summary_record_bytes(const locks_config_t* cfg);
  * pages (one buffer of this size serves all three, in any interleaving).
  * Writes *bytes; returns a status.
  * The workspace must be zero-filled once before its first use: its first
- * bytes hold control words (per-(sequence, KV head) arrival counters and
- * ready flags, work tickets) that every call returns to zero and that no
- * call uses as scratch; the rest is scratch. Calls that share a workspace
- * must not overlap in time (same stream, or synchronised). */
+ * bytes hold control words (per-(sequence, KV head) arrival counters) that
+ * every call returns to zero and that no call uses as scratch; each call's
+ * scratch ends at the end of the buffer. A workspace sized for a batch also
+ * serves calls with fewer sequences of at most as many pages. Calls that share
+ * a workspace must not overlap in time (same stream, or synchronised). */
 int locks_workspace_size(const locks_config_t* cfg, int32_t batch, int32_t max_pages,
                          size_t* bytes);
 

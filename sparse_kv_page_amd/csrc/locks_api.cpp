@@ -62,16 +62,27 @@ int64_t rec_bytes(const locks_config_t* c) {
 }
 
 // Workspace layout, shared by every entry point that takes a workspace:
-//   control region: the decode arrival counters, one int32 per (sequence,
-//     KV head); zero between calls, never written as scratch
-//   data region (scratch, overwritten by every call):
+//   control words at the front: the decode arrival counters, one int32 per
+//     (sequence, KV head), then as many scorer arrival counters (the scorer
+//     that also selects); zero between calls, never written as scratch
+//   scratch at the back (overwritten by every call), ending at the end of the
+//     buffer:
 //     score/select: head scores, page keys
 //     decode:       split partials
 //     decode step:  the two above in turn
-// Because the control words sit in front of every data region, calls of
-// different entry points may share one workspace.
+// Control words sit in front of every scratch region, and a call with fewer
+// sequences uses a prefix of the control words of a call with more and a
+// shorter scratch ending at the same place, so calls of different entry points
+// and batch sizes may share one workspace sized for the largest of them.
 size_t ctl_bytes(const locks_config_t* c, int32_t batch) {
-  return align_up((size_t)batch * c->num_kv_heads * sizeof(int32_t));
+  return align_up(2 * (size_t)batch * c->num_kv_heads * sizeof(int32_t));
+}
+
+// first scratch byte of a call needing `scratch` bytes: as late as the buffer
+// allows, 256-byte aligned (at or past the control words, since ws_bytes >=
+// control + scratch and the control region is a multiple of 256 bytes)
+uint8_t* scratch_base(void* ws, size_t ws_bytes, size_t scratch) {
+  return static_cast<uint8_t*>(ws) + (ws_bytes - scratch) / kAlign * kAlign;
 }
 
 size_t score_ws_bytes(const locks_config_t* c, int32_t batch, int32_t max_pages) {
@@ -266,10 +277,20 @@ int locks_score_select(const locks_config_t* cfg, const void* q, const void* sum
   if (num_blocks == 0) return LOCKS_E_INVALID_ARG;  // an empty pool cannot be read
   if (!q || !summary_pool || !block_table || !seq_lens || !selected) return LOCKS_E_INVALID_ARG;
   if (!ws || ws_bytes < score_ws_bytes(cfg, batch, max_pages)) return LOCKS_E_WORKSPACE;
-  uint8_t* region = static_cast<uint8_t*>(ws) + ctl_bytes(cfg, batch);
+  uint8_t* region = scratch_base(ws, ws_bytes, score_ws_bytes(cfg, batch, max_pages) - ctl_bytes(cfg, batch));
   float* scores = reinterpret_cast<float*>(region);
   float* sigma = reinterpret_cast<float*>(region +
                                           align_up((size_t)batch * cfg->num_q_heads * max_pages * sizeof(float)));
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  if (cfg->summary_dtype != LOCKS_I4 &&
+      locks::page_score_selects(cfg->kv_dtype, cfg->head_dim, cfg->rank, G, cfg->page_size, max_pages)) {
+    // one launch: the scorer's last workgroup of each unit selects its pages
+    locks::ScoreArgs a = score_args(cfg, q, summary_pool, num_blocks, block_table, seq_lens, max_pages, scores);
+    a.arrive = static_cast<int32_t*>(ws) + (size_t)batch * cfg->num_kv_heads;
+    a.selected = selected;
+    a.k = cfg->budget_pages;
+    return hip_status(locks::launch_page_score(a, cfg->kv_dtype, cfg->head_dim, batch, stream));
+  }
   st = locks_page_score(cfg, q, summary_pool, num_blocks, block_table, seq_lens, batch, max_pages,
                         scores, stream);
   if (st != LOCKS_OK) return st;
@@ -293,7 +314,7 @@ int locks_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_
   if (!ws || ws_bytes < decode_ws_bytes(cfg, batch)) return LOCKS_E_WORKSPACE;
   // partial rows laid out for the most splits any batch uses (the workspace layout)
   const size_t rows = (size_t)batch * cfg->num_q_heads * locks::decode_max_splits(cfg->budget_pages, cfg->page_size);
-  uint8_t* region = static_cast<uint8_t*>(ws) + ctl_bytes(cfg, batch);
+  uint8_t* region = scratch_base(ws, ws_bytes, decode_ws_bytes(cfg, batch) - ctl_bytes(cfg, batch));
   locks::DecodeArgs a = decode_args(cfg, q, k_pool, v_pool, num_blocks, block_table, seq_lens, selected,
                                     batch, max_pages, out, lse, static_cast<int32_t*>(ws),
                                     reinterpret_cast<float*>(region),

@@ -130,6 +130,71 @@ def test_select_ties_go_to_lower_page():
     assert sel2[0, 0].tolist() == [0, 1, 2, 3, 4, 39]
 
 
+def _record_pool(wl, cfg, g, page_mu_weight):
+    """bf16 summary pool whose record of logical page j has V = 0, C = 0 and
+    mu = page_mu_weight[j] * (mean query of the group), so a page's score is
+    w_j * (q_g . mean q) * scale + log P: equal weights give bit-equal scores."""
+    d, r, P, G = wl.head_dim, wl.rank, wl.page_size, wl.group
+    rec_elems = d * (1 + r) + P * r
+    pool = torch.zeros((wl.num_blocks, wl.num_kv_heads, rec_elems), dtype=torch.bfloat16)
+    q = g["q"].float().cpu()
+    bt = g["block_table"].cpu()
+    for b in range(wl.batch):
+        for h in range(wl.num_kv_heads):
+            qbar = q[b, h * G:(h + 1) * G].mean(0)
+            for j, w in enumerate(page_mu_weight):
+                pool[int(bt[b, j]), h, :d] = (w * qbar).to(torch.bfloat16)
+    assert L.locks_summary_record_bytes(cfg) == rec_elems * 2
+    return pool.view(torch.uint8).reshape(-1).to(gg.DEV)
+
+
+def test_fused_select_ties_go_to_lower_page():
+    """locks_score_select runs the selection inside the scorer for this shape:
+    tied keys go to the lower page id, as in the two-launch path."""
+    wl = E2E.with_(batch=1, seq_lens=(64 * 40,), budget_pages=6)
+    cfg = _cfg(wl)
+    assert wl.max_pages <= 64 * 32  # the one-wave selection's range for G = 4
+    data, g = gg.make_inputs(wl, seed=2)
+    w = [0.0] * wl.max_pages
+    for j in (3, 7, 11, 20, 30):
+        w[j] = 0.5      # 5 tied winners for 4 free slots
+    w[38] = 1.0         # page J-1 = 39 is mandatory; 38 wins outright
+    pool = _record_pool(wl, cfg, g, w)
+    sel = gg.gpu_score_select(wl, cfg, g, pool)
+    hs = gg.gpu_scores(wl, cfg, g, pool)
+    sel_s, _ = gg.gpu_select(wl, cfg, g, hs)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel_s)
+    for h in range(wl.num_kv_heads):
+        assert sel[0, h].tolist() == [0, 3, 7, 11, 38, 39]
+    # all pages equal: lowest ids
+    pool2 = _record_pool(wl, cfg, g, [0.25] * wl.max_pages)
+    sel2 = gg.gpu_score_select(wl, cfg, g, pool2)
+    torch.cuda.synchronize()
+    for h in range(wl.num_kv_heads):
+        assert sel2[0, h].tolist() == [0, 1, 2, 3, 4, 39]
+
+
+@pytest.mark.parametrize("G,lens", [(4, (64 * 2048, 64 * 2047 + 5, 64 * 1500, 64 * 3 + 1)),
+                                    (8, (64 * 1024, 64 * 1000 + 63, 64 * 31))],
+                         ids=["g4_2048pages", "g8_1024pages"])
+def test_fused_select_matches_two_launches(G, lens):
+    """The selection inside the scorer gives the two-launch path's page ids bit
+    for bit (same arithmetic for sigma), up to its largest unit size."""
+    # 4 KV heads: a workgroup's waves take adjacent heads; 2: one head per workgroup
+    hkv = 4 if G == 4 else 2
+    wl = synth.Workload(f"fused_g{G}", len(lens), hkv, G, 128, 64, lens, 8, 32, "bf16", "bf16",
+                        n_needles=4, extra_blocks=3)
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=11, gen_device=gg.DEV)
+    pool = gg.gpu_build(wl, cfg, g)
+    sel = gg.gpu_score_select(wl, cfg, g, pool)
+    hs = gg.gpu_scores(wl, cfg, g, pool)
+    sel_s, _ = gg.gpu_select(wl, cfg, g, hs)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel_s)
+
+
 # --------------------------------------------------------------------------
 # (a5) sparse decode on the oracle's page selection
 # --------------------------------------------------------------------------
