@@ -580,7 +580,6 @@ def summarize_profiles(wl, flags, stats_dir, fetch_dir, write_dir):
 # reported only while these files are unchanged)
 KERNEL_SOURCES = {
     "page_score": ("page_score.hip", "score_lds.h", "common.h", "kernels.h"),
-    "score_select": ("page_score.hip", "score_lds.h", "select_wave.h", "select_unit.h", "common.h", "kernels.h"),
     "page_score_i4": ("page_score_i4.hip", "score_lds.h", "common.h", "kernels.h"),
     "select": ("select.hip", "select_unit.h", "common.h", "kernels.h"),
     "sparse_decode": ("sparse_decode.hip", "decode_split.h", "common.h", "kernels.h"),

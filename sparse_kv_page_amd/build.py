@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["locks_api.cpp", "page_score.hip", "page_score_i4.hip", "select.hip", "sparse_decode.hip",
            "build_summaries.hip"]
-HEADERS = ["common.h", "kernels.h", "score_lds.h", "select_unit.h", "select_wave.h", "decode_split.h",
+HEADERS = ["common.h", "kernels.h", "score_lds.h", "select_unit.h", "decode_split.h",
            os.path.join("..", "..", "include", "locks.h")]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-fno-gpu-rdc",

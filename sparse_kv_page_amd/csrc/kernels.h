@@ -18,12 +18,6 @@ struct ScoreArgs {
   int ppw;                    // pages per wave, set by the launcher (<= 128 LDS-staged, else <= 64)
   int head_major;             // LDS-staged scorer: a workgroup's waves take adjacent KV heads
   float scale;
-  // selection fused into the scorer (null arrive: scores only): per-(sequence,
-  // scorer row) arrival counters, zero between calls; the last workgroup of a
-  // row to arrive selects its units' pages into `selected` ([B][Hkv][k])
-  int32_t* arrive;
-  int32_t* selected;
-  int k;
 };
 
 struct SelectArgs {
@@ -79,8 +73,6 @@ constexpr int i4_record_bytes(int d, int r, int P) {
 }
 
 hipError_t launch_page_score(const ScoreArgs& a, int dtype, int D, int batch, hipStream_t s);
-// whether the scorer can also select (ScoreArgs::arrive) for this shape
-bool page_score_selects(int dtype, int D, int r, int G, int P, int max_pages);
 hipError_t launch_select(const SelectArgs& a, int batch, hipStream_t s);
 hipError_t launch_sparse_decode(const DecodeArgs& a, int dtype, int D, int batch, hipStream_t s);
 int decode_pages_per_split(int page_size, int tiles_per_wave);

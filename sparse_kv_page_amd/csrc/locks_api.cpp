@@ -63,8 +63,7 @@ int64_t rec_bytes(const locks_config_t* c) {
 
 // Workspace layout, shared by every entry point that takes a workspace:
 //   control words at the front: the decode arrival counters, one int32 per
-//     (sequence, KV head), then as many scorer arrival counters (the scorer
-//     that also selects); zero between calls, never written as scratch
+//     (sequence, KV head); zero between calls, never written as scratch
 //   scratch at the back (overwritten by every call), ending at the end of the
 //     buffer:
 //     score/select: head scores, page keys
@@ -75,7 +74,7 @@ int64_t rec_bytes(const locks_config_t* c) {
 // shorter scratch ending at the same place, so calls of different entry points
 // and batch sizes may share one workspace sized for the largest of them.
 size_t ctl_bytes(const locks_config_t* c, int32_t batch) {
-  return align_up(2 * (size_t)batch * c->num_kv_heads * sizeof(int32_t));
+  return align_up((size_t)batch * c->num_kv_heads * sizeof(int32_t));
 }
 
 // first scratch byte of a call needing `scratch` bytes: as late as the buffer
@@ -281,16 +280,6 @@ int locks_score_select(const locks_config_t* cfg, const void* q, const void* sum
   float* scores = reinterpret_cast<float*>(region);
   float* sigma = reinterpret_cast<float*>(region +
                                           align_up((size_t)batch * cfg->num_q_heads * max_pages * sizeof(float)));
-  const int G = cfg->num_q_heads / cfg->num_kv_heads;
-  if (cfg->summary_dtype != LOCKS_I4 &&
-      locks::page_score_selects(cfg->kv_dtype, cfg->head_dim, cfg->rank, G, cfg->page_size, max_pages)) {
-    // one launch: the scorer's last workgroup of each unit selects its pages
-    locks::ScoreArgs a = score_args(cfg, q, summary_pool, num_blocks, block_table, seq_lens, max_pages, scores);
-    a.arrive = static_cast<int32_t*>(ws) + (size_t)batch * cfg->num_kv_heads;
-    a.selected = selected;
-    a.k = cfg->budget_pages;
-    return hip_status(locks::launch_page_score(a, cfg->kv_dtype, cfg->head_dim, batch, stream));
-  }
   st = locks_page_score(cfg, q, summary_pool, num_blocks, block_table, seq_lens, batch, max_pages,
                         scores, stream);
   if (st != LOCKS_OK) return st;

@@ -21,7 +21,6 @@
 #include "common.h"
 #include "kernels.h"
 #include "score_lds.h"
-#include "select_wave.h"
 
 #include <atomic>
 
@@ -178,41 +177,16 @@ __global__ __launch_bounds__(256) void page_score_kernel(ScoreArgs a) {
 }
 
 // LDS-staged variant (bf16 records, rank 1/2/4/8, G * P >= 64): see score_lds.h.
-//
-// SEL: the selection ([Locks] §2, §4) runs in the same launch. A row of the
-// grid (blockIdx.y, blockIdx.z) holds whole units: one KV head's pages, or
-// with head_major the pages of kScoreLdsWaves adjacent heads. Each workgroup
-// stores its scores with device-scope stores, waits for them, and counts its
-// arrival on the row's counter; the last of the row's gridDim.x workgroups to
-// arrive selects the row's units, one wave per unit (select_wave.h), and
-// returns the counter to zero. Nothing waits on another workgroup.
-template <int D, int RT, int GQ, int P, bool SEL>
+template <int D, int RT, int GQ, int P>
 __global__ __launch_bounds__(kScoreLdsWaves * 64, 2) void page_score_lds_kernel(ScoreArgs a) {
   __shared__ ScoreLds<D, RT, GQ, P> lds;
   const int wave = threadIdx.x >> 6;
   if (a.head_major) {  // grid (page ranges, H_kv / waves, batch): adjacent heads, same pages
     const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * kScoreLdsWaves + wave);
-    score_wave_lds<D, RT, GQ, P, SEL>(a, blockIdx.z, h, __builtin_amdgcn_readfirstlane(blockIdx.x * a.ppw), a.ppw,
-                                      lds);
+    score_wave_lds<D, RT, GQ, P>(a, blockIdx.z, h, __builtin_amdgcn_readfirstlane(blockIdx.x * a.ppw), a.ppw, lds);
   } else {  // grid (page ranges / waves, H_kv, batch): consecutive page ranges of one head
     const int p0 = __builtin_amdgcn_readfirstlane((blockIdx.x * kScoreLdsWaves + wave) * a.ppw);
-    score_wave_lds<D, RT, GQ, P, SEL>(a, blockIdx.z, blockIdx.y, p0, a.ppw, lds);
-  }
-  if constexpr (SEL) {
-    __shared__ int last_s;
-    const int row = blockIdx.z * gridDim.y + blockIdx.y;
-    wait_vm_const<0>();  // this wave's score stores are done
-    __syncthreads();
-    if (threadIdx.x == 0) last_s = atomicAdd(&a.arrive[row], 1) == (int)gridDim.x - 1;
-    __syncthreads();
-    if (!last_s) return;
-    if (a.head_major) {
-      select_wave<GQ>(a.scores, a.seq_lens, a.selected, blockIdx.z, blockIdx.y * kScoreLdsWaves + wave, a.Hkv, a.P,
-                      a.k, a.max_pages);
-    } else if (wave == 0) {
-      select_wave<GQ>(a.scores, a.seq_lens, a.selected, blockIdx.z, blockIdx.y, a.Hkv, a.P, a.k, a.max_pages);
-    }
-    if (threadIdx.x == 0) atomicExch(&a.arrive[row], 0);
+    score_wave_lds<D, RT, GQ, P>(a, blockIdx.z, blockIdx.y, p0, a.ppw, lds);
   }
 }
 
@@ -253,18 +227,14 @@ dim3 score_grid(ScoreArgs& a, int batch, int waves, int max_ppw) {
   return dim3((waves_per_unit + kScoreWaves - 1) / kScoreWaves, a.Hkv, batch);
 }
 
-template <int D, int RT, int GQ, int P, bool SEL>
+template <int D, int RT, int GQ, int P>
 struct LdsTag {};
 
 template <int D, int RT, int GQ, int P>
 hipError_t launch_lds(ScoreArgs a, int batch, hipStream_t stream) {
+  const void* fn = reinterpret_cast<const void*>(&page_score_lds_kernel<D, RT, GQ, P>);
   constexpr int kThreads = kScoreLdsWaves * 64;
-  const int waves =
-      a.arrive ? cached_waves<LdsTag<D, RT, GQ, P, true>>(
-                     reinterpret_cast<const void*>(&page_score_lds_kernel<D, RT, GQ, P, true>), kThreads)
-               : cached_waves<LdsTag<D, RT, GQ, P, false>>(
-                     reinterpret_cast<const void*>(&page_score_lds_kernel<D, RT, GQ, P, false>), kThreads);
-  dim3 grid = score_grid(a, batch, waves, kScoreMaxPpw);
+  dim3 grid = score_grid(a, batch, cached_waves<LdsTag<D, RT, GQ, P>>(fn, kThreads), kScoreMaxPpw);
   a.head_major = a.Hkv % kScoreLdsWaves == 0;
   if (a.head_major) {
     grid = dim3((a.max_pages + a.ppw - 1) / a.ppw, a.Hkv / kScoreLdsWaves, batch);
@@ -272,12 +242,7 @@ hipError_t launch_lds(ScoreArgs a, int batch, hipStream_t stream) {
     const int waves_per_unit = (a.max_pages + a.ppw - 1) / a.ppw;
     grid = dim3((waves_per_unit + kScoreLdsWaves - 1) / kScoreLdsWaves, a.Hkv, batch);
   }
-  if (a.arrive) {
-    if (a.max_pages > 64 * kSelWaveNpl<GQ>) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((page_score_lds_kernel<D, RT, GQ, P, true>), grid, dim3(kThreads), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((page_score_lds_kernel<D, RT, GQ, P, false>), grid, dim3(kThreads), 0, stream, a);
-  }
+  hipLaunchKernelGGL((page_score_lds_kernel<D, RT, GQ, P>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -286,7 +251,6 @@ struct RegTag {};
 
 template <typename T, int D, int RT, int GQ, int TPL>
 hipError_t launch_one(ScoreArgs a, int batch, hipStream_t stream) {
-  if (a.arrive) return hipErrorInvalidValue;  // this kernel only scores
   const int waves = cached_waves<RegTag<T, D, RT, GQ, TPL>>(
       reinterpret_cast<const void*>(&page_score_kernel<T, D, RT, GQ, TPL>));
   // one round of resident waves; a wave keeps its block ids in one VGPR, so
@@ -347,16 +311,6 @@ hipError_t launch_rank(const ScoreArgs& a, int batch, hipStream_t s) {
 }
 
 }  // namespace
-
-// The LDS-staged kernel (bf16 records of rank 1, 2, 4 or 8, G = 4 or 8) selects
-// too, for units whose scores fit the one-wave selection's registers.
-bool page_score_selects(int dtype, int D, int r, int G, int P, int max_pages) {
-  if (dtype != 0 || (D != 64 && D != 128) || (P != 16 && P != 32 && P != 64)) return false;
-  if (r != 1 && r != 2 && r != 4 && r != 8) return false;
-  if (G == 4) return max_pages <= 64 * kSelWaveNpl<4>;
-  if (G == 8) return max_pages <= 64 * kSelWaveNpl<8>;
-  return false;
-}
 
 hipError_t launch_page_score(const ScoreArgs& args, int dtype, int D, int batch, hipStream_t stream) {
   if (dtype == 0) return D == 64 ? launch_rank<bf16_t, 64>(args, batch, stream)

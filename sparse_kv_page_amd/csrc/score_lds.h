@@ -169,9 +169,8 @@ struct alignas(16) ScoreLds {
 };
 
 // One wave scores pages [p0, p0 + min(ppw, Jc - p0)) of the unit (b, h) for
-// all G heads (ppw <= kScoreMaxPpw, p0 wave-uniform). SEL: the scores are
-// stored with device-scope stores (the scorer selects in the same launch).
-template <int D, int RT, int GQ, int P, bool SEL>
+// all G heads (ppw <= kScoreMaxPpw, p0 wave-uniform).
+template <int D, int RT, int GQ, int P>
 __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h, int p0, int ppw,
                                                ScoreLds<D, RT, GQ, P>& L) {
   using M = ScoreMfma<bf16_t, D>;
@@ -367,19 +366,14 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
   }
   wave_lds_sync();
   // coalesced store of the wave's scores: lane t writes page p0 + t of each head
-  // (device-scope stores when another workgroup reads them back in this launch)
   float* out = a.scores + ((int64_t)b * Hq + (int64_t)h * G) * a.max_pages + p0;
-  auto put = [&](float* p, float v) {
-    if constexpr (SEL) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else *p = v;
-  };
   if (lane < np) {
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) put(out + (int64_t)gg * a.max_pages + lane, sbuf[wave][lane][gg]);
+    for (int gg = 0; gg < G; ++gg) out[(int64_t)gg * a.max_pages + lane] = sbuf[wave][lane][gg];
   }
   if (lane + 64 < np) {
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) put(out + (int64_t)gg * a.max_pages + lane + 64, sbuf[wave][lane + 64][gg]);
+    for (int gg = 0; gg < G; ++gg) out[(int64_t)gg * a.max_pages + lane + 64] = sbuf[wave][lane + 64][gg];
   }
 }
 
