@@ -69,6 +69,9 @@ struct alignas(16) ScoreI4Lds {
   float sbuf[kScoreWaves][kI4MaxPpw][GQ];
 };
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f2_t;
+
 constexpr uint32_t kNibMask = 0x00780078u;  // one nibble at mantissa bits 3..6 of each bf16 half
 constexpr uint32_t kNibBias = 0x41804180u;  // bf16 16.0 in both halves
 
@@ -102,6 +105,7 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   constexpr int kSteps = M::kSteps;
   constexpr int kWVec = (RT + 1 + 3) / 4;        // scaled basis rows and the centroid term
   constexpr int kCi = RT % 4;                    // the centroid's rows RT, RT + 1 sit in lane group RT / 4
+  constexpr bool kMfmaB = RT == 8 && G == 4 && P >= 16;  // phase B on the matrix cores
   auto& slots = L.slots;
   auto& wbuf = L.wbuf;
   auto& sbuf = L.sbuf;
@@ -174,6 +178,98 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   const int npre = np < NS ? np : NS;
   for (int t = 0; t < npre; ++t) issue(t, t);
 
+  // Phase B on the matrix cores (rank 8, 4 query heads per KV head): the
+  // logits of up to 4 pages come from one v_mfma_f32_16x16x32_bf16 per 16
+  // tokens and per half of w,
+  //   Z[token][4 p + g] = sum_rho code_p[token][rho] w_(p,g)[rho] - 128 sum_rho w_(p,g)[rho],
+  // with A row = token, k = 8 p + rho (a lane's k group kg is the page p)
+  // and B block-diagonal: column 4 p + g holds w_(p,g) in k rows 8 p .. 8 p + 7
+  // and zero elsewhere. Coefficient bytes are exact in bf16; w is split into
+  // bf16 hi + lo (RNE twice: relative error below 2^-17), so every product is
+  // exact and the sums are fp32 as on the VALU path. Lane (n, kg) then holds
+  // tokens 16 m + 4 kg .. + 3 of column n = (page n / 4, head n % 4); its page
+  // LSE takes the lane's values and the three other k groups' (xor 16, 32).
+  auto score_pages_mfma_b = [&](auto npg_tag, int t, const uint8_t* const* rec) {
+    constexpr int NPG = decltype(npg_tag)::value;
+    constexpr int kTiles = P / 16;
+    const int cp = n >> 2, cg = n & 3;  // the lane's column: page, head
+    const uint8_t* rec_k = rec[0];      // the page of the lane's k group (A)
+    const uint8_t* rec_c = rec[0];      // the page of the lane's column (token scales)
+    bool ok[NPG];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      if (p > 0 && kg == p) rec_k = rec[p];
+      if (p > 0 && cp == p) rec_c = rec[p];
+      ok[p] = bid_ok(bid_at(t + p));
+    }
+    const bool col_ok = cp < NPG;
+    const bool mine = col_ok && kg == cp;
+    const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(&wbuf[wave][cp][cg][0]);
+    const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(&wbuf[wave][cp][cg][4]);
+    const float qmu_c = wbuf[wave][cp][cg][RT];
+    const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    float wsum_c = 0.f;
+#pragma unroll
+    for (int rho = 0; rho < RT; ++rho) wsum_c += wv[rho];
+    const float init = col_ok ? -128.f * wsum_c : 0.f;
+    u32x4_t bh, bl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f2_t x = {mine ? wv[2 * e] : 0.f, mine ? wv[2 * e + 1] : 0.f};
+      const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+      const f2_t r = {x[0] - bf16_lo(h), x[1] - bf16_hi(h)};
+      bh[e] = h;
+      bl[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+    }
+    const bf16x8_t Bh = __builtin_bit_cast(bf16x8_t, bh);
+    const bf16x8_t Bl = __builtin_bit_cast(bf16x8_t, bl);
+    const uint8_t* cb = rec_k + R::kHeadBytes;
+    const uint8_t* tsc = rec_c + R::kScaleOff + 2 * (RT + 1);
+    float z[kTiles][4];
+#pragma unroll
+    for (int m = 0; m < kTiles; ++m) {
+      const u32x2_t cw = *reinterpret_cast<const u32x2_t*>(cb + (16 * m + n) * 8);
+      u32x4_t av;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t wd = cw[e >> 1];
+        const int sh = 16 * (e & 1);
+        const f2_t x = {(float)((wd >> sh) & 0xffu), (float)((wd >> (sh + 8)) & 0xffu)};
+        av[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+      }
+      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av);
+      f32x4_t acc = {init, init, init, init};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl, acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float st = bf16_to_f32(*reinterpret_cast<const bf16_t*>(tsc + 2 * (16 * m + 4 * kg + i)));
+        z[m][i] = st * acc[i];
+      }
+    }
+    float mx = z[0][0];
+#pragma unroll
+    for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[m][i]);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    float sm = 0.f;
+#pragma unroll
+    for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm += exp2_fast(z[m][i] - mx);
+    sm += shfl_xor(sm, 16);
+    sm += shfl_xor(sm, 32);
+    bool okc = false;
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) okc = cp == p ? ok[p] : okc;
+    if (kg == 0 && col_ok) {
+      const float s = qmu_c + (mx + log2_fast(sm)) * kLn2;
+      sbuf[wave][t + cp][cg] = okc ? s : -INFINITY;
+    }
+  };
+
   auto score_pages = [&](auto npg_tag, int t, int s0) {
     constexpr int NPG = decltype(npg_tag)::value;
     const uint8_t* rec[NPG];
@@ -219,6 +315,9 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
       if (n < G) *reinterpret_cast<f32x4_t*>(&wbuf[wave][p][n][kg * 4]) = o;
     }
     wave_lds_sync();
+    if constexpr (kMfmaB) {
+      score_pages_mfma_b(std::integral_constant<int, NPG>{}, t, rec);
+    } else {
     float ws[NPG][RT], wsum[NPG], qmu[NPG];
 #pragma unroll
     for (int p = 0; p < NPG; ++p) {
@@ -293,6 +392,7 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
         const float s = qmu[p] + (mx[p] + log2_fast(sm[p])) * kLn2;
         sbuf[wave][t + p][g] = bid_ok(bid) ? s : -INFINITY;
       }
+    }
     }
   };
 
