@@ -105,7 +105,7 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   constexpr int kSteps = M::kSteps;
   constexpr int kWVec = (RT + 1 + 3) / 4;        // scaled basis rows and the centroid term
   constexpr int kCi = RT % 4;                    // the centroid's rows RT, RT + 1 sit in lane group RT / 4
-  constexpr bool kMfmaB = RT == 8 && G == 4 && P >= 16;  // phase B on the matrix cores
+  constexpr bool kMfmaB = (RT == 8 || RT == 4) && G == 4 && P >= 16;  // phase B on the matrix cores
   auto& slots = L.slots;
   auto& wbuf = L.wbuf;
   auto& sbuf = L.sbuf;
@@ -178,12 +178,12 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   const int npre = np < NS ? np : NS;
   for (int t = 0; t < npre; ++t) issue(t, t);
 
-  // Phase B on the matrix cores (rank 8, 4 query heads per KV head): the
-  // logits of up to 4 pages come from one v_mfma_f32_16x16x32_bf16 per 16
-  // tokens and per half of w,
+  // Phase B on the matrix cores (rank 8 or 4, 4 query heads per KV head): the
+  // logits of up to 4 pages come from one v_mfma_f32_16x16x32_bf16 (rank 8) or
+  // v_mfma_f32_16x16x16_bf16 (rank 4) per 16 tokens and per half of w,
   //   Z[token][4 p + g] = sum_rho code_p[token][rho] w_(p,g)[rho] - 128 sum_rho w_(p,g)[rho],
-  // with A row = token, k = 8 p + rho (a lane's k group kg is the page p)
-  // and B block-diagonal: column 4 p + g holds w_(p,g) in k rows 8 p .. 8 p + 7
+  // with A row = token, k = r p + rho (a lane's k group kg is the page p)
+  // and B block-diagonal: column 4 p + g holds w_(p,g) in k rows r p .. r p + r - 1
   // and zero elsewhere. Coefficient bytes are exact in bf16; w is split into
   // bf16 hi + lo (RNE twice: relative error below 2^-17), so every product is
   // exact and the sums are fp32 as on the VALU path. Lane (n, kg) then holds
@@ -192,6 +192,7 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   auto score_pages_mfma_b = [&](auto npg_tag, int t, const uint8_t* const* rec) {
     constexpr int NPG = decltype(npg_tag)::value;
     constexpr int kTiles = P / 16;
+    constexpr int kW = RT >= 2 ? RT / 2 : 1;  // packed bf16 pairs per lane operand (one page's k range)
     const int cp = n >> 2, cg = n & 3;  // the lane's column: page, head
     const uint8_t* rec_k = rec[0];      // the page of the lane's k group (A)
     const uint8_t* rec_c = rec[0];      // the page of the lane's column (token scales)
@@ -204,43 +205,63 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
     }
     const bool col_ok = cp < NPG;
     const bool mine = col_ok && kg == cp;
-    const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(&wbuf[wave][cp][cg][0]);
-    const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(&wbuf[wave][cp][cg][4]);
+    float wv[RT >= 4 ? RT : 4];
+#pragma unroll
+    for (int v = 0; v < RT / 4; ++v) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&wbuf[wave][cp][cg][4 * v]);
+      wv[4 * v] = x[0]; wv[4 * v + 1] = x[1]; wv[4 * v + 2] = x[2]; wv[4 * v + 3] = x[3];
+    }
     const float qmu_c = wbuf[wave][cp][cg][RT];
-    const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
     float wsum_c = 0.f;
 #pragma unroll
     for (int rho = 0; rho < RT; ++rho) wsum_c += wv[rho];
     const float init = col_ok ? -128.f * wsum_c : 0.f;
-    u32x4_t bh, bl;
+    uint32_t bh[kW], bl[kW];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < kW; ++e) {
       const f2_t x = {mine ? wv[2 * e] : 0.f, mine ? wv[2 * e + 1] : 0.f};
       const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
       const f2_t r = {x[0] - bf16_lo(h), x[1] - bf16_hi(h)};
       bh[e] = h;
       bl[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
     }
-    const bf16x8_t Bh = __builtin_bit_cast(bf16x8_t, bh);
-    const bf16x8_t Bl = __builtin_bit_cast(bf16x8_t, bl);
     const uint8_t* cb = rec_k + R::kHeadBytes;
     const uint8_t* tsc = rec_c + R::kScaleOff + 2 * (RT + 1);
     float z[kTiles][4];
 #pragma unroll
     for (int m = 0; m < kTiles; ++m) {
-      const u32x2_t cw = *reinterpret_cast<const u32x2_t*>(cb + (16 * m + n) * 8);
-      u32x4_t av;
+      // the RT coefficient bytes of token 16 m + n of the lane's page, exact in bf16
+      uint32_t cw[RT >= 4 ? RT / 4 : 1];
+      if constexpr (RT == 8) {
+        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(cb + (16 * m + n) * 8);
+        cw[0] = v[0]; cw[1] = v[1];
+      } else {
+        cw[0] = *reinterpret_cast<const uint32_t*>(cb + (16 * m + n) * 4);
+      }
+      uint32_t av[kW];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < kW; ++e) {
         const uint32_t wd = cw[e >> 1];
         const int sh = 16 * (e & 1);
         const f2_t x = {(float)((wd >> sh) & 0xffu), (float)((wd >> (sh + 8)) & 0xffu)};
         av[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
       }
-      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av);
       f32x4_t acc = {init, init, init, init};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bh, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl, acc, 0, 0, 0);
+      if constexpr (RT == 8) {
+        // v_mfma_f32_16x16x32_bf16: the lane's k range is 8 kg .. 8 kg + 7
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, u32x4_t{av[0], av[1], av[2], av[3]});
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, u32x4_t{bh[0], bh[1], bh[2], bh[3]}),
+                                                      acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, u32x4_t{bl[0], bl[1], bl[2], bl[3]}),
+                                                      acc, 0, 0, 0);
+      } else {
+        // v_mfma_f32_16x16x16_bf16: the lane's k range is 4 kg .. 4 kg + 3
+        const bf16x4_t A = __builtin_bit_cast(bf16x4_t, u32x2_t{av[0], av[1]});
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(bf16x4_t, u32x2_t{bh[0], bh[1]}), acc, 0,
+                                                        0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(bf16x4_t, u32x2_t{bl[0], bl[1]}), acc, 0,
+                                                        0, 0);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float st = bf16_to_f32(*reinterpret_cast<const bf16_t*>(tsc + 2 * (16 * m + 4 * kg + i)));

@@ -40,12 +40,15 @@ SHAPES = [
     synth.Workload("i4_d64_p16_r8_g2", 2, 2, 2, 64, 16, (16 * 77, 16 * 20 + 9), 8, 10, "bf16", "i4"),
     synth.Workload("i4_d64_p32_r2_g2", 1, 2, 2, 64, 32, (32 * 64 + 1,), 2, 8, "bf16", "i4"),
     synth.Workload("i4_d64_p64_r1_g8", 2, 1, 8, 64, 64, (64 * 50, 64 * 3), 1, 8, "bf16", "i4"),
-    # rank 8 with 4 query heads per KV head scores its tokens on the matrix
-    # cores (up to 4 pages per product): page counts that leave 1-3 pages over
+    # ranks 8 and 4 with 4 query heads per KV head score their tokens on the
+    # matrix cores (up to 4 pages per product): page counts that leave 1-3
+    # pages over
     synth.Workload("i4_d128_p16_r8_g4", 2, 2, 4, 128, 16, (16 * 139 + 7, 16 * 66), 8, 16, "bf16", "i4",
                    extra_blocks=2),
     synth.Workload("i4_d128_p32_r8_g4", 3, 1, 4, 128, 32, (32 * 71, 32 * 5 + 3, 32 * 2), 8, 8, "bf16", "i4"),
     synth.Workload("i4_d64_p64_r8_g4", 2, 2, 4, 64, 64, (64 * 45 + 1, 64 * 7), 8, 8, "bf16", "i4"),
+    synth.Workload("i4_d128_p16_r4_g4", 2, 2, 4, 128, 16, (16 * 101 + 9, 16 * 18), 4, 16, "bf16", "i4"),
+    synth.Workload("i4_d64_p64_r4_g4", 1, 3, 4, 64, 64, (64 * 37 + 50,), 4, 8, "bf16", "i4"),
 ]
 
 
