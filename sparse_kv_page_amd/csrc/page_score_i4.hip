@@ -69,9 +69,6 @@ struct alignas(16) ScoreI4Lds {
   float sbuf[kScoreWaves][kI4MaxPpw][GQ];
 };
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-typedef __attribute__((ext_vector_type(2))) float f2_t;
-
 constexpr uint32_t kNibMask = 0x00780078u;  // one nibble at mantissa bits 3..6 of each bf16 half
 constexpr uint32_t kNibBias = 0x41804180u;  // bf16 16.0 in both halves
 

@@ -80,6 +80,8 @@ struct ScoreMfma<float, D> {
 // conflict-free, with the G head groups reading the same addresses.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f2_t;
 
 __host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
@@ -252,6 +254,94 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
   const int npre = np < NS ? np : NS;
   for (int t = 0; t < npre; ++t) issue(t, t);
 
+  // Token logits on the matrix cores (rank 8 or 4, 4 query heads per KV
+  // head): for up to 4 pages at once,
+  //   Z[token][4 p + g] = sum_rho C_p[token][rho] w_(p,g)[rho] * scale * log2(e)
+  // is one v_mfma_f32_16x16x32_bf16 (rank 8) or v_mfma_f32_16x16x16_bf16
+  // (rank 4) per 16 tokens and per half of w. A row = token, k = r p + rho (a
+  // lane's k group kg is page p: the token's coefficient row, read from LDS as
+  // it is stored); B is block-diagonal, column 4 p + g holding w_(p,g) in k
+  // rows r p .. r p + r - 1 and zero elsewhere. w is split into bf16 hi + lo
+  // (RNE twice, relative error below 2^-17), so every product is exact and
+  // the sums are fp32 as on the VALU path. Lane (n, kg) then holds tokens
+  // 16 m + 4 kg .. + 3 of column n = (page n / 4, head n % 4); the page LSE
+  // takes the lane's values and the three other k groups' (xor 16, 32).
+  constexpr bool kMfmaB = (RT == 8 || RT == 4) && G == 4 && P >= 16;
+  auto score_pages_mfma_b = [&](auto npg_tag, int t, const uint8_t* const* rec) {
+    constexpr int NPG = decltype(npg_tag)::value;
+    constexpr int kTiles = P / 16;
+    constexpr int kW = RT >= 2 ? RT / 2 : 1;  // packed bf16 pairs per lane operand (one page's k range)
+    const int cp = n >> 2, cg = n & 3;        // the lane's column: page, head
+    const uint8_t* rec_k = rec[0];            // the page of the lane's k group (A)
+    bool ok[NPG];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) {
+      if (p > 0 && kg == p) rec_k = rec[p];
+      ok[p] = bid_ok(bid_at(t + p));
+    }
+    const bool col_ok = cp < NPG;
+    const bool mine = col_ok && kg == cp;
+    float wv[RT >= 4 ? RT : 4];
+#pragma unroll
+    for (int v = 0; v < RT / 4; ++v) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&wbuf[wave][cp][cg][4 * v]);
+      wv[4 * v] = x[0] * zscale; wv[4 * v + 1] = x[1] * zscale;
+      wv[4 * v + 2] = x[2] * zscale; wv[4 * v + 3] = x[3] * zscale;
+    }
+    const float qmu_c = wbuf[wave][cp][cg][RT];
+    uint32_t bh[kW], bl[kW];
+#pragma unroll
+    for (int e = 0; e < kW; ++e) {
+      const f2_t x = {mine ? wv[2 * e] : 0.f, mine ? wv[2 * e + 1] : 0.f};
+      const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+      const f2_t r = {x[0] - bf16_lo(h), x[1] - bf16_hi(h)};
+      bh[e] = h;
+      bl[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+    }
+    const uint8_t* cb = rec_k + R::kHeadBytes;
+    float z[kTiles][4];
+#pragma unroll
+    for (int m = 0; m < kTiles; ++m) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (RT == 8) {
+        const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(cb + (16 * m + n) * 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, u32x4_t{bh[0], bh[1], bh[2], bh[3]}),
+                                                      acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, u32x4_t{bl[0], bl[1], bl[2], bl[3]}),
+                                                      acc, 0, 0, 0);
+      } else {
+        const bf16x4_t A = *reinterpret_cast<const bf16x4_t*>(cb + (16 * m + n) * 8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(bf16x4_t, u32x2_t{bh[0], bh[1]}), acc, 0,
+                                                        0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(bf16x4_t, u32x2_t{bl[0], bl[1]}), acc, 0,
+                                                        0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[m][i] = acc[i];
+    }
+    float mx = z[0][0];
+#pragma unroll
+    for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[m][i]);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    float sm = 0.f;
+#pragma unroll
+    for (int m = 0; m < kTiles; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm += exp2_fast(z[m][i] - mx);
+    sm += shfl_xor(sm, 16);
+    sm += shfl_xor(sm, 32);
+    bool okc = false;
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) okc = cp == p ? ok[p] : okc;
+    if (kg == 0 && col_ok) {
+      const float sc = qmu_c * a.scale + (mx + log2_fast(sm)) * kLn2;
+      sbuf[wave][t + cp][cg] = okc ? sc : -INFINITY;
+    }
+  };
+
   // Several pages per iteration: their dependent chains (LDS reads -> MFMA ->
   // transpose through LDS -> logits -> DPP reductions) interleave, which hides
   // the chain latency the two resident waves per SIMD cannot (4 pages measured
@@ -277,6 +367,9 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
       for (int p = 0; p < NPG; ++p) *reinterpret_cast<f32x4_t*>(&wbuf[wave][p][n][kg * 4]) = acc[p];
     }
     wave_lds_sync();
+    if constexpr (kMfmaB) {
+      score_pages_mfma_b(std::integral_constant<int, NPG>{}, t, rec);
+    } else {
     float ws[NPG][RT], qmu[NPG];
 #pragma unroll
     for (int p = 0; p < NPG; ++p) {
@@ -342,6 +435,7 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
         const float sc = qmu[p] * a.scale + (mx[p] + log2_fast(sm[p])) * kLn2;
         sbuf[wave][t + p][g] = bid_ok(bid) ? sc : -INFINITY;
       }
+    }
     }
   };
 
