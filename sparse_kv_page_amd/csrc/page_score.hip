@@ -18,6 +18,8 @@
 //    reads the coefficient rows of its TPL consecutive tokens straight from
 //    the record, forms their logits w_g . c_i, and the page LSE is reduced
 //    across the head's lanes with DPP (max, then sum of 2^(z - max)).
+//    The LDS-staged kernel (score_lds.h) forms these logits on the matrix
+//    cores instead at rank 8 or 4 with G = 4, four pages per product.
 #include "common.h"
 #include "kernels.h"
 #include "score_lds.h"
