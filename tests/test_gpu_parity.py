@@ -820,3 +820,117 @@ def test_decode_step_large_budget():
     torch.cuda.synchronize()
     assert torch.equal(sel_f, sel_s)
     assert torch.equal(out_f, out_s)
+
+
+# --------------------------------------------------------------------------
+# the whole-model step at its full size: 32 layers x 16 sequences of ~64K
+# tokens (all layers' K/V in one ~138 GB pool, block offsets past 4 GiB),
+# r = 4, k = 32, with the builds of completing pages interleaved; sampled
+# (layer, sequence, KV head) units against the oracle
+# --------------------------------------------------------------------------
+def _full_step_check():
+    nl, B, Hkv, G, d, P, r, k = 32, 16, 8, 4, 128, 64, 4, 32
+    Hq = Hkv * G
+    lens0 = [65536 + 4 * s for s in range(B)]
+    steps = 5
+    max_pages = -(-(max(lens0) + steps + P) // P)
+    nb = B * max_pages
+    NB = nl * nb
+    cfg = L.make_config(d, P, r, Hq, Hkv, k, "bf16", "bf16", 1.0 / np.sqrt(d))
+    dev = gg.DEV
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    kp = torch.empty((NB, Hkv, P, d), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty((NB, Hkv, P, d), dtype=torch.bfloat16, device=dev)
+    for pool, flip in ((kp, False), (vp, True)):
+        slab = torch.randn((nb, Hkv, P, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        for layer in range(nl):
+            pool[layer * nb:(layer + 1) * nb].copy_(slab.flip(0) if flip else slab)
+        del slab
+    bt = torch.empty((nl, B, max_pages), dtype=torch.int32, device=dev)
+    for layer in range(nl):
+        bt[layer] = (torch.randperm(nb, generator=g, device=dev).to(torch.int32) + layer * nb).view(B, max_pages)
+    q = torch.randn((nl, B, Hq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    seq = torch.tensor(lens0, dtype=torch.int32, device=dev)
+    spool = L.summary_pool_for(cfg, NB, dev)
+    full_ids = torch.cat([bt[layer, s, :lens0[s] // P] for layer in range(nl) for s in range(B)]).contiguous()
+    L.locks_build_summaries(cfg, kp, NB, full_ids, full_ids.numel(), spool)
+    torch.cuda.synchronize()
+    print(f"[full step] {NB} blocks filled, {full_ids.numel() * Hkv} tiles built", flush=True)
+    ws_bytes = L.locks_workspace_size(cfg, B, max_pages)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    sel = torch.empty((nl, B, Hkv, k), dtype=torch.int32, device=dev)
+    out = torch.empty((nl, B, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((nl, B, Hq), dtype=torch.float32, device=dev)
+    bt_c = bt.cpu()
+    built = []
+    for t in range(steps):
+        for layer in range(nl):
+            L.locks_decode_step(cfg, q[layer], spool, kp, vp, NB, bt[layer], seq, B, max_pages, sel[layer],
+                                out[layer], lse[layer], ws, ws_bytes)
+        if t == steps - 1:
+            break
+        ids = []
+        for s in range(B):
+            T = lens0[s] + t + 1
+            if T % P == 0:
+                ids += [int(bt_c[layer, s, T // P - 1]) for layer in range(nl)]
+                built.append((s, T // P - 1))
+        if ids:
+            idt = torch.tensor(ids, dtype=torch.int32, device=dev)
+            L.locks_build_summaries(cfg, kp, NB, idt, idt.numel(), spool)
+        seq.add_(1)
+    torch.cuda.synchronize()
+    print(f"[full step] {steps} steps done, pages built during them: {built}", flush=True)
+    assert built, "a page completes during the steps"
+    lens_now = [x + steps - 1 for x in lens0]
+    q_c = q.cpu()
+    sel_c = sel.cpu()
+    out_c = gg.f64(out.cpu())
+    units = [(0, 0, 0), (31, 15, 7), (17, built[0][0], 3)]
+    for layer, s, h in units:
+        T = lens_now[s]
+        J, Jc = -(-T // P), T // P
+        idx = bt_c[layer, s, :Jc].long().to(dev)
+        mu, vt, cf = (gg.f64(x) for x in L.split_records(cfg, spool[idx, h].cpu()))
+        qu = gg.f64(q_c[layer, s, h * G:(h + 1) * G])
+        s_o = oracle.page_scores(qu, mu, vt, cf, cfg.softmax_scale)
+        if J <= k:
+            sel_o, sigma_o = oracle.select(np.zeros(0), Jc, J, k), None
+        else:
+            _, sigma_o = oracle.combine(s_o)
+            sel_o = oracle.select(sigma_o, Jc, J, k)
+        wl_u = synth.Workload("full_unit", 1, Hkv, G, d, P, (T,), r, k, "bf16", "bf16")
+        gg.check_selection(wl_u, 0, sel_c[layer, s, h].tolist(), sel_o.tolist(), sigma_o)
+        # attention over the GPU's own selection, original K/V
+        ks, vs = [], []
+        for j in sel_c[layer, s, h].tolist():
+            if j < 0:
+                continue
+            blk = int(bt_c[layer, s, j])
+            nt = min(P, T - j * P)
+            ks.append(gg.f64(kp[blk, h, :nt].cpu()))
+            vs.append(gg.f64(vp[blk, h, :nt].cpu()))
+        o_ref, _ = oracle.attend(qu, np.concatenate(ks), np.concatenate(vs), cfg.softmax_scale)
+        assert np.max(np.abs(out_c[layer, s, h * G:(h + 1) * G] - o_ref)) <= 2e-2
+    # the pages built during the steps: a rank-4 fit within the Eckart-Young residual
+    s, j = built[0]
+    for layer in (0, nl - 1):
+        blk = int(bt_c[layer, s, j])
+        keys = np.stack([gg.f64(kp[blk, h].cpu()) for h in range(Hkv)])
+        _, _, _, ev, _ = oracle.build_pages(keys, r)
+        _, vt_g, _ = L.split_records(cfg, spool[blk].cpu())
+        for h in range(Hkv):
+            D = keys[h] - keys[h].mean(0)
+            vt = gg.f64(vt_g[h])
+            tau = float(np.sum(np.clip(ev[h, r:], 0, None)))
+            resid = float(np.linalg.norm(D - D @ vt.T @ vt) ** 2)
+            assert resid <= tau + 2e-2 * float(np.sum(np.clip(ev[h], 0, None)))
+
+
+def test_full_step_sampled():
+    try:
+        _full_step_check()  # its ~150 GB of device buffers are released on return
+    finally:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
