@@ -42,6 +42,9 @@ def parse():
                     help="summary records (default: the workload's); i4 = 4-bit basis, 8-bit "
                          "centroid and coefficients, bf16 scales, reported as workload <name>_i4")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kv-host", action="store_true",
+                    help="hold the K/V pools in pinned host memory: the decode reads the selected pages "
+                         "over the host link (the summaries stay in HBM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -135,6 +138,15 @@ def main():
     print(f"[bench] prefill build of {n_full * Hkv} page tiles: {prefill_build_ms:.2f} ms",
           file=sys.stderr, flush=True)
 
+    # K/V in pinned host memory: the decode reads the selected pages in place
+    kp_dec, vp_dec, kv_host = kp, vp, None
+    if args.kv_host:
+        kh, kp_dec = host_pool(kp)
+        vh, vp_dec = host_pool(vp)
+        kv_host = (kh, vh)
+        print(f"[bench] K/V pools in pinned host memory ({2 * kh.numel() * kh.element_size() / 2**30:.1f} GiB)",
+              file=sys.stderr, flush=True)
+
     # pages completing in a decode step: the current page of every sequence whose
     # length is a multiple of the page size
     step_ids = torch.stack([bt[b, int(wl.seq_lens[b]) // P - 1] for b in range(B)
@@ -156,7 +168,7 @@ def main():
         L.locks_select_pages(cfg, scores, sl, B, maxp, sel, sigma)
 
     def decode():
-        L.locks_sparse_decode(cfg, q, kp, vp, wl.num_blocks, bt, sl, sel, B, maxp, out, lse, ws,
+        L.locks_sparse_decode(cfg, q, kp_dec, vp_dec, wl.num_blocks, bt, sl, sel, B, maxp, out, lse, ws,
                               ws_bytes)
 
     def staged():
@@ -167,7 +179,7 @@ def main():
 
     def step():
         # the whole step through the library's one-call entry point
-        L.locks_decode_step(cfg, q, pool, kp, vp, wl.num_blocks, bt, sl, B, maxp, sel, out, lse, ws,
+        L.locks_decode_step(cfg, q, pool, kp_dec, vp_dec, wl.num_blocks, bt, sl, B, maxp, sel, out, lse, ws,
                             ws_bytes)
 
     for _ in range(args.warmup):
@@ -245,7 +257,8 @@ def main():
         "vs_baseline": None,
         "dtype": wl.kv_dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": B, "context_tokens": int(wl.seq_lens[0]),
+        "config": {"workload": wl.name + ("_kvhost" if kv_host is not None else ""), "batch": B,
+                   "context_tokens": int(wl.seq_lens[0]),
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "page_size": P, "rank": r,
                    "budget_tokens": k * P, "summary_dtype": wl.summary_dtype,
                    "parallelism": "single-gpu"},
@@ -253,7 +266,13 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "step_achieved_GBps": round(step_gbs, 1),
         "roofline": roofline("page_score", wl, summary_bytes, stage_us["page_score"]),
-        "sparse_decode_roofline": roofline("sparse_decode", wl, kv_bytes, stage_us["sparse_decode"]),
+        "sparse_decode_roofline": (roofline("sparse_decode", wl, kv_bytes, stage_us["sparse_decode"])
+                                   if kv_host is None else
+                                   {"bound": "host link", "kernel": "sparse_decode",
+                                    "achieved": round(kv_bytes / (stage_us["sparse_decode"] * 1e-6) / 1e9, 1),
+                                    "unit": "GB/s", "algorithmic_bytes_per_launch": kv_bytes,
+                                    "avg_launch_us": round(stage_us["sparse_decode"], 3)}),
+        "kv_resident": "host" if kv_host is not None else "hbm",
         "staged_step_us": round(staged_ms * 1e3, 3),
         "stages_us": {n: round(v, 3) for n, v in stage_us.items()},
         "step_with_build_us": round(step_ms * 1e3 + stage_us["build_step"], 3),
@@ -449,6 +468,25 @@ KERNEL_PATTERNS = (("page_score", ("page_score_lds_kernel", "page_score_kernel",
                    ("select", ("select_kernel",)),
                    ("sparse_decode", ("sparse_decode_kernel",)),
                    ("build", ("build_kernel",)))
+
+
+def host_pool(t):
+    """Pinned host copy of a device pool and the address the GPU reads it at
+    (hipHostGetDevicePointer; raises when the memory is not mapped for the
+    device, so no kernel ever gets an unmapped address)."""
+    import ctypes
+
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    hip.hipHostGetDevicePointer.restype = ctypes.c_int
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    dptr = ctypes.c_void_p()
+    st = hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(h.data_ptr()), 0)
+    if st != 0 or not dptr.value:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({st})")
+    return h, int(dptr.value)
 
 
 def _clean(name):

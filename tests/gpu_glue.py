@@ -312,3 +312,34 @@ def i4_unit_summaries(wl, qs, bt, b, h, n):
     sub = {k: (v.cpu().numpy() if torch.is_tensor(v) else np.asarray(v))[idx, h] for k, v in qs.items()
            if k != "padding"}
     return oracle.dequantize_summaries(sub)
+
+
+# --------------------------------------------------------------------------
+# host-resident K/V: pinned host memory that the GPU reads over the host link
+# --------------------------------------------------------------------------
+_hip = None
+
+
+def _hip_runtime():
+    global _hip
+    if _hip is None:
+        import ctypes
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                                 ctypes.c_uint]
+        _hip.hipHostGetDevicePointer.restype = ctypes.c_int
+    return _hip
+
+
+def host_pool(t: torch.Tensor):
+    """A pinned host copy of the pool `t` and the address the GPU reads it at
+    (hipHostGetDevicePointer; raises when the memory is not mapped for the
+    device, so no kernel is launched on an unmapped address)."""
+    import ctypes
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    dptr = ctypes.c_void_p()
+    st = _hip_runtime().hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(h.data_ptr()), 0)
+    if st != 0 or not dptr.value:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({st})")
+    return h, int(dptr.value)

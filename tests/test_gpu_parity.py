@@ -823,6 +823,29 @@ def test_decode_step_large_budget():
 
 
 # --------------------------------------------------------------------------
+# K/V held in pinned host memory (the capacity use of [Locks] §5: only the
+# selected pages cross the host link); the decode reads them in place
+# --------------------------------------------------------------------------
+def test_decode_with_host_resident_kv():
+    wl = E2E
+    cfg = _cfg(wl)
+    data, g = gg.make_inputs(wl, seed=13)
+    pool = gg.gpu_build(wl, cfg, g)
+    ref_sel, ref_out, ref_lse = gg.gpu_decode_step(wl, cfg, g, pool)
+    kh, kdev = gg.host_pool(data["k_pool"])
+    vh, vdev = gg.host_pool(data["v_pool"])
+    gh = dict(g, k_pool=kdev, v_pool=vdev)
+    sel, out, lse = gg.gpu_decode_step(wl, cfg, gh, pool)
+    out2, lse2 = gg.gpu_decode(wl, cfg, gh, ref_sel)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, ref_sel)
+    assert torch.equal(out.view(torch.uint16), ref_out.view(torch.uint16))
+    assert torch.equal(lse, ref_lse)
+    assert torch.equal(out2.view(torch.uint16), ref_out.view(torch.uint16))
+    del kh, vh
+
+
+# --------------------------------------------------------------------------
 # the whole-model step at its full size: 32 layers x 16 sequences of ~64K
 # tokens (all layers' K/V in one ~138 GB pool, block offsets past 4 GiB),
 # r = 4, k = 32, with the builds of completing pages interleaved; sampled
