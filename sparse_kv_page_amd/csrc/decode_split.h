@@ -73,7 +73,12 @@ template <int D, int GQ>
 struct alignas(16) DecodeLds {
   float pbuf[kDecWaves][4][GQ][4];
   float abuf[kDecWaves][GQ];
-  float mo[kDecWaves][4][GQ][D];
+  // per wave: its current K tile (bf16, staged for the MFMA operand layout)
+  // while it streams, then its output partials for the workgroup merge
+  union alignas(16) WaveBuf {
+    float mo[4][GQ][D];
+    uint8_t kst[kDecTile * D * 2];
+  } wv[kDecWaves];
   float mm[kDecWaves][GQ];
   float ml[kDecWaves][GQ];
   int last_s;
@@ -93,7 +98,6 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
   constexpr int kColPasses = NC >= 16 ? NC / 16 : 1;  // d = 64: lanes with c >= 8 idle
   auto& pbuf = lds.pbuf;
   auto& abuf = lds.abuf;
-  auto& mo = lds.mo;
   auto& mm = lds.mm;
   auto& ml = lds.ml;
   int& last_s = lds.last_s;
@@ -161,15 +165,31 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
   // past the valid tokens reads the tile's first row) so that no load sits
   // inside a branch; K rows past ntok only reach S rows that are masked to
   // -inf, and V rows past ntok are zeroed below.
-  typename Q::Op ka[TPW][Q::kSteps];
+  // bf16: the K tile (16 rows of D) is loaded as contiguous 1 KiB blocks (lane
+  // l takes bytes 16 l .. 16 l + 15 of each) and rearranged through the
+  // wave's LDS buffer into the MFMA operand layout (lane (n, kg) needs row n);
+  // the 16-byte chunks of a row are XOR-swizzled by row so those reads are
+  // free of bank conflicts. fp32 K rows, and the two-tile variant (whose
+  // register budget is 128 and would spill the staging), load the operand
+  // layout straight into registers.
+  constexpr bool kLdsK = sizeof(T) == 2 && TPW >= 4;
+  constexpr int kRowBytes = D * 2;
+  auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  typename Q::Op ka[kLdsK ? 1 : TPW][Q::kSteps];
+  u32x4_t kraw[kLdsK ? TPW : 1][Q::kSteps];
   VRow<T> vr[TPW][kColPasses][4];
   const int cc = c_ok ? c : 0;
   auto load_tile = [&](int i) {
     const T* kt = kp + tile_off[i];
     const T* vt = vp + tile_off[i];
-    const int krow = n < ntok[i] ? n : 0;
+    if constexpr (kLdsK) {
 #pragma unroll
-    for (int s = 0; s < Q::kSteps; ++s) ka[i][s] = Q::load_nt(kt + (int64_t)krow * D + Q::off(s, kg));
+      for (int s = 0; s < Q::kSteps; ++s) kraw[i][s] = ld_nt4(kt + s * 512 + lane * 8);
+    } else {
+      const int krow = n < ntok[i] ? n : 0;
+#pragma unroll
+      for (int s = 0; s < Q::kSteps; ++s) ka[i][s] = Q::load_nt(kt + (int64_t)krow * D + Q::off(s, kg));
+    }
 #pragma unroll
     for (int cp = 0; cp < kColPasses; ++cp)
 #pragma unroll
@@ -205,9 +225,29 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
           if (!c_ok || 4 * tg + e >= ntok[i]) vr[i][cp][e].zero();
     }
     if (ntok[i] == 0) continue;
+    if constexpr (kLdsK) {
+      // rows past ntok hold other tokens' (or unused) keys; their logits are
+      // masked to -inf below
+      uint8_t* ks = lds.wv[wave].kst;
+#pragma unroll
+      for (int s = 0; s < Q::kSteps; ++s) {
+        const int e0 = s * 512 + lane * 8;
+        const int r = e0 / D;
+        *reinterpret_cast<u32x4_t*>(ks + r * kRowBytes + (((e0 % D) / 8) ^ kswz(r)) * 16) = kraw[i][s];
+      }
+      wave_lds_sync();
+    }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < Q::kSteps; ++s) acc = Q::mfma(ka[i][s], qb[s], acc);
+    for (int s = 0; s < Q::kSteps; ++s) {
+      if constexpr (kLdsK) {
+        const typename Q::Op kop = *reinterpret_cast<const typename Q::Op*>(
+            lds.wv[wave].kst + n * kRowBytes + ((4 * s + kg) ^ kswz(n)) * 16);
+        acc = Q::mfma(kop, qb[s], acc);
+      } else {
+        acc = Q::mfma(ka[i][s], qb[s], acc);
+      }
+    }
     // lane holds S[token 4 kg + e][head n]
     float z[4];
     float mt = -INFINITY;
@@ -261,7 +301,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
     for (int cp = 0; cp < kColPasses; ++cp)
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float* dst = &mo[wave][tg][g][(cp * 16 + c) * 8];
+        float* dst = &lds.wv[wave].mo[tg][g][(cp * 16 + c) * 8];
         *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{o[cp][g][0], o[cp][g][1], o[cp][g][2], o[cp][g][3]};
         *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{o[cp][g][4], o[cp][g][5], o[cp][g][6], o[cp][g][7]};
       }
@@ -290,7 +330,8 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
       for (int w = 0; w < kDecWaves; ++w) {
         const float cw = exp2_fast(mm[w][g] - M);
         L = fmaf(cw, ml[w][g], L);
-        O = fmaf(cw, (mo[w][0][g][e] + mo[w][1][g][e]) + (mo[w][2][g][e] + mo[w][3][g][e]), O);
+        const auto& mw = lds.wv[w].mo;
+        O = fmaf(cw, (mw[0][g][e] + mw[1][g][e]) + (mw[2][g][e] + mw[3][g][e]), O);
       }
     }
     __hip_atomic_store(&part_o[x], L > 0.f ? O / L : 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

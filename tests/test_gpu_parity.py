@@ -179,8 +179,12 @@ def test_score_select_ties_go_to_lower_page():
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("wl", [TINY, E2E, W32K], ids=["tiny_f32", "e2e_bf16", "llama8b_32k"])
 def test_sparse_decode_parity(wl):
+    _decode_parity(wl)
+
+
+def _decode_parity(wl):
     cfg = _cfg(wl)
-    data, g = gg.make_inputs(wl, seed=3)
+    data, g = gg.make_inputs(wl, seed=3, gen_device=gg.DEV if wl.batch * wl.num_kv_heads > 64 else "cpu")
     rng = np.random.default_rng(3)
     k = wl.budget_pages
     sel = np.full((wl.batch, wl.num_kv_heads, k), -1, dtype=np.int32)
@@ -204,6 +208,18 @@ def test_sparse_decode_parity(wl):
             worst_l = max(worst_l, gg.mixed_violation(lse[b, sl], l_ref))
     assert worst_o <= gg.out_tol(wl), worst_o
     assert worst_l <= 1.0, worst_l
+
+
+@pytest.mark.parametrize("d,G,P", [(128, 4, 64), (64, 4, 16), (128, 8, 32), (64, 1, 64), (128, 2, 16)],
+                         ids=["d128-g4-p64", "d64-g4-p16", "d128-g8-p32", "d64-g1-p64", "d128-g2-p16"])
+def test_sparse_decode_four_tile_workgroups(d, G, P):
+    """Grids of at least 256 workgroups take four 16-token tiles per wave (K
+    staged through LDS); 256 (sequence, KV head) units with ragged lengths,
+    partial current pages and J <= k units, against the oracle."""
+    B, Hkv, k = 32, 8, 8
+    lens = tuple(P * (3 + (7 * b) % 37) + (b * 5) % P for b in range(B))
+    wl = synth.Workload(f"four_tile_d{d}_g{G}_p{P}", B, Hkv, G, d, P, lens, 2, k, "bf16", "bf16")
+    _decode_parity(wl)
 
 
 def test_full_budget_decode_is_dense():
