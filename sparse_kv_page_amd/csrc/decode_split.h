@@ -9,8 +9,12 @@ namespace locks {
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kDecTile = 16;
-// 16-token tiles per wave: 4 (8 pages of 64 per 8-wave workgroup) when the
-// grid still holds a workgroup per CU, else 2 (more, smaller splits)
+// 16-token tiles per wave: 8 (16 pages of 64 per 8-wave workgroup) or 4
+// (8 pages) when the grid still holds a workgroup per CU, else 2 (more,
+// smaller splits). The largest that fills the chip is taken: fewer, longer
+// workgroups keep fewer loads in flight per CU, which the scattered tiles are
+// served faster with.
+constexpr int kDecTilesPerWaveXL = 8;
 constexpr int kDecTilesPerWaveLarge = 4;
 constexpr int kDecTilesPerWaveSmall = 2;
 // tiles whose K/V loads a wave keeps in flight: one (the next tile's loads go

@@ -37,14 +37,16 @@ int decode_pages_per_split(int page_size, int tiles_per_wave) {
   return kDecWaves * tiles_per_wave * kDecTile / page_size;
 }
 
-// Four tiles per wave halve the splits (a shorter merge) while the grid
-// still holds at least 256 workgroups (one per CU); smaller grids and fp32
-// (whose four-tile kernel spills) keep two.
+// Eight or four tiles per wave cut the splits (a shorter merge, fewer loads
+// in flight per CU) while the grid still holds at least 256 workgroups (one
+// per CU); smaller grids and fp32 (whose larger kernels spill) keep two.
 int decode_tiles_per_wave(int64_t units, int k, int page_size, bool f32) {
   if (f32) return kDecTilesPerWaveSmall;
-  const int pps = decode_pages_per_split(page_size, kDecTilesPerWaveLarge);
-  const int64_t wgs = units * ((k + pps - 1) / pps);
-  return wgs >= 256 ? kDecTilesPerWaveLarge : kDecTilesPerWaveSmall;
+  for (int tpw : {kDecTilesPerWaveXL, kDecTilesPerWaveLarge}) {
+    const int pps = decode_pages_per_split(page_size, tpw);
+    if (units * ((k + pps - 1) / pps) >= 256) return tpw;
+  }
+  return kDecTilesPerWaveSmall;
 }
 
 int decode_max_splits(int k, int page_size) {
@@ -54,9 +56,13 @@ int decode_max_splits(int k, int page_size) {
 
 namespace {
 template <typename T, int D, int G>
-void launch_tpw(const DecodeArgs& a, dim3 grid, hipStream_t stream, bool large) {
+void launch_tpw(const DecodeArgs& a, dim3 grid, hipStream_t stream, int tpw) {
   if constexpr (sizeof(T) == 2) {
-    if (large) {
+    if (tpw == kDecTilesPerWaveXL) {
+      hipLaunchKernelGGL((sparse_decode_kernel<T, D, G, kDecTilesPerWaveXL>), grid, dim3(kDecThreads), 0, stream, a);
+      return;
+    }
+    if (tpw == kDecTilesPerWaveLarge) {
       hipLaunchKernelGGL((sparse_decode_kernel<T, D, G, kDecTilesPerWaveLarge>), grid, dim3(kDecThreads), 0, stream, a);
       return;
     }
@@ -67,8 +73,9 @@ void launch_tpw(const DecodeArgs& a, dim3 grid, hipStream_t stream, bool large) 
 
 hipError_t launch_sparse_decode(const DecodeArgs& a, int dtype, int D, int batch, hipStream_t stream) {
   dim3 grid(a.splits, a.Hkv, batch);
-  const bool large = dtype == 0 && a.pages_per_split * a.P == kDecWaves * kDecTilesPerWaveLarge * kDecTile;
-#define LAUNCH(T, DD, GG) launch_tpw<T, DD, GG>(a, grid, stream, large)
+  // tiles per wave of the host's split plan (pages_per_split = waves * tiles * 16 / P)
+  const int tpw = dtype == 0 ? a.pages_per_split * a.P / (kDecWaves * kDecTile) : kDecTilesPerWaveSmall;
+#define LAUNCH(T, DD, GG) launch_tpw<T, DD, GG>(a, grid, stream, tpw)
 #define LAUNCH_G(T, DD)                  \
   switch (a.G) {                         \
     case 1: LAUNCH(T, DD, 1); break;     \

@@ -212,13 +212,16 @@ def _decode_parity(wl):
 
 @pytest.mark.parametrize("d,G,P", [(128, 4, 64), (64, 4, 16), (128, 8, 32), (64, 1, 64), (128, 2, 16)],
                          ids=["d128-g4-p64", "d64-g4-p16", "d128-g8-p32", "d64-g1-p64", "d128-g2-p16"])
-def test_sparse_decode_four_tile_workgroups(d, G, P):
-    """Grids of at least 256 workgroups take four 16-token tiles per wave (K
-    staged through LDS); 256 (sequence, KV head) units with ragged lengths,
-    partial current pages and J <= k units, against the oracle."""
-    B, Hkv, k = 32, 8, 8
+@pytest.mark.parametrize("tiles", [8, 4], ids=["eight-tile", "four-tile"])
+def test_sparse_decode_large_workgroups(d, G, P, tiles):
+    """Grids of at least 256 workgroups take eight or four 16-token tiles per
+    wave (K staged through LDS): 256 units at k = 8 pages give eight, 128
+    units at k = 1024 / P pages four. Ragged lengths, partial current pages
+    and J <= k units, against the oracle."""
+    Hkv = 8
+    B, k = (32, 8) if tiles == 8 else (16, 1024 // P)
     lens = tuple(P * (3 + (7 * b) % 37) + (b * 5) % P for b in range(B))
-    wl = synth.Workload(f"four_tile_d{d}_g{G}_p{P}", B, Hkv, G, d, P, lens, 2, k, "bf16", "bf16")
+    wl = synth.Workload(f"large_wg_d{d}_g{G}_p{P}_t{tiles}", B, Hkv, G, d, P, lens, 2, k, "bf16", "bf16")
     _decode_parity(wl)
 
 
