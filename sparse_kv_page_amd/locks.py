@@ -105,10 +105,21 @@ def _check(fn: str, st: int) -> None:
 
 
 def _ptr(t):
+    """Device address of a tensor (ints pass through as raw device addresses).
+
+    The kernels index every buffer as dense row-major memory on the GPU, so a
+    tensor in host memory or a strided view is refused here rather than read
+    as the wrong bytes (or as an address the GPU cannot reach)."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"expected a GPU tensor, got one on {t.device}; pass host-resident "
+                         "buffers as their mapped device address (an int)")
+    if not t.is_contiguous():
+        raise ValueError(f"expected a contiguous tensor, got strides {t.stride()} "
+                         f"for shape {tuple(t.shape)}")
     return t.data_ptr()
 
 

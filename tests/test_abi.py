@@ -226,3 +226,13 @@ def test_workspace_monotone_and_empty_calls():
                           stream=0)
     L.locks_decode_step(cfg, None, None, None, None, 0, None, None, 0, 0, None, None, None, None, 0,
                         stream=0)
+
+
+def test_binding_refuses_host_tensors():
+    """A tensor in host memory is refused before the call: its address would
+    reach a kernel as a device pointer."""
+    import torch
+    cfg = _cfg()
+    fake = 1 << 20
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L.locks_select_pages(cfg, torch.zeros(4), fake, 1, 4, fake, fake, stream=0)
