@@ -357,48 +357,56 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
   const float* pl = a.part_lse + unit * splits * (int64_t)G;
   // every output of this thread (kNx of them) and splits in chunks of
   // kMergeChunk: all loads of a chunk are issued before any is used, then the
-  // chunk is folded into a running (M, L, O) per output
-  constexpr int kMergeChunk = 16;
+  // chunk is folded into a running (M, L, O) per output. Up to 4 splits take
+  // one chunk of 4 (no clamped duplicate loads); with one chunk either way
+  // the fold is the same arithmetic.
   constexpr int kNx = (G * D + kDecThreads - 1) / kDecThreads;
   float M[kNx], L[kNx], O[kNx];
 #pragma unroll
   for (int xi = 0; xi < kNx; ++xi) { M[xi] = -INFINITY; L[xi] = 0.f; O[xi] = 0.f; }
-  for (int s0 = 0; s0 < splits; s0 += kMergeChunk) {
-    float ls[kNx][kMergeChunk], ov[kNx][kMergeChunk];
+  auto merge = [&](auto chunk) {
+    constexpr int kMergeChunk = decltype(chunk)::value;
+    for (int s0 = 0; s0 < splits; s0 += kMergeChunk) {
+      float ls[kNx][kMergeChunk], ov[kNx][kMergeChunk];
 #pragma unroll
-    for (int xi = 0; xi < kNx; ++xi) {
-      const int x = threadIdx.x + kDecThreads * xi;
-      const int xc = x < G * D ? x : 0;
-      const int g = xc / D;
-#pragma unroll
-      for (int i = 0; i < kMergeChunk; ++i) {
-        const int sp = s0 + i < splits ? s0 + i : splits - 1;
-        ls[xi][i] = __hip_atomic_load(&pl[sp * G + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ov[xi][i] = __hip_atomic_load(&po[(int64_t)sp * G * D + xc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-#pragma unroll
-    for (int xi = 0; xi < kNx; ++xi) {
-      float Mc = M[xi];
-#pragma unroll
-      for (int i = 0; i < kMergeChunk; ++i)
-        if (s0 + i < splits) Mc = fmaxf(Mc, ls[xi][i]);
-      if (Mc > -INFINITY) {
-        const float r = exp2_fast((M[xi] - Mc) * kLog2e);  // M = -inf -> 0
-        L[xi] *= r;
-        O[xi] *= r;
+      for (int xi = 0; xi < kNx; ++xi) {
+        const int x = threadIdx.x + kDecThreads * xi;
+        const int xc = x < G * D ? x : 0;
+        const int g = xc / D;
 #pragma unroll
         for (int i = 0; i < kMergeChunk; ++i) {
-          if (s0 + i < splits && ls[xi][i] > -INFINITY) {
-            const float cw = exp2_fast((ls[xi][i] - Mc) * kLog2e);
-            L[xi] += cw;
-            O[xi] = fmaf(cw, ov[xi][i], O[xi]);
-          }
+          const int sp = s0 + i < splits ? s0 + i : splits - 1;
+          ls[xi][i] = __hip_atomic_load(&pl[sp * G + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ov[xi][i] = __hip_atomic_load(&po[(int64_t)sp * G * D + xc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        M[xi] = Mc;
+      }
+#pragma unroll
+      for (int xi = 0; xi < kNx; ++xi) {
+        float Mc = M[xi];
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i)
+          if (s0 + i < splits) Mc = fmaxf(Mc, ls[xi][i]);
+        if (Mc > -INFINITY) {
+          const float r = exp2_fast((M[xi] - Mc) * kLog2e);  // M = -inf -> 0
+          L[xi] *= r;
+          O[xi] *= r;
+#pragma unroll
+          for (int i = 0; i < kMergeChunk; ++i) {
+            if (s0 + i < splits && ls[xi][i] > -INFINITY) {
+              const float cw = exp2_fast((ls[xi][i] - Mc) * kLog2e);
+              L[xi] += cw;
+              O[xi] = fmaf(cw, ov[xi][i], O[xi]);
+            }
+          }
+          M[xi] = Mc;
+        }
       }
     }
-  }
+  };
+  if (splits <= 4)
+    merge(std::integral_constant<int, 4>{});
+  else
+    merge(std::integral_constant<int, 16>{});
   T* out = reinterpret_cast<T*>(a.out) + ((int64_t)b * Hq + (int64_t)h * G) * D;
 #pragma unroll
   for (int xi = 0; xi < kNx; ++xi) {
