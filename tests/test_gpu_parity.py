@@ -225,6 +225,21 @@ def test_sparse_decode_large_workgroups(d, G, P, tiles):
     _decode_parity(wl)
 
 
+@pytest.mark.parametrize("k", [8, 32, 40, 136, 264],
+                         ids=["2-splits", "4-splits", "5-splits", "9-splits", "17-splits"])
+def test_sparse_decode_split_merge_runs(k):
+    """The last workgroup of a unit folds the split partials in runs of 4
+    loads when a unit has at most 4 splits, else in runs of 16. At batch 8
+    with 8 KV heads and 64-token pages the budgets give 2 splits (two tiles
+    per wave), 4 and 5 splits (four tiles per wave), 9 splits (eight tiles
+    per wave: one run of 16, 7 loads past the end) and 17 splits (two runs,
+    the second mostly past the end). One short sequence has J <= k."""
+    B, Hkv, G, d, P = 8, 8, 4, 128, 64
+    lens = tuple(P * (k + 3 + (7 * b) % 29) + (b * 5) % P for b in range(B - 1)) + (P * 3 + 17,)
+    wl = synth.Workload(f"split_runs_k{k}", B, Hkv, G, d, P, lens, 2, k, "bf16", "bf16")
+    _decode_parity(wl)
+
+
 def test_full_budget_decode_is_dense():
     """k >= J: every page is selected and the result is dense decode attention."""
     wl = E2E.with_(budget_pages=64)
