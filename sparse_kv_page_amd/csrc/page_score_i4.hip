@@ -32,8 +32,13 @@
 
 namespace locks {
 
-constexpr int kI4MaxPpw = 64;        // pages per wave (block ids in one VGPR; 128 measured slower:
-                                      // the larger score staging leaves fewer ring slots)
+// Pages per wave, at most. A 128K-context batch of 8 has 32 per wave in one
+// resident round at 64-token pages; 16-token pages then run four rounds,
+// and the later rounds' workgroups go to whichever CUs free up first, which
+// evens out the tail: measured faster than two rounds of 64 (by 7.5 us at
+// rank 4, level at rank 8), than one round of 128 (block ids in two VGPRs)
+// and than eight rounds of 16.
+constexpr int kI4MaxPpw = 32;
 constexpr int kI4Budget = 40 * 1024;  // LDS bytes per workgroup: 4 workgroups per CU
 constexpr int kI4PagesPerIter = kScorePagesPerIter;  // at most this many pages scored together
 constexpr int kI4MaxNs = 8;           // ring slots per wave
@@ -464,7 +469,8 @@ hipError_t launch_i4(ScoreArgs a, int batch, hipStream_t stream) {
     waves = cus * blocks * kScoreWaves;
     cached.store(waves, std::memory_order_relaxed);
   }
-  // pages per wave for one round of resident waves, at most kI4MaxPpw
+  // pages per wave for one round of resident waves, at most kI4MaxPpw (then
+  // several rounds)
   const int64_t total = (int64_t)batch * a.Hkv * a.max_pages;
   int64_t ppw = (total + waves - 1) / waves;
   ppw = ppw < 1 ? 1 : (ppw > kI4MaxPpw ? kI4MaxPpw : ppw);
