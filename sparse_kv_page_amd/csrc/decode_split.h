@@ -357,9 +357,9 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
   const float* pl = a.part_lse + unit * splits * (int64_t)G;
   // every output of this thread (kNx of them) and splits in chunks of
   // kMergeChunk: all loads of a chunk are issued before any is used, then the
-  // chunk is folded into a running (M, L, O) per output. Up to 4 splits take
-  // one chunk of 4 (no clamped duplicate loads); with one chunk either way
-  // the fold is the same arithmetic.
+  // chunk is folded into a running (M, L, O) per output. Up to 4 or 8 splits
+  // take one chunk of 4 or 8 (no clamped duplicate loads); with one chunk
+  // either way the fold is the same arithmetic.
   constexpr int kNx = (G * D + kDecThreads - 1) / kDecThreads;
   float M[kNx], L[kNx], O[kNx];
 #pragma unroll
@@ -405,6 +405,8 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
   };
   if (splits <= 4)
     merge(std::integral_constant<int, 4>{});
+  else if (splits <= 8)
+    merge(std::integral_constant<int, 8>{});
   else
     merge(std::integral_constant<int, 16>{});
   T* out = reinterpret_cast<T*>(a.out) + ((int64_t)b * Hq + (int64_t)h * G) * D;
