@@ -177,6 +177,60 @@ locks::DecodeArgs decode_args(const locks_config_t* cfg, const void* q, const vo
   return a;
 }
 
+// score -> select on a checked workspace
+int enqueue_score_select(const locks_config_t* cfg, const void* q, const void* summary_pool, int64_t num_blocks,
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t batch, int32_t max_pages,
+                         int32_t* selected, void* ws, size_t ws_bytes, hipStream_t stream) {
+  uint8_t* region = scratch_base(ws, ws_bytes, score_ws_bytes(cfg, batch, max_pages) - ctl_bytes(cfg, batch));
+  float* scores = reinterpret_cast<float*>(region);
+  float* sigma = reinterpret_cast<float*>(region +
+                                          align_up((size_t)batch * cfg->num_q_heads * max_pages * sizeof(float)));
+  locks::ScoreArgs sa = score_args(cfg, q, summary_pool, num_blocks, block_table, seq_lens, max_pages, scores);
+  const hipError_t e = cfg->summary_dtype == LOCKS_I4
+                           ? locks::launch_page_score_i4(sa, cfg->head_dim, batch, stream)
+                           : locks::launch_page_score(sa, cfg->kv_dtype, cfg->head_dim, batch, stream);
+  if (e != hipSuccess) return LOCKS_E_HIP;
+  locks::SelectArgs a = select_args(cfg, scores, seq_lens, max_pages, selected, sigma);
+  return hip_status(locks::launch_select(a, batch, stream));
+}
+
+// split-K decode on a checked workspace (arrival counters at its front)
+int enqueue_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_pool, const void* v_pool,
+                          int64_t num_blocks, const int32_t* block_table, const int32_t* seq_lens,
+                          const int32_t* selected, int32_t batch, int32_t max_pages, void* out, float* lse, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  // partial rows laid out for the most splits any batch uses (the workspace layout)
+  const size_t rows = (size_t)batch * cfg->num_q_heads * locks::decode_max_splits(cfg->budget_pages, cfg->page_size);
+  uint8_t* region = scratch_base(ws, ws_bytes, decode_ws_bytes(cfg, batch) - ctl_bytes(cfg, batch));
+  locks::DecodeArgs a = decode_args(cfg, q, k_pool, v_pool, num_blocks, block_table, seq_lens, selected,
+                                    batch, max_pages, out, lse, static_cast<int32_t*>(ws),
+                                    reinterpret_cast<float*>(region),
+                                    reinterpret_cast<float*>(region + align_up(rows * cfg->head_dim * sizeof(float))));
+  return hip_status(locks::launch_sparse_decode(a, cfg->kv_dtype, cfg->head_dim, batch, stream));
+}
+
+size_t step_ws_bytes(const locks_config_t* cfg, int32_t batch, int32_t max_pages) {
+  const size_t a = score_ws_bytes(cfg, batch, max_pages);
+  const size_t b = decode_ws_bytes(cfg, batch);
+  return a > b ? a : b;
+}
+
+// argument checks shared by the two whole-step entry points
+int check_step(const locks_config_t* cfg, const void* q, const void* summary_pool, const void* k_pool,
+               const void* v_pool, int64_t num_blocks, const int32_t* block_table, const int32_t* seq_lens,
+               int32_t batch, int32_t max_pages, const int32_t* selected, const void* out) {
+  int st = check_config(cfg);
+  if (st != LOCKS_OK) return st;
+  st = check_batch(batch, max_pages);
+  if (st != LOCKS_OK) return st;
+  if (num_blocks < 0) return LOCKS_E_INVALID_ARG;
+  if (batch == 0) return LOCKS_OK;
+  if (num_blocks == 0) return LOCKS_E_INVALID_ARG;  // an empty pool cannot be read
+  if (!q || !summary_pool || !k_pool || !v_pool || !block_table || !seq_lens || !selected || !out)
+    return LOCKS_E_INVALID_ARG;
+  return LOCKS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -205,9 +259,7 @@ int locks_workspace_size(const locks_config_t* cfg, int32_t batch, int32_t max_p
   if (!bytes) return LOCKS_E_INVALID_ARG;
   st = check_batch(batch, max_pages);
   if (st != LOCKS_OK) return st;
-  const size_t a = score_ws_bytes(cfg, batch, max_pages);
-  const size_t b = decode_ws_bytes(cfg, batch);
-  *bytes = a > b ? a : b;
+  *bytes = step_ws_bytes(cfg, batch, max_pages);
   return LOCKS_OK;
 }
 
@@ -276,14 +328,8 @@ int locks_score_select(const locks_config_t* cfg, const void* q, const void* sum
   if (num_blocks == 0) return LOCKS_E_INVALID_ARG;  // an empty pool cannot be read
   if (!q || !summary_pool || !block_table || !seq_lens || !selected) return LOCKS_E_INVALID_ARG;
   if (!ws || ws_bytes < score_ws_bytes(cfg, batch, max_pages)) return LOCKS_E_WORKSPACE;
-  uint8_t* region = scratch_base(ws, ws_bytes, score_ws_bytes(cfg, batch, max_pages) - ctl_bytes(cfg, batch));
-  float* scores = reinterpret_cast<float*>(region);
-  float* sigma = reinterpret_cast<float*>(region +
-                                          align_up((size_t)batch * cfg->num_q_heads * max_pages * sizeof(float)));
-  st = locks_page_score(cfg, q, summary_pool, num_blocks, block_table, seq_lens, batch, max_pages,
-                        scores, stream);
-  if (st != LOCKS_OK) return st;
-  return locks_select_pages(cfg, scores, seq_lens, batch, max_pages, selected, sigma, stream);
+  return enqueue_score_select(cfg, q, summary_pool, num_blocks, block_table, seq_lens, batch, max_pages, selected,
+                              ws, ws_bytes, stream);
 }
 
 int locks_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_pool,
@@ -301,38 +347,25 @@ int locks_sparse_decode(const locks_config_t* cfg, const void* q, const void* k_
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !selected || !out)
     return LOCKS_E_INVALID_ARG;
   if (!ws || ws_bytes < decode_ws_bytes(cfg, batch)) return LOCKS_E_WORKSPACE;
-  // partial rows laid out for the most splits any batch uses (the workspace layout)
-  const size_t rows = (size_t)batch * cfg->num_q_heads * locks::decode_max_splits(cfg->budget_pages, cfg->page_size);
-  uint8_t* region = scratch_base(ws, ws_bytes, decode_ws_bytes(cfg, batch) - ctl_bytes(cfg, batch));
-  locks::DecodeArgs a = decode_args(cfg, q, k_pool, v_pool, num_blocks, block_table, seq_lens, selected,
-                                    batch, max_pages, out, lse, static_cast<int32_t*>(ws),
-                                    reinterpret_cast<float*>(region),
-                                    reinterpret_cast<float*>(region + align_up(rows * cfg->head_dim * sizeof(float))));
-  return hip_status(locks::launch_sparse_decode(a, cfg->kv_dtype, cfg->head_dim, batch, stream));
+  return enqueue_sparse_decode(cfg, q, k_pool, v_pool, num_blocks, block_table, seq_lens, selected, batch,
+                               max_pages, out, lse, ws, ws_bytes, stream);
 }
 
 int locks_decode_step(const locks_config_t* cfg, const void* q, const void* summary_pool, const void* k_pool,
                       const void* v_pool, int64_t num_blocks, const int32_t* block_table,
                       const int32_t* seq_lens, int32_t batch, int32_t max_pages, int32_t* selected,
                       void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = check_config(cfg);
-  if (st != LOCKS_OK) return st;
-  st = check_batch(batch, max_pages);
-  if (st != LOCKS_OK) return st;
-  if (num_blocks < 0) return LOCKS_E_INVALID_ARG;
-  if (batch == 0) return LOCKS_OK;
-  if (num_blocks == 0) return LOCKS_E_INVALID_ARG;  // an empty pool cannot be read
-  if (!q || !summary_pool || !k_pool || !v_pool || !block_table || !seq_lens || !selected || !out)
-    return LOCKS_E_INVALID_ARG;
-  if (!ws || ws_bytes < score_ws_bytes(cfg, batch, max_pages) || ws_bytes < decode_ws_bytes(cfg, batch))
-    return LOCKS_E_WORKSPACE;
+  int st = check_step(cfg, q, summary_pool, k_pool, v_pool, num_blocks, block_table, seq_lens, batch, max_pages,
+                      selected, out);
+  if (st != LOCKS_OK || batch == 0) return st;
+  if (!ws || ws_bytes < step_ws_bytes(cfg, batch, max_pages)) return LOCKS_E_WORKSPACE;
   // the head scores and page keys of the first call are consumed before the
   // second call's partials overwrite them (same stream)
-  st = locks_score_select(cfg, q, summary_pool, num_blocks, block_table, seq_lens, batch, max_pages, selected,
-                          ws, ws_bytes, stream);
+  st = enqueue_score_select(cfg, q, summary_pool, num_blocks, block_table, seq_lens, batch, max_pages, selected, ws,
+                            ws_bytes, stream);
   if (st != LOCKS_OK) return st;
-  return locks_sparse_decode(cfg, q, k_pool, v_pool, num_blocks, block_table, seq_lens, selected, batch,
-                             max_pages, out, lse, ws, ws_bytes, stream);
+  return enqueue_sparse_decode(cfg, q, k_pool, v_pool, num_blocks, block_table, seq_lens, selected, batch,
+                               max_pages, out, lse, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

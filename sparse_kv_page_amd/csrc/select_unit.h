@@ -288,7 +288,7 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   // common bits above `hi` (taken from the largest key)
   uint64_t prefix = (((uint64_t)kmax << idb) >> hi) << hi;
   int kr = K;
-  const bool take_all = K >= ncand;  // every candidate fits
+  const bool take_all = K == 0 || K >= ncand;  // nothing to rank: none wanted, or every candidate fits
   int cur = 0;
   while (!take_all && hi > 0) {
     const int lo = hi > kSelDigit ? hi - kSelDigit : 0;

@@ -130,6 +130,26 @@ def test_select_ties_go_to_lower_page():
     assert sel2[0, 0].tolist() == [0, 1, 2, 3, 4, 39]
 
 
+@pytest.mark.parametrize("lens", [(64 * 40 + 7, 64 * 3, 64 * 2, 17), (64 * 2000, 64 * 1 + 1, 64 * 300, 0)],
+                         ids=["short", "long"])
+def test_select_budget_of_two_pages(lens):
+    """k = 2 leaves no free slot: only the sink and the current page are kept
+    (and J <= 2 keeps every page), whatever the scores."""
+    wl = E2E.with_(batch=len(lens), seq_lens=lens, budget_pages=2, extra_blocks=0)
+    cfg = _cfg(wl)
+    gen = torch.Generator().manual_seed(57)
+    hs = (torch.randn((wl.batch, wl.num_q_heads, wl.max_pages), generator=gen) * 3).float()
+    g = {"seq_lens": torch.tensor(list(lens), dtype=torch.int32, device=gg.DEV)}
+    sel, _ = gg.gpu_select(wl, cfg, g, hs.to(gg.DEV))
+    torch.cuda.synchronize()
+    for b in range(wl.batch):
+        _, J, Jc = gg.lens(wl, b)
+        sel_o, sigma_o = gg.oracle_unit_select(wl, b, hs[b, :, :Jc].double().numpy())
+        assert sel_o.tolist() == ([0, J - 1] if J > 2 else [j if j < J else -1 for j in range(2)])
+        for h in range(wl.num_kv_heads):
+            assert sel[b, h].tolist() == sel_o.tolist()
+
+
 def _record_pool(wl, cfg, g, page_mu_weight):
     """bf16 summary pool whose record of logical page j has V = 0, C = 0 and
     mu = page_mu_weight[j] * (mean query of the group), so a page's score is
