@@ -113,7 +113,7 @@ def quantize_summaries(mu, vt, coef):
 
     One symmetric scale per basis vector (4-bit codes in [-7, 7]), per token's
     coefficient row and for the centroid (8-bit codes in [-127, 127]); scale =
-    bf16(max|x| / L), code = round-half-even(x / scale), decided in fp32."""
+    bf16(max|x| / L), code = round-half-even(x / scale), in double precision."""
     mu = _f64(mu); vt = _f64(vt); coef = _f64(coef)
     n, r, d = vt.shape
     P = coef.shape[1]

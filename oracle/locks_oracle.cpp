@@ -346,26 +346,24 @@ int lo_attend(int G, int d, int n_tok, const double* q, const double* keys,
 //   * scale = bf16(max|x| / L) with L = 7 (4-bit) or 127 (8-bit), code =
 //     round-half-even(x / scale), clamped to [-L, L]; a group of zeros has
 //     scale 0 and codes 0;
-//   * the code is an integer decided by floating point, so it is decided in
-//     fp32, the precision of the GPU build: x is first rounded to fp32 and the
-//     maximum, the division by L and the division by the scale are fp32
-//     operations (each correctly rounded).
+//   * every step in double precision like the rest of this file: the maximum,
+//     the division by L (then one rounding to bf16) and the division by the
+//     scale. For values held in fp32 or below, the double quotient x / scale
+//     sits on a half-integer only when the exact quotient does, so the
+//     round-half-even decision is the exact one.
 // The three parts are quantized independently from the full-precision fit.
 static void quantize_group(const double* x, long n, long stride, int L, int* code, long cstride,
                            double* scale) {
-  float amax = 0.0f;
-  for (long i = 0; i < n; ++i) amax = std::max(amax, std::fabs((float)x[i * stride]));
-  const float s32 = amax / (float)L;
+  double amax = 0.0;
+  for (long i = 0; i < n; ++i) amax = std::max(amax, std::fabs(x[i * stride]));
+  const double s64 = amax / (double)L;
   double sb = 0.0;
-  const double s64 = (double)s32;
   lo_round_bf16(&s64, 1, &sb);
   *scale = sb;
-  const float sf = (float)sb;  // a bf16 value, exact in fp32
   for (long i = 0; i < n; ++i) {
     int c = 0;
-    if (sf > 0.0f) {
-      const float t = (float)x[i * stride] / sf;
-      c = (int)std::nearbyint(t);  // ties to even in the default rounding mode
+    if (sb > 0.0) {
+      c = (int)std::nearbyint(x[i * stride] / sb);  // ties to even in the default rounding mode
       c = std::min(L, std::max(-L, c));
     }
     code[i * cstride] = c;

@@ -364,6 +364,51 @@ def test_decode_step_full_budget_is_dense():
         assert res[(0, h)]["sel"].tolist() == list(range(J))
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_step_over_budget_selects_exact_set_at_full_rank(seed):
+    """The J > k branch of the whole step ([Locks] §2 budget and mandatory
+    pages, §4 share-average selection, Thm. 1 (i)): summaries gathered through
+    a shuffled block table, scored, combined, selected and attended with a
+    partial current page. With full-rank summaries (r = P - 1 spans every
+    centred page) the selection must be the exact-LSE page set and the output
+    softmax attention over those pages' valid tokens, both computed here from
+    the keys with numpy and scipy."""
+    rng = np.random.default_rng(100 + seed)
+    B, Hkv, G, d, P, k, scale = 3, 2, 3, 16, 8, 6, 0.3
+    lens = [P * 20 + 3, P * 14, P * 9 + 7]  # partial, complete and partial current pages
+    maxp = max(-(-T // P) for T in lens)
+    nblk = B * maxp + 4
+    bt = rng.permutation(nblk)[:B * maxp].reshape(B, maxp)
+    keys = rng.standard_normal((nblk, Hkv, P, d)) * 0.7
+    vals = rng.standard_normal((nblk, Hkv, P, d))
+    q = rng.standard_normal((B, Hkv * G, d))
+    for b, T in enumerate(lens):  # slots past T hold a poison value
+        if T % P:
+            keys[bt[b, T // P], :, T % P:] = 100.0
+            vals[bt[b, T // P], :, T % P:] = 100.0
+    mu, vt, cf, _, _ = oracle.build_pages(keys.reshape(-1, P, d), P - 1)
+    res = oracle.decode_step(q, mu.reshape(nblk, Hkv, d), vt.reshape(nblk, Hkv, P - 1, d),
+                             cf.reshape(nblk, Hkv, P, P - 1), keys, vals, bt, lens, P, k, scale,
+                             threads=2)
+    for b, T in enumerate(lens):
+        J, Jc = -(-T // P), T // P
+        for h in range(Hkv):
+            qg = q[b, h * G:(h + 1) * G]
+            s = logsumexp(np.einsum("gd,jpd->gjp", qg, keys[bt[b, :Jc], h]) * scale, axis=2)
+            sigma = logsumexp(s - logsumexp(s, axis=1)[:, None], axis=0) - math.log(G)
+            cand = sorted((j for j in range(1, Jc) if j != J - 1), key=lambda j: (-sigma[j], j))
+            assert sigma[cand[k - 3]] - sigma[cand[k - 2]] > 1e-6  # no near-tie at the cut
+            want = sorted([0, J - 1] + cand[:k - 2])
+            assert res[(b, h)]["sel"].tolist() == want
+            kk = np.concatenate([keys[bt[b, j], h, :min(P, T - j * P)] for j in want])
+            vv = np.concatenate([vals[bt[b, j], h, :min(P, T - j * P)] for j in want])
+            z = qg @ kk.T * scale
+            lse = logsumexp(z, axis=1)
+            o = np.exp(z - lse[:, None]) @ vv
+            np.testing.assert_allclose(res[(b, h)]["out"], o, atol=1e-12)
+            np.testing.assert_allclose(res[(b, h)]["lse"], lse, atol=1e-12)
+
+
 # --------------------------------------------------------------------------
 # bf16 storage rounding (summaries are stored in bf16, [Locks] §4 storage)
 # --------------------------------------------------------------------------
