@@ -23,18 +23,20 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
 METRIC = "decode-step score+select+sparse-attn µs and % HBM roofline, 128K ctx, batch 8"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+N_QUERY_SETS = 8  # query sets rotated through timed steps (default of --query-sets)
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=192, help="timed steps, in three windows")
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama8b_128k_b8")
     ap.add_argument("--rank", type=int, default=None)
@@ -45,8 +47,11 @@ def parse():
     ap.add_argument("--kv-host", action="store_true",
                     help="hold the K/V pools in pinned host memory: the decode reads the selected pages "
                          "over the host link (the summaries stay in HBM)")
+    ap.add_argument("--query-sets", type=int, default=N_QUERY_SETS,
+                    help="query sets rotated through the timed steps (1: every step repeats one query)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=24.0,
+                    help="CPU time of the oracle baseline (two legs of three runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run 3 plain device copies of MIB MiB "
                          "(reference dispatches for scaling memory counters)")
@@ -161,54 +166,90 @@ def main():
     scores = torch.empty((B, Hq, maxp), dtype=torch.float32, device=dev)
     sigma = torch.empty((B, Hkv, maxp), dtype=torch.float32, device=dev)
 
-    def score():
-        L.locks_page_score(cfg, q, pool, wl.num_blocks, bt, sl, B, maxp, scores)
+    # Query sets rotated through the timed steps (each step is a new decode
+    # step of the same batch): their selections differ, so the selected K/V
+    # of consecutive steps (64 MiB each at the headline) never add up to
+    # fewer bytes than the 256 MB last-level cache holds, and no step is
+    # served from what an earlier step left there.
+    gq = torch.Generator(device=dev)
+    gq.manual_seed(args.seed + 1)
+    nq = max(1, args.query_sets)
+    qsets = [q] + [torch.randn(q.shape, generator=gq, device=dev, dtype=torch.float32).to(q.dtype)
+                   for _ in range(nq - 1)]
+    sels = [torch.empty_like(sel) for _ in qsets]
+    for qi, si in zip(qsets, sels):
+        L.locks_score_select(cfg, qi, pool, wl.num_blocks, bt, sl, B, maxp, si, ws, ws_bytes)
+    torch.cuda.synchronize()
+    distinct_kv = selected_kv_footprint(wl, sels, bt)
 
-    def select():
+    def score(t):
+        L.locks_page_score(cfg, qsets[t % nq], pool, wl.num_blocks, bt, sl, B, maxp, scores)
+
+    def select(t):
         L.locks_select_pages(cfg, scores, sl, B, maxp, sel, sigma)
 
-    def decode():
-        L.locks_sparse_decode(cfg, q, kp_dec, vp_dec, wl.num_blocks, bt, sl, sel, B, maxp, out, lse, ws,
-                              ws_bytes)
+    def decode(t):
+        i = t % nq
+        L.locks_sparse_decode(cfg, qsets[i], kp_dec, vp_dec, wl.num_blocks, bt, sl, sels[i], B, maxp, out, lse,
+                              ws, ws_bytes)
 
-    def staged():
+    def staged(t):
         # page scoring -> combine + selection -> sparse decode, three launches
-        score()
-        select()
-        decode()
+        L.locks_page_score(cfg, qsets[t % nq], pool, wl.num_blocks, bt, sl, B, maxp, scores)
+        L.locks_select_pages(cfg, scores, sl, B, maxp, sel, sigma)
+        L.locks_sparse_decode(cfg, qsets[t % nq], kp_dec, vp_dec, wl.num_blocks, bt, sl, sel, B, maxp,
+                              out, lse, ws, ws_bytes)
 
-    def step():
+    def step(t):
         # the whole step through the library's one-call entry point
-        L.locks_decode_step(cfg, q, pool, kp_dec, vp_dec, wl.num_blocks, bt, sl, B, maxp, sel, out, lse, ws,
-                            ws_bytes)
+        L.locks_decode_step(cfg, qsets[t % nq], pool, kp_dec, vp_dec, wl.num_blocks, bt, sl, B, maxp,
+                            sel, out, lse, ws, ws_bytes)
 
-    for _ in range(args.warmup):
-        step()
-        staged()
+    for t in range(args.warmup):
+        step(t)
+        staged(t)
     torch.cuda.synchronize()
+    throttle = ThrottleMonitor()
 
-    def timed(fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+    def windows(fn, n_steps, n_windows=3):
+        """n_steps launches of fn in n_windows timed windows (HIP events on
+        torch's stream, which is the stream every call above enqueues on),
+        synchronised between windows. Returns the per-window ms per step and
+        each window's throttle record."""
+        sizes = [n_steps // n_windows + (1 if i < n_steps % n_windows else 0) for i in range(n_windows)]
+        per, thr = [], []
+        t = 0
+        for n in sizes:
+            if n == 0:
+                continue
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            before = throttle.read()
+            e0.record()
+            for _ in range(n):
+                fn(t)
+                t += 1
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / n)
+            thr.append(throttle.delta(before, throttle.read()))
+        return per, thr, sizes
 
-    # ---- timed region: exactly K steps ----
+    # ---- timed region: exactly K steps, in three windows ----
     wall0 = time.perf_counter()
-    step_ms = timed(step)
+    step_win, step_thr, win_sizes = windows(step, args.steps)
     wall1 = time.perf_counter()
+    step_ms = sum(w * n for w, n in zip(step_win, win_sizes)) / args.steps
 
     # ---- the same step as three launches, and each launch on its own: K
-    # back-to-back launches on the same stream and inputs, HIP events around ----
-    staged_ms = timed(staged)
+    # back-to-back launches on the same stream, HIP events around ----
+    staged_win, _, _ = windows(staged, args.steps)
+    staged_ms = sum(w * n for w, n in zip(staged_win, win_sizes)) / args.steps
     stage_us = {"decode_step": 1e3 * step_ms}
-    score()
+    score(0)
     for name, fn in (("page_score", score), ("select", select), ("sparse_decode", decode)):
-        stage_us[name] = 1e3 * timed(fn)
+        w, _, _ = windows(fn, args.steps)
+        stage_us[name] = 1e3 * sum(x * n for x, n in zip(w, win_sizes)) / args.steps
 
     # ---- summary build of the pages that complete in a step (off the decode path) ----
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -229,6 +270,7 @@ def main():
     step_gbs = step_bytes / (step_ms * 1e-3) / 1e9
     gram_flops = 2.0 * P * d * d * n_full * Hkv
     build_tflops = gram_flops / (prefill_build_ms * 1e-3) / 1e12
+    copy = copy_bandwidth(dev)
 
     if args.copy_calibration > 0:
         nb = args.copy_calibration << 20
@@ -242,8 +284,10 @@ def main():
     # ---- CPU oracle on a bounded sample of the same step ----
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, cfg, data, args.cpu_seconds)
+        cpu = cpu_baseline(wl, cfg, data, args.cpu_seconds, step_bytes)
 
+    us = [round(1e3 * w, 3) for w in step_win]
+    ok = [w for w, t in zip(us, step_thr) if not (t or {}).get("throttled")]
     res = {
         "metric": METRIC,
         "value": round(step_ms * 1e3, 3),
@@ -261,10 +305,15 @@ def main():
                    "context_tokens": int(wl.seq_lens[0]),
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "page_size": P, "rank": r,
                    "budget_tokens": k * P, "summary_dtype": wl.summary_dtype,
-                   "parallelism": "single-gpu"},
+                   "query_sets": nq, "parallelism": "single-gpu"},
         "hbm_roofline_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": step_bytes,
         "step_achieved_GBps": round(step_gbs, 1),
+        "windows": {"steps_per_window": win_sizes, "us_per_step": us,
+                    "median_us": round(statistics.median(us), 3), "mean_us": round(statistics.mean(us), 3),
+                    "sd_us": round(statistics.stdev(us), 3) if len(us) > 1 else 0.0,
+                    "throttle": step_thr, "unthrottled_mean_us": round(statistics.mean(ok), 3) if ok else None},
+        "measured_copy_GBps": copy,
         "roofline": roofline("page_score", wl, summary_bytes, stage_us["page_score"]),
         "sparse_decode_roofline": (roofline("sparse_decode", wl, kv_bytes, stage_us["sparse_decode"])
                                    if kv_host is None else
@@ -272,6 +321,7 @@ def main():
                                     "achieved": round(kv_bytes / (stage_us["sparse_decode"] * 1e-6) / 1e9, 1),
                                     "unit": "GB/s", "algorithmic_bytes_per_launch": kv_bytes,
                                     "avg_launch_us": round(stage_us["sparse_decode"], 3)}),
+        "selected_kv_bytes_across_query_sets": distinct_kv,
         "kv_resident": "host" if kv_host is not None else "hbm",
         "staged_step_us": round(staged_ms * 1e3, 3),
         "stages_us": {n: round(v, 3) for n, v in stage_us.items()},
@@ -665,60 +715,198 @@ def roofline(kernel, wl, alg_bytes, avg_us):
     return rec
 
 
-def cpu_baseline(wl, cfg, data, seconds):
-    """Oracle score -> combine -> select -> attend on the first sequences of the batch,
-    with synthetic summary records of the same shape; scaled to one full step."""
-    import numpy as np
+def selected_kv_footprint(wl, sels, bt):
+    """Distinct K/V bytes selected over the rotated query sets (the working
+    set that consecutive timed decodes cycle through)."""
+    P, d = wl.page_size, wl.head_dim
+    e = 2 if wl.kv_dtype == "bf16" else 4
+    seen = set()
+    bt_c = bt.cpu()
+    for sel in sels:
+        sc = sel.cpu()
+        for b in range(wl.batch):
+            for h in range(wl.num_kv_heads):
+                for j in sc[b, h].tolist():
+                    if j >= 0:
+                        seen.add((int(bt_c[b, j]), h))
+    return len(seen) * P * 2 * d * e
+
+
+class ThrottleMonitor:
+    """Reads the GPU's accumulated violation counters (thermal, power, VR,
+    HBM thermal) through amdsmi; a window is throttled when any of them grew
+    while it ran. Reports itself unavailable when amdsmi cannot reach the GPU."""
+    KEYS = ("acc_prochot_thrm", "acc_ppt_pwr", "acc_socket_thrm", "acc_vr_thrm", "acc_hbm_thrm")
+
+    def __init__(self):
+        self.h = None
+        self.err = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                raise RuntimeError("no GPU handle")
+            self.h = handles[0]
+            self.smi = amdsmi
+            self.smi.amdsmi_get_violation_status(self.h)
+        except Exception as ex:  # noqa: BLE001 - monitoring only
+            self.h = None
+            self.err = f"{type(ex).__name__}: {ex}"[:200]
+
+    def read(self):
+        if self.h is None:
+            return None
+        try:
+            v = self.smi.amdsmi_get_violation_status(self.h)
+            return {k: v.get(k) for k in self.KEYS + ("acc_counter",)}
+        except Exception as ex:  # noqa: BLE001
+            self.err = f"{type(ex).__name__}: {ex}"[:200]
+            return None
+
+    def delta(self, a, b):
+        if a is None or b is None:
+            return {"available": False, "reason": self.err}
+        out = {"available": True}
+        grew = False
+        for k in self.KEYS + ("acc_counter",):
+            x, y = a.get(k), b.get(k)
+            dv = (y - x) if isinstance(x, int) and isinstance(y, int) else None
+            out[k] = dv
+            if k != "acc_counter" and dv:
+                grew = True
+        out["throttled"] = grew
+        return out
+
+
+def copy_bandwidth(dev, mib=1024, reps=5):
+    """Device-to-device copy of `mib` MiB (read + write bytes over time), the
+    best of `reps` copies: the bandwidth this machine delivers to a plain stream."""
+    import torch
+    src = torch.ones(mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return {"bytes_moved": 2 * (mib << 20), "GBps": round(2 * (mib << 20) / (best * 1e-3) / 1e9, 1),
+            "kernel": "torch copy_ (device to device)"}
+
+
+def host_cpus():
+    """CPUs this process may run on: the affinity mask, cut to the cgroup CPU
+    quota when one is set; and the CPU model."""
+    n = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = float(q) / float(per)
+    except (OSError, ValueError):
+        try:
+            q = int(open("/sys/fs/cgroup/cpu/cpu.cfs_quota_us").read())
+            per = int(open("/sys/fs/cgroup/cpu/cpu.cfs_period_us").read())
+            if q > 0:
+                quota = q / per
+        except (OSError, ValueError):
+            pass
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    usable = n if quota is None else max(1, min(n, int(math.ceil(quota))))
+    return usable, {"affinity_cpus": n, "cgroup_cpu_quota": quota, "os_cpu_count": os.cpu_count(),
+                    "cpu_model": model}
+
+
+# the CPU share of one GPU on the machines this runs on: worker pools stay within it
+CPU_SHARE_PER_GPU = 16
+
+
+def cpu_baseline(wl, cfg, data, seconds, step_bytes):
+    """The fp64 oracle (score -> combine -> select -> attend, test
+    infrastructure, untuned) on a bounded sample of the same step, with
+    synthetic summary records of the same shape, timed with every usable host
+    CPU and with one thread: each leg three runs of about seconds / 6, median
+    reported, scaled to one full step."""
     import torch
 
     import oracle
     from sparse_kv_page_amd import synth
 
+    usable, info = host_cpus()
+    threads_all = max(1, min(usable, CPU_SHARE_PER_GPU))
+
+    def sample(nseq):
+        sub = wl.with_(batch=nseq, seq_lens=wl.seq_lens[:nseq])
+        bt = data["block_table"][:nseq].cpu()
+        used = torch.unique(bt.reshape(-1)).long()
+        remap = torch.full((wl.num_blocks,), -1, dtype=torch.long)
+        remap[used] = torch.arange(used.numel())
+        bt_local = remap[bt.long()].numpy()
+        to32 = lambda t: t.to("cpu", torch.float32).numpy()
+        kp = to32(data["k_pool"][used.to(data["k_pool"].device)])
+        vp = to32(data["v_pool"][used.to(data["v_pool"].device)])
+        # records indexed by the local block ids; quantized records are
+        # dequantized by the oracle inside the timed loop
+        if wl.summary_dtype == "i4":
+            codes = synth.random_i4_codes(sub.with_(extra_blocks=0), seed=1, device="cpu")
+            codes = {kk: v.reshape((-1,) + tuple(v.shape[2:])).numpy() for kk, v in codes.items()}
+            shape = (used.numel(), wl.num_kv_heads)
+
+            def summaries():
+                m, v, c = oracle.dequantize_summaries(codes)
+                return tuple(x.reshape(shape + x.shape[1:]) for x in (m, v, c))
+        else:
+            recs = [x.double().numpy() for x in synth.random_summaries(sub.with_(extra_blocks=0), seed=1,
+                                                                        device="cpu")]
+
+            def summaries():
+                return recs
+        q = data["q"][:nseq].to("cpu", torch.float64).numpy()
+        return sub, q, kp, vp, bt_local, summaries
+
+    def leg(nseq, units, threads, budget_s):
+        sub, q, kp, vp, bt_local, summaries = sample(nseq)
+        run = lambda: oracle.decode_step(q, *summaries(), kp, vp, bt_local, list(sub.seq_lens), wl.page_size,
+                                         wl.budget_pages, wl.softmax_scale, units=units, threads=threads)
+        run()  # warm (loads the library)
+        per_unit = []
+        for _ in range(3):
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                run()
+                reps += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            per_unit.append((time.perf_counter() - t0) / reps / len(units))
+        n_units = wl.batch * wl.num_kv_heads
+        runs_us = [round(x * n_units * 1e6, 1) for x in per_unit]
+        return statistics.median(runs_us), runs_us
+
     nseq = min(2, wl.batch)
-    sub = wl.with_(batch=nseq, seq_lens=wl.seq_lens[:nseq])
-    bt = data["block_table"][:nseq].cpu()
-    used = torch.unique(bt.reshape(-1)).long()
-    remap = torch.full((wl.num_blocks,), -1, dtype=torch.long)
-    remap[used] = torch.arange(used.numel())
-    bt_local = remap[bt.long()].numpy()
-    to32 = lambda t: t.to("cpu", torch.float32).numpy()
-    kp = to32(data["k_pool"][used.to(data["k_pool"].device)])
-    vp = to32(data["v_pool"][used.to(data["v_pool"].device)])
-    # records indexed by the local block ids (one per (page, KV head) of the sample);
-    # quantized records are dequantized by the oracle inside the timed loop
-    if wl.summary_dtype == "i4":
-        codes = synth.random_i4_codes(sub.with_(extra_blocks=0), seed=1, device="cpu")
-        codes = {kk: v.reshape((-1,) + tuple(v.shape[2:])).numpy() for kk, v in codes.items()}
-        shape = (used.numel(), wl.num_kv_heads)
-
-        def summaries():
-            m, v, c = oracle.dequantize_summaries(codes)
-            return (x.reshape(shape + x.shape[1:]) for x in (m, v, c))
-    else:
-        recs = synth.random_summaries(sub.with_(extra_blocks=0), seed=1, device="cpu")
-        recs = [x.double().numpy() for x in recs]
-
-        def summaries():
-            return recs
-    q = data["q"][:nseq].to("cpu", torch.float64).numpy()
-    threads = oracle.default_threads()
-    mu, vt, cf = summaries()
-    assert mu.shape[0] == used.numel()
-    oracle.decode_step(q, mu, vt, cf, kp, vp, bt_local, list(sub.seq_lens), wl.page_size,
-                       wl.budget_pages, wl.softmax_scale, threads=threads)  # warm (loads lib)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        mu, vt, cf = summaries()
-        oracle.decode_step(q, mu, vt, cf, kp, vp, bt_local, list(sub.seq_lens), wl.page_size,
-                           wl.budget_pages, wl.softmax_scale, threads=threads)
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    per_rep = (time.perf_counter() - t0) / reps
-    per_step_us = per_rep * (wl.batch / nseq) * 1e6
-    return {"value": round(per_step_us, 1), "unit": "us", "cores": threads, "kind": "oracle",
-            "sample": f"{nseq} of {wl.batch} sequences x {wl.num_kv_heads} KV heads "
-                      f"(score+combine+select+attend, fp64), {reps} repeats, scaled x{wl.batch // nseq}"}
+    all_units = [(b, h) for b in range(nseq) for h in range(wl.num_kv_heads)]
+    one_units = all_units[:2]
+    v_all, runs_all = leg(nseq, all_units, threads_all, seconds / 6)
+    v_one, runs_one = leg(nseq, one_units, 1, seconds / 6)
+    return {"value": v_all, "unit": "us", "cores": threads_all, "kind": "oracle",
+            "sample": f"{len(all_units)} of {wl.batch * wl.num_kv_heads} (sequence, KV head) units "
+                      f"(score+combine+select+attend, fp64), scaled to the whole step; median of 3 runs",
+            "runs_us": runs_all, "GBps_effective": round(step_bytes / (v_all * 1e-6) / 1e9, 2),
+            "one_thread": {"value": v_one, "unit": "us", "runs_us": runs_one,
+                           "sample": f"{len(one_units)} units, scaled to the whole step"},
+            "host": dict(info, usable_cpus=usable, thread_cap=CPU_SHARE_PER_GPU)}
 
 
 if __name__ == "__main__":

@@ -11,7 +11,9 @@ Key generator, per (sequence, KV head, page p) and token i:
     c_p ~ N(0, centroid_std^2 I), or with ar_rho > 0 an AR(1) drift along the
           sequence: c_0 ~ N(0, s^2 I), c_p = rho c_{p-1} + sqrt(1 - rho^2) eta_p,
           eta_p ~ N(0, s^2 I) (stationary variance s^2)
-Values ~ N(0, I_d); queries q_g ~ N(0, I_d) (drawn first). In `n_needles`
+A constant `key_offset` may be added to every coordinate of every key (a
+common offset, as in models whose keys share a large mean). Values ~ N(0, I_d);
+queries q_g ~ N(0, I_d) (drawn first). In `n_needles`
 pages per (sequence, KV head), chosen uniformly without replacement among the
 complete pages other than the sink page 0 and the current page J-1, one
 uniformly chosen token key is replaced by needle_scale * qhat, qhat the unit
@@ -51,6 +53,7 @@ class Workload:
     n_needles: int = 0
     needle_scale: float = 6.0
     extra_blocks: int = 0    # unused physical blocks appended to the pools
+    key_offset: float = 0.0  # added to every coordinate of every key (a common offset)
 
     @property
     def num_q_heads(self) -> int:
@@ -155,6 +158,8 @@ def generate(wl: Workload, seed: int = 0, device="cpu"):
         coef = torch.randn((Hkv, J, P, R), generator=g, device=dev, dtype=f32) * sd
         keys = c[:, :, None, :] + torch.einsum("hjdr,hjpr->hjpd", basis, coef)
         keys = keys + wl.noise * torch.randn((Hkv, J, P, d), generator=g, device=dev, dtype=f32)
+        if wl.key_offset:
+            keys = keys + wl.key_offset
         vals = torch.randn((Hkv, J, P, d), generator=g, device=dev, dtype=f32)
         # needles
         if wl.n_needles > 0:

@@ -11,6 +11,8 @@ page scores, page selections) are produced by the oracle or the generator.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -223,6 +225,117 @@ def gpu_decode_step(wl, cfg, g, pool, ws=None):
     L.locks_decode_step(cfg, g["q"], pool, g["k_pool"], g["v_pool"], wl.num_blocks, g["block_table"],
                         g["seq_lens"], wl.batch, wl.max_pages, sel, out, lse, ws, nbytes)
     return sel, out, lse
+
+
+# --------------------------------------------------------------------------
+# every unit of a full-size batch against the oracle (host threads)
+# --------------------------------------------------------------------------
+HOST_THREADS = 8
+
+
+def check_all_units(wl, data_c, hs_c, sel_c, unit_summaries, threads=HOST_THREADS):
+    """For every (sequence, KV head) unit: the GPU page scores hs_c element by
+    element against Eq. (2) evaluated by the oracle on the unit's stored
+    records (unit_summaries(b, h, Jc) -> (mu, vt, coef) as float64), and the
+    GPU selection sel_c against the oracle's under the window rule. data_c
+    holds CPU copies of q and block_table. Returns the oracle selections
+    [B][H_kv][k] (int32) and the number of pages inside the window."""
+    G = wl.group
+    units = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
+
+    def one(u):
+        b, h = u
+        _, J, Jc = lens(wl, b)
+        s_o = None
+        if Jc > 0:
+            mu, vt, cf = unit_summaries(b, h, Jc)
+            s_o = oracle_unit_scores(wl, data_c, b, h, mu, vt, cf)
+            v = mixed_violation(f64(hs_c[b, h * G:(h + 1) * G, :Jc]), s_o)
+            assert v <= 1.0, f"unit {u}: score violation {v:.3f} x tolerance"
+        sel_o, sigma_o = oracle_unit_select(wl, b, s_o if J > wl.budget_pages else None)
+        nd = check_selection(wl, b, sel_c[b, h].tolist(), sel_o.tolist(), sigma_o)
+        return u, sel_o, nd
+
+    sel_o_all = torch.full((wl.batch, wl.num_kv_heads, wl.budget_pages), -1, dtype=torch.int32)
+    ndiff = 0
+    with ThreadPoolExecutor(threads) as ex:
+        for (b, h), sel_o, nd in ex.map(one, units):
+            sel_o_all[b, h] = torch.from_numpy(sel_o)
+            ndiff += nd
+    return sel_o_all, ndiff
+
+
+def check_all_outputs(wl, data, out_c, sel_c, threads=HOST_THREADS):
+    """Attention output of every unit against the oracle over the pages listed
+    in sel_c (the partial current page's valid tokens only)."""
+    G = wl.group
+    kp, vp = data["k_pool"], data["v_pool"]
+    bt = data["block_table"].cpu()
+    q_c = data["q"].cpu()
+    units = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
+    gathered = {}
+    for b, h in units:  # device gathers stay on this thread
+        T, _, _ = lens(wl, b)
+        pages = [j for j in sel_c[b, h].tolist() if j >= 0]
+        if not pages:
+            continue
+        idx = torch.tensor([int(bt[b, j]) for j in pages], device=kp.device)
+        nv = [min(wl.page_size, T - j * wl.page_size) for j in pages]
+        gathered[(b, h)] = (kp[idx, h].cpu(), vp[idx, h].cpu(), nv)
+
+    def one(u):
+        b, h = u
+        sl = slice(h * G, (h + 1) * G)
+        if u not in gathered:
+            assert not np.any(f64(out_c[b, sl])), f"unit {u}: empty selection must give zeros"
+            return
+        k_, v_, nv = gathered[u]
+        ks = np.concatenate([f64(k_[i, :n]) for i, n in enumerate(nv)])
+        vs = np.concatenate([f64(v_[i, :n]) for i, n in enumerate(nv)])
+        o_ref, _ = oracle.attend(f64(q_c[b, sl]), ks, vs, wl.softmax_scale)
+        err = float(np.max(np.abs(f64(out_c[b, sl]) - o_ref)))
+        assert err <= out_tol(wl), f"unit {u}: output error {err}"
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, units))
+
+
+# --------------------------------------------------------------------------
+# summary fits: basis-invariant checks against the oracle ([Locks] §4,
+# App. A.2 Cor. 1: the top-r right singular subspace of the centred page)
+# --------------------------------------------------------------------------
+FIT_ENERGY_SLACK = 1e-3   # of the page's total centred energy
+FIT_SUBSPACE_TOL = 2e-2   # sine of the angles (Frobenius) to the oracle's leading subspace
+FIT_GAP = 0.2             # relative eigen-gap that makes a leading subspace well defined
+
+
+def check_fit(keys, vt_stored, ev_o, vt_o, r, energy_slack=FIT_ENERGY_SLACK, subspace_tol=FIT_SUBSPACE_TOL):
+    """keys [P][d] as stored; vt_stored [r][d] the GPU basis as stored;
+    ev_o [d] the oracle's eigenvalues of D^T D (descending) and vt_o [r][d]
+    its basis. With Q an orthonormal basis of the stored span (QR):
+      * Eckart-Young: ||D - D Q Q^T||_F^2 <= sum_{l > r} ev_l + slack * sum ev;
+      * every leading oracle subspace of size m <= r that is separated from
+        the next eigenvalue by a relative gap lies in span(Q) up to the
+        tolerance (||(I - Q Q^T) V_o[:m]||_F).
+    Returns the number of leading subspaces checked."""
+    keys = np.asarray(keys, dtype=np.float64)
+    D = keys - keys.mean(0)
+    Q, _ = np.linalg.qr(np.asarray(vt_stored, dtype=np.float64).T)  # d x r
+    ev = np.clip(np.asarray(ev_o, dtype=np.float64), 0.0, None)
+    total = float(np.sum(ev))
+    opt = float(np.sum(ev[r:]))
+    resid = float(np.linalg.norm(D - D @ Q @ Q.T) ** 2)
+    assert resid <= opt + energy_slack * total, \
+        f"residual {resid:.6g} > optimum {opt:.6g} + {energy_slack} x {total:.6g}"
+    checked = 0
+    for m in range(1, r + 1):
+        if ev[m - 1] <= 0 or (ev[m - 1] - ev[m]) / ev[m - 1] <= FIT_GAP:
+            continue
+        Vm = np.asarray(vt_o[:m], dtype=np.float64).T
+        off = float(np.linalg.norm(Vm - Q @ (Q.T @ Vm)))
+        assert off <= subspace_tol, f"leading {m}-subspace off by {off:.4g}"
+        checked += 1
+    return checked
 
 
 # --------------------------------------------------------------------------

@@ -236,7 +236,7 @@ def test_i4_decode_step_end_to_end():
 @pytest.mark.parametrize("name,rank", [("llama8b_128k_b8", 8), ("llama8b_128k_b8_p16", 8),
                                        ("llama8b_128k_b8_p16", 4)],
                          ids=["p64_r8", "p16_r8", "p16_r4"])
-def test_i4_full_size_sampled(name, rank):
+def test_i4_full_size_all_units(name, rank):
     wl = W[name].with_(summary_dtype="i4", rank=rank)
     cfg = L.config_for(wl)
     G = wl.group
@@ -247,25 +247,15 @@ def test_i4_full_size_sampled(name, rank):
     sel = gg.gpu_score_select(wl, cfg, d, pool)
     torch.cuda.synchronize()
     data_c = {"q": d["q"].cpu(), "block_table": d["block_table"].cpu()}
-    units = [(0, 0), (3, 5), (7, 7)]
-    hs_c = hs.cpu()
-    sel_o_all = sel.clone()
-    refs = {}
-    for b, h in units:
-        _, J, Jc = gg.lens(wl, b)
-        mu, vt, cf = gg.i4_unit_summaries(wl, qs, data_c["block_table"], b, h, Jc)
-        s_o = gg.oracle_unit_scores(wl, data_c, b, h, mu, vt, cf)
-        assert gg.mixed_violation(gg.f64(hs_c[b, h * G:(h + 1) * G, :Jc]), s_o) <= 1.0
-        sel_o, sigma_o = gg.oracle_unit_select(wl, b, s_o)
-        gg.check_selection(wl, b, sel[b, h].tolist(), sel_o.tolist(), sigma_o)
-        sel_o_all[b, h] = torch.from_numpy(sel_o).to(gg.DEV)
-        refs[(b, h)] = sel_o
-    out, _ = gg.gpu_decode(wl, cfg, d, sel_o_all)
+    # every unit: scores element by element and selections against the oracle
+    # on the dequantized records, outputs on the oracle's selections
+    sel_o, ndiff = gg.check_all_units(
+        wl, data_c, hs.cpu(), sel.cpu(),
+        lambda b, h, Jc: gg.i4_unit_summaries(wl, qs, data_c["block_table"], b, h, Jc))
+    assert ndiff <= wl.batch * wl.num_kv_heads
+    out, _ = gg.gpu_decode(wl, cfg, d, sel_o.to(gg.DEV))
     torch.cuda.synchronize()
-    out = gg.f64(out.cpu())
-    for (b, h), sel_o in refs.items():
-        o_ref, _ = gg.oracle_unit_attend(wl, d, b, h, sel_o)
-        assert np.max(np.abs(out[b, h * G:(h + 1) * G] - o_ref)) <= gg.out_tol(wl)
+    gg.check_all_outputs(wl, d, out.cpu(), sel_o)
     # full-size build, every page of every unit; a sample checked for validity
     del pool, hs
     ids = d["block_table"].reshape(-1).contiguous()
