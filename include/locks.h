@@ -129,16 +129,35 @@ int locks_workspace_size(const locks_config_t* cfg, int32_t batch, int32_t max_p
  * into the record of (block, h) in summary_pool. For LOCKS_I4 each group (the
  * centroid, each basis vector, each token's coefficient row) is quantized
  * symmetrically: scale = bf16(max|x| / L) with L = 127 (8-bit) or 7 (4-bit),
- * code = round-half-even(x / scale) in fp32, scale 0 for an all-zero group. Keys are read as stored;
- * the fit is computed in fp32 (Gram matrix on the matrix cores, subspace
- * iteration with a Rayleigh-Ritz step). Within an eigenvalue cluster any
- * orthonormal basis of the subspace is an equally valid result; each basis
- * vector is sign-fixed so its largest-magnitude entry is positive.
+ * code = round-half-even(x / scale) in fp32, scale 0 for an all-zero group.
+ * Keys are read as stored; the fit is computed in fp32 (centred keys, Gram
+ * matrix on the matrix cores, subspace iteration with Rayleigh-Ritz steps; see
+ * locks_build_summaries_ex). Within an eigenvalue cluster any orthonormal
+ * basis of the subspace is an equally valid result; each basis vector is
+ * sign-fixed so its largest-magnitude entry is positive.
  * Only summarise complete pages. Ids outside [0, num_blocks) are skipped;
  * duplicate ids race. n_ids == 0 enqueues nothing. */
 int locks_build_summaries(const locks_config_t* cfg, const void* k_pool, int64_t num_blocks,
                           const int32_t* block_ids, int32_t n_ids, void* summary_pool,
                           hipStream_t stream);
+
+/* locks_build_summaries with a report of every fit. The top-r eigenvectors
+ * are reached through the P x P dual Gram M = D D^T by subspace iteration on
+ * a 16-column block with a Rayleigh-Ritz step after every product M X from
+ * the third on ([Locks] App. A.2: the page's top-r right singular vectors);
+ * a fit has converged when each of its r leading Ritz pairs has a residual
+ * ||M u - theta u|| <= 2^-10 times the largest Ritz value and every leading
+ * m-subspace (m <= r) whose Ritz gap exceeds 2^-7 of the largest Ritz value
+ * has a residual norm <= 2^-6 of that gap (an angle of about 2^-6 to the
+ * exact subspace by the sin-theta bound). P = 16 pages are
+ * solved on the whole 16-dimensional space in one step. fit_info ([n_ids]
+ * [num_kv_heads] int32, device, may be NULL) receives for the tile
+ * (block_ids[t], h) the number of products taken, negated when the bound was
+ * not met within the cap of 32 products (the record then holds the last
+ * Ritz basis). Entries of skipped ids are left untouched. */
+int locks_build_summaries_ex(const locks_config_t* cfg, const void* k_pool, int64_t num_blocks,
+                             const int32_t* block_ids, int32_t n_ids, void* summary_pool,
+                             int32_t* fit_info, hipStream_t stream);
 
 /* (a2) Page scoring, [Locks] §4 Eq. (2): for every sequence b, query head g
  * and complete page j < floor(T_b / P), with mu, V, C the summary of

@@ -1,46 +1,64 @@
 // (a1) Summary build, [Locks] §3-§4: for one (physical block, KV head) tile of
 // P keys, fit
-//   mu = (1/P) sum_i k_i,  D = K - 1 mu^T,  H = D^T D (d x d),
-//   V  = top-r eigenvectors of H,  C = D V,
+//   mu = (1/P) sum_i k_i,  D = K - 1 mu^T,
+//   V  = top-r eigenvectors of H = D^T D (d x d),  C = D V,
 // and store (mu, V^T, C) in the summary record.
 //
-// One workgroup (4 waves) per tile, everything in LDS and registers:
-//  1. K is staged transposed in LDS; mu is a plain fp32 mean.
-//  2. Gram on the matrix cores. bf16 keys: H = K^T K - P mu mu^T with
-//     v_mfma_f32_16x16x16_bf16 (exact bf16 products, fp32 accumulation);
-//     fp32 keys are centred first and use v_mfma_f32_16x16x4_f32. Wave w
-//     computes the 16-row tiles it owns against every column tile; because H
-//     is symmetric the MFMA output registers already are the A operand of
-//     H X for those rows, with the k index permuted as
-//     k(step = 4*tile + i, lane group lg) = 16*tile + 4*lg + i.
-//     H therefore never leaves registers.
-//  3. Subspace iteration on a 16-column block X: Y = H X (fp32 MFMA), then
-//     X = Y R^-1 from a Cholesky factor of the column-scaled Gram Y^T Y
-//     (columns that collapse are replaced by fresh pseudo-random vectors).
-//     Each pass has two workgroup barriers: the waves' partial Grams meet in
-//     LDS, then every wave factors the 16 x 16 Gram and inverts the factor
-//     in registers (lane l holds row l, broadcasts by readlane) and forms its
-//     own rows of X on the matrix cores.
-//  4. A second Cholesky-QR pass, then Rayleigh-Ritz: T = X^T H X (16 x 16)
-//     diagonalised by parallel cyclic Jacobi (8 disjoint rotations per
-//     round applied in one pass, stopping once the off-diagonal mass is
-//     negligible); the r largest Ritz pairs give V = X W_r, each column
-//     sign-fixed so its largest-magnitude entry is positive (lowest index on
-//     ties).
-//  5. C = D V in fp32 from the unrounded V; mu, V, C are rounded to the
-//     summary dtype independently. Quantized ("i4") records, [Locks] §4 and
-//     App. C.7: per group (the centroid, each basis vector, each token's
-//     coefficient row) scale = bf16(max|x| / L), L = 127 for the 8-bit
-//     centroid and coefficients and 7 for the 4-bit basis, and code =
+// The top-r eigenvectors of D^T D are the top-r right singular vectors of D
+// ([Locks] App. A.2), reached here through the P x P dual Gram M = D D^T
+// (P <= d for every supported shape): if M u = theta u with theta > 0, then
+// v = D^T u / sqrt(theta) is a unit eigenvector of D^T D with the same
+// eigenvalue. One workgroup (4 waves) per tile, all in LDS and registers:
+//  1. Keys -> registers; the centroid is a plain fp32 mean; the centred keys
+//     D = K - mu are kept in LDS, for bf16 keys as bf16 hi + lo parts (their
+//     sum is D to about 2^-16 relative), so the Gram needs no uncentred
+//     subtraction whatever the keys' common offset.
+//  2. M = D D^T on the matrix cores: v_mfma_f32_16x16x32_bf16 on hi.hi +
+//     hi.lo + lo.hi (exact bf16 products, fp32 sums) for bf16 keys,
+//     v_mfma_f32_16x16x4_f32 for fp32 keys. Wave w computes the 16-row block
+//     w of M; by symmetry its MFMA outputs already are the A operand of M X
+//     for those rows (k index permuted as k = 16 I + 4 g + i), so M never
+//     leaves registers.
+//  3. Top-r eigenvectors of M: for P = 16 one Rayleigh-Ritz step on the whole
+//     space (X = I, exact); for P >= 32 subspace iteration on a 16-column
+//     block started from signed Hadamard columns, X <- orth(M X) by
+//     Cholesky-QR (columns that collapse are replaced by pseudo-random
+//     vectors), from the third product on each followed by a Rayleigh-Ritz
+//     step: T = X^T M X (16 x 16) diagonalised by parallel
+//     cyclic Jacobi, Ritz vectors U = X W, Ritz values theta. The fit has
+//     converged when (a) every one of the r leading Ritz pairs has a residual
+//     ||M u_i - theta_i u_i|| <= 2^-10 theta_1, i.e. each vector is exact for
+//     a Gram within 2^-10 of the stored one (below the bf16 rounding of the
+//     keys themselves), and (b) every leading m-subspace (m <= r) whose Ritz
+//     gap theta_m - theta_(m+1) exceeds 2^-7 theta_1 has a residual
+//     ||R_m||_F <= 2^-6 (theta_m - theta_(m+1)), which by the sin-theta bound
+//     puts it within an angle of about 2^-6 of the exact one; otherwise the
+//     iteration continues from M U. The number of products, and whether the
+//     bounds were met within the cap, are reported by
+//     locks_build_summaries_ex.
+//  4. V = D^T U_r (matrix cores), orthonormalised by Cholesky-QR (a second
+//     pass when a column vanished and was replaced), each column sign-fixed so
+//     its largest-magnitude entry is positive (lowest index on ties).
+//  5. C = D V in fp32 from the unrounded V (matrix cores); mu, V, C are rounded
+//     to the summary dtype independently. Quantized ("i4") records, [Locks] §4
+//     and App. C.7: per group (the centroid, each basis vector, each token's
+//     coefficient row) scale = bf16(max|x| / L), L = 127 for the 8-bit centroid
+//     and coefficients and 7 for the 4-bit basis, and code =
 //     round-half-even(x / scale), all in fp32 (correctly rounded division).
 #include "common.h"
 #include "kernels.h"
 
 namespace locks {
 
-constexpr int kBuildIters = 10;   // subspace iterations
-constexpr int kJacobiSweeps = 8;  // sweeps of the 16 x 16 Rayleigh-Ritz problem
-constexpr int kBlk = 16;          // block size of the subspace iteration
+constexpr int kBlk = 16;                    // block size of the subspace iteration
+constexpr int kFirstRitzCheck = 3;          // the product after which the first Rayleigh-Ritz step comes (P >= 32)
+constexpr int kMaxProducts = 32;            // cap on products M X
+constexpr float kRitzTol = 1.0f / 1024.0f;  // residual bound of every pair, relative to the largest Ritz value
+constexpr float kGapFloor = 1.0f / 128.0f;  // a Ritz gap above this fraction of the largest value is significant
+constexpr float kSubspaceTol = 1.0f / 64.0f;   // residual bound of a leading subspace, relative to its gap
+constexpr int kMaxSweeps = 12;              // Jacobi sweeps of one Rayleigh-Ritz step
+constexpr float kJacobiRel = 0x1p-12f;      // off-diagonal entries below this relative size are converged
+constexpr float kJacobiStop = 0x1p-8f;      // a sweep whose largest rotated relative entry is below this is the last
 
 namespace {
 
@@ -52,173 +70,184 @@ __device__ __forceinline__ float hash_unit(uint32_t a, uint32_t b, uint32_t salt
   return (float)(x >> 8) * (1.0f / 8388608.0f) - 1.0f;  // [-1, 1)
 }
 
-template <typename T>
-struct GramOp;
+__device__ __forceinline__ float rdl(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 
-template <>
-struct GramOp<bf16_t> {
-  static constexpr int kStep = 16;  // tokens per MFMA
-  // kt row r holds the keys of dimension r over tokens (stride in elements)
-  static __device__ __forceinline__ f32x4_t mfma(const bf16_t* kt, int stride, int ra, int rb, int tok0,
-                                                 int lane, f32x4_t c) {
-    const int t = tok0 + 4 * (lane >> 4);
-    const bf16x4_t av = *reinterpret_cast<const bf16x4_t*>(kt + (ra + (lane & 15)) * stride + t);
-    const bf16x4_t bv = *reinterpret_cast<const bf16x4_t*>(kt + (rb + (lane & 15)) * stride + t);
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, c, 0, 0, 0);
+// Centred keys in LDS: row-major [P][D], 16-byte chunks XOR-swizzled by row so
+// that 16 lanes reading one chunk of 16 different rows hit distinct banks.
+template <typename T, int D, int P>
+struct CentredKeys;
+
+template <int D, int P>
+struct CentredKeys<bf16_t, D, P> {
+  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  bf16_t hi[P * D];
+  bf16_t lo[P * D];
+  static __device__ __forceinline__ int chunk_off(int row, int chunk) {
+    return row * D + ((chunk ^ (row & (kChunks - 1))) << 3);
+  }
+  __device__ __forceinline__ float at(int row, int a) const {
+    const int o = chunk_off(row, a >> 3) + (a & 7);
+    return bf16_to_f32(hi[o]) + bf16_to_f32(lo[o]);
   }
 };
 
-template <>
-struct GramOp<float> {
-  static constexpr int kStep = 4;
-  static __device__ __forceinline__ f32x4_t mfma(const float* kt, int stride, int ra, int rb, int tok0,
-                                                 int lane, f32x4_t c) {
-    const int t = tok0 + (lane >> 4);
-    const float av = kt[(ra + (lane & 15)) * stride + t];
-    const float bv = kt[(rb + (lane & 15)) * stride + t];
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c, 0, 0, 0);
+template <int D, int P>
+struct CentredKeys<float, D, P> {
+  static constexpr int kChunks = D / 4;
+  float v[P * D];
+  static __device__ __forceinline__ int chunk_off(int row, int chunk) {
+    return row * D + ((chunk ^ (row & (kChunks - 1))) << 2);
   }
+  __device__ __forceinline__ float at(int row, int a) const { return v[chunk_off(row, a >> 2) + (a & 3)]; }
+};
+
+template <typename T, int D, int P>
+struct alignas(16) BuildLds {
+  CentredKeys<T, D, P> dk;
+  float mu[D];
+  float X[P][kBlk];        // orthonormal block; at the end the Ritz vectors U
+  float Y[P][kBlk];        // M X, then M U; at the end C = D V
+  float Vb[D][kBlk];       // D^T U, then the orthonormal basis V
+  float Gp[4][kBlk][kBlk]; // the waves' partial Gram matrices (and centroid partial sums)
+  float RiW[4][kBlk][kBlk];  // each wave's R^-1 of the Cholesky-QR
+  float Ms[2][kBlk][kBlk + 1];  // Rayleigh quotient T, ping-pong
+  float Wm[2][kBlk][kBlk + 1];  // its accumulated rotations, ping-pong
+  float Wo[kBlk][kBlk];    // eigenvectors of T, descending eigenvalue order
+  float th[kBlk];          // Ritz values, descending
+  float jc[2][kBlk], jo[2][kBlk];  // rotation of a Jacobi round (this one, the next): self / other coefficient
+  uint32_t swmax[2];       // largest relative off-diagonal rotated in a sweep (float bits), alternating
+  float res[4][kBlk];      // partial squared residual norms
+  int order[kBlk];
+  int flag;
 };
 
 }  // namespace
 
-template <typename T, int D, bool I4>
+template <typename T, int D, int P, bool I4>
 __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
-  constexpr int NT = D / 16;          // row tiles of H
-  constexpr int RTW = NT / 4;         // row tiles per wave
-  constexpr int KT_STRIDE = 64 + 4;   // LDS row stride of the transposed keys
-  __shared__ __attribute__((aligned(16))) T kt[D * KT_STRIDE];
-  __shared__ float mu[D];
-  __shared__ __attribute__((aligned(16))) float X[D][kBlk];
-  __shared__ __attribute__((aligned(16))) float Y[D][kBlk];
-  __shared__ __attribute__((aligned(16))) float Mp[4][kBlk][kBlk];
-  __shared__ __attribute__((aligned(16))) float RiW[4][kBlk][kBlk];  // each wave's copy of R^-1
-  __shared__ float Ms[2][kBlk][kBlk + 1];  // Rayleigh quotient, ping-pong
-  __shared__ float Wm[2][kBlk][kBlk + 1];  // its eigenvectors, ping-pong
-  __shared__ float jsc[kBlk], joc[kBlk];   // rotation of the index's pair: self / other coefficient
-  __shared__ int jpt[kBlk];                // partner index
-  __shared__ int order[kBlk];
-  __shared__ int cur_s;  // which Ms / Wm buffer holds the result
+  constexpr int NB = P / 16;  // 16-row blocks of M (and of X, Y, C)
+  constexpr int DB = D / 16;  // 16-row blocks of V
+  static_assert(P == 16 || P == 32 || P == 64, "page size");
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(sizeof(BuildLds<T, D, P>) <= 64 * 1024, "LDS budget");
+  __shared__ BuildLds<T, D, P> L;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int ln = lane & 15;  // MFMA column / row-in-tile
+  const int lg = lane >> 4;  // MFMA k group / row group
   const int h = blockIdx.y;
-  const int P = a.P, r = a.r;
+  const int r = a.r;
   const int blk = a.block_ids[blockIdx.x];
   if (blk < 0 || (int64_t)blk >= a.num_blocks) return;  // uniform for the workgroup
   const T* tile = reinterpret_cast<const T*>(a.k_pool) + ((int64_t)blk * a.Hkv + h) * (int64_t)P * D;
 
-  // ---- 1. keys -> LDS (transposed), centroid ----
+  // ---- 1. keys -> registers, centroid, centred keys -> LDS ----
   {
     constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
-    const int chunks = P * D / EPC;
-    for (int c = tid; c < chunks; c += 256) {
-      const int e0 = c * EPC;
-      const int i = e0 / D;
-      const int a0 = e0 - i * D;
-      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(tile + e0);
-      const T* v = reinterpret_cast<const T*>(&w);
+    constexpr int CPR = D / EPC;         // chunks per row
+    constexpr int NCHUNK = P * CPR;      // chunks in the tile
+    constexpr int NCH = (NCHUNK + 255) / 256;  // chunks per thread
+    static_assert(64 % CPR == 0 && (NCHUNK >= 256 ? NCHUNK % 256 == 0 : 256 % NCHUNK == 0), "chunk split");
+    u32x4_t raw[NCH];
 #pragma unroll
-      for (int x = 0; x < EPC; ++x) kt[(a0 + x) * KT_STRIDE + i] = v[x];
+    for (int m = 0; m < NCH; ++m) {
+      const int c = tid + 256 * m;
+      raw[m] = c < NCHUNK ? *reinterpret_cast<const u32x4_t*>(tile + (int64_t)c * EPC) : u32x4_t{0u, 0u, 0u, 0u};
     }
-  }
-  __syncthreads();
-  for (int d0 = tid; d0 < D; d0 += 256) {
-    float s = 0.f;
-    for (int i = 0; i < P; ++i) s += Elem<T>::load(&kt[d0 * KT_STRIDE + i]);
-    mu[d0] = s / (float)P;
-  }
-  __syncthreads();
-  if constexpr (sizeof(T) == 4) {  // fp32 keys: centre in place
-    for (int e = tid; e < D * P; e += 256) {
-      const int d0 = e / P, i = e - d0 * P;
-      kt[d0 * KT_STRIDE + i] -= mu[d0];
+    // thread t holds chunk column t % CPR of rows t / CPR + (256 / CPR) m
+    const int cc = tid % CPR;
+    float part[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) s += Elem<T>::load(reinterpret_cast<const T*>(&raw[m]) + e);
+      part[e] = s;
+    }
+    // lanes with the same chunk column are CPR apart: fold the wave, then the waves
+#pragma unroll
+    for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) part[e] += __shfl_xor(part[e], o, 64);
+    float* msum = &L.Gp[0][0][0];  // [4][D]
+    if (lane < CPR) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) msum[wave * D + cc * EPC + e] = part[e];
     }
     __syncthreads();
-  }
-
-  // ---- 2. Gram matrix: hreg[t][c][i] = H[16*tc + lane%16][16*c + 4*(lane/16) + i], tc = wave*RTW + t ----
-  f32x4_t hreg[RTW][NT];
+    if (tid < D) L.mu[tid] = ((msum[tid] + msum[D + tid]) + (msum[2 * D + tid] + msum[3 * D + tid])) / (float)P;
+    __syncthreads();
 #pragma unroll
-  for (int t = 0; t < RTW; ++t) {
-    const int tc = wave * RTW + t;
-#pragma unroll
-    for (int c = 0; c < NT; ++c) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < P; k0 += GramOp<T>::kStep)
-        acc = GramOp<T>::mfma(kt, KT_STRIDE, 16 * c, 16 * tc, k0, lane, acc);
+    for (int m = 0; m < NCH; ++m) {
+      if (tid + 256 * m >= NCHUNK) continue;
+      const int row = (tid + 256 * m) / CPR;
       if constexpr (sizeof(T) == 2) {
-        const float mrow = mu[16 * tc + (lane & 15)] * (float)P;
+        uint32_t wh[4], wl[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] -= mrow * mu[16 * c + 4 * (lane >> 4) + i];
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const uint32_t w = raw[m][e2];
+          const float d0 = bf16_lo(w) - L.mu[cc * 8 + 2 * e2];
+          const float d1 = bf16_hi(w) - L.mu[cc * 8 + 2 * e2 + 1];
+          const bf16_t h0 = f32_to_bf16(d0), h1 = f32_to_bf16(d1);
+          const bf16_t l0 = f32_to_bf16(d0 - bf16_to_f32(h0)), l1 = f32_to_bf16(d1 - bf16_to_f32(h1));
+          wh[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          wl[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        const int o = CentredKeys<T, D, P>::chunk_off(row, cc);
+        *reinterpret_cast<u32x4_t*>(&L.dk.hi[o]) = u32x4_t{wh[0], wh[1], wh[2], wh[3]};
+        *reinterpret_cast<u32x4_t*>(&L.dk.lo[o]) = u32x4_t{wl[0], wl[1], wl[2], wl[3]};
+      } else {
+        const float* f = reinterpret_cast<const float*>(&raw[m]);
+        const int o = CentredKeys<T, D, P>::chunk_off(row, cc);
+        *reinterpret_cast<f32x4_t*>(&L.dk.v[o]) =
+            f32x4_t{f[0] - L.mu[cc * 4], f[1] - L.mu[cc * 4 + 1], f[2] - L.mu[cc * 4 + 2], f[3] - L.mu[cc * 4 + 3]};
       }
-      hreg[t][c] = acc;
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. M = D D^T: wave w < NB holds hreg[I][i] = M[16 I + 4 lg + i][16 w + ln] ----
+  f32x4_t hreg[NB];
+  if (wave < NB) {
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+          const int oa = CentredKeys<T, D, P>::chunk_off(16 * I + ln, 4 * s + lg);
+          const int ob = CentredKeys<T, D, P>::chunk_off(16 * wave + ln, 4 * s + lg);
+          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&L.dk.hi[oa]);
+          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&L.dk.lo[oa]);
+          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&L.dk.hi[ob]);
+          const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&L.dk.lo[ob]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+        }
+      } else {
+#pragma unroll 8
+        for (int s = 0; s < D / 4; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(L.dk.at(16 * I + ln, 4 * s + lg), L.dk.at(16 * wave + ln, 4 * s + lg),
+                                                     acc, 0, 0, 0);
+      }
+      hreg[I] = acc;
     }
   }
 
-  // helpers ---------------------------------------------------------------
-  // Y = H X for this wave's rows; ytile[t][i] = Y[16*tc + 4*(lane/16) + i][lane%16]
-  auto matmul_hx = [&](f32x4_t* ytile) {
-#pragma unroll
-    for (int t = 0; t < RTW; ++t) ytile[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NT; ++c) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float bx = X[16 * c + 4 * (lane >> 4) + i][lane & 15];
-#pragma unroll
-        for (int t = 0; t < RTW; ++t)
-          ytile[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(hreg[t][c][i], bx, ytile[t], 0, 0, 0);
-      }
-    }
-  };
-  // partial Gram of the rows in `rows` (same layout as ytile) against `cols`
-  auto partial_gram = [&](const f32x4_t* rows, const f32x4_t* cols) {
-    f32x4_t m = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < RTW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = __builtin_amdgcn_mfma_f32_16x16x4f32(rows[t][i], cols[t][i], m, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Mp[wave][4 * (lane >> 4) + i][lane & 15] = m[i];
-  };
-  auto load_x_tiles = [&](f32x4_t* xt) {
-#pragma unroll
-    for (int t = 0; t < RTW; ++t) {
-      const int tc = wave * RTW + t;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xt[t][i] = X[16 * tc + 4 * (lane >> 4) + i][lane & 15];
-    }
-  };
-  auto store_y_tiles = [&](const f32x4_t* yt) {
-#pragma unroll
-    for (int t = 0; t < RTW; ++t) {
-      const int tc = wave * RTW + t;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Y[16 * tc + 4 * (lane >> 4) + i][lane & 15] = yt[t][i];
-    }
-  };
-  // Sum Mp into Ms[0] (wave 0), symmetrised.
-  auto reduce_gram = [&]() {
-    if (wave == 0) {
-      for (int e = lane; e < kBlk * kBlk; e += 64) {
-        const int i = e / kBlk, j = e % kBlk;
-        const float v = Mp[0][i][j] + Mp[1][i][j] + Mp[2][i][j] + Mp[3][i][j];
-        const float vt = Mp[0][j][i] + Mp[1][j][i] + Mp[2][j][i] + Mp[3][j][i];
-        Ms[0][i][j] = 0.5f * (v + vt);
-      }
-    }
-  };
-  auto rdl = [](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  // ---- helpers ----
   // Every wave, in registers (lane l holds row l & 15 of the block Gram M in
-  // a[]): column scaling S (columns with a vanishing norm are dead), Cholesky
+  // am[]): column scaling S (columns with a vanishing norm are dead), Cholesky
   // S M S = L L^T (right-looking; a column whose pivot vanishes is dead and
-  // gets L = unit column), then L^-1 column by column (lane c forms column c)
-  // and Ri = S L^-T with dead columns zeroed, written to this wave's RiW.
-  // Returns the dead-column mask (uniform).
+  // gets L = unit column), then L^-1 column by column and Ri = S L^-T with dead
+  // columns zeroed, written to this wave's RiW. Returns the dead-column mask
+  // (uniform).
   auto chol_rinv = [&](float* am) -> uint32_t {
-    const int row = lane & 15;
+    const int row = ln;
     float sd[kBlk];
     float dmax = 0.f;
 #pragma unroll
@@ -265,165 +294,278 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
     // Ri[row][j] = s_row * (L^-1)[j][row] for j >= row, live j
     if (lane < kBlk) {
 #pragma unroll
-      for (int j = 0; j < kBlk; ++j) RiW[wave][row][j] = (j >= row && !((dead >> j) & 1u)) ? srow * li[j] : 0.f;
+      for (int j = 0; j < kBlk; ++j) L.RiW[wave][row][j] = (j >= row && !((dead >> j) & 1u)) ? srow * li[j] : 0.f;
     }
     return dead;
   };
-  // One Cholesky-QR pass of the block Y whose rows owned by this wave are in
-  // yt: X = Y Ri for the wave's rows (matrix cores), dead columns replaced by
-  // fresh pseudo-random vectors, X -> LDS. Two workgroup barriers.
-  auto cholqr = [&](const f32x4_t* yt, uint32_t salt) {
-    store_y_tiles(yt);  // read back below by this wave only
-    partial_gram(yt, yt);
-    __syncthreads();
-    float am[kBlk];
-    {
-      const int row = lane & 15;
+
+  // Cholesky-QR of the NR x 16 rows in `buf` (LDS, row-major), in place: wave
+  // w takes the 16-row tiles w, w + 4, ...; dead columns become pseudo-random
+  // vectors (call again to orthonormalise those). Two workgroup barriers;
+  // returns the dead-column mask (uniform).
+  auto cholqr = [&](float (*buf)[kBlk], int NR, uint32_t salt) -> uint32_t {
+    f32x4_t m = {0.f, 0.f, 0.f, 0.f};
+    for (int t = wave; t < NR / 16; t += 4) {
 #pragma unroll
-      for (int c = 0; c < kBlk; c += 4) {
-        f32x4_t v = *reinterpret_cast<const f32x4_t*>(&Mp[0][row][c]);
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-          const f32x4_t u = *reinterpret_cast<const f32x4_t*>(&Mp[w][row][c]);
-          v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
-        }
-        am[c] = v[0]; am[c + 1] = v[1]; am[c + 2] = v[2]; am[c + 3] = v[3];
+      for (int i = 0; i < 4; ++i) {
+        const float v = buf[16 * t + 4 * lg + i][ln];
+        m = __builtin_amdgcn_mfma_f32_16x16x4f32(v, v, m, 0, 0, 0);
       }
     }
-    const uint32_t dead = chol_rinv(am);
-    wave_lds_sync();  // RiW[wave] and this wave's Y rows are visible to the wave
-    const bool dcol = (dead >> (lane & 15)) & 1u;
 #pragma unroll
-    for (int t = 0; t < RTW; ++t) {
-      const int tc = wave * RTW + t;
+    for (int i = 0; i < 4; ++i) L.Gp[wave][4 * lg + i][ln] = m[i];
+    __syncthreads();
+    float am[kBlk];
+#pragma unroll
+    for (int c = 0; c < kBlk; c += 4) {
+      f32x4_t v = *reinterpret_cast<const f32x4_t*>(&L.Gp[0][ln][c]);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const f32x4_t u = *reinterpret_cast<const f32x4_t*>(&L.Gp[w][ln][c]);
+        v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
+      }
+      am[c] = v[0]; am[c + 1] = v[1]; am[c + 2] = v[2]; am[c + 3] = v[3];
+    }
+    const uint32_t dead = chol_rinv(am);
+    wave_lds_sync();  // RiW[wave] visible to the wave
+    const bool dcol = (dead >> ln) & 1u;
+    for (int t = wave; t < NR / 16; t += 4) {
       f32x4_t x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k0 = 0; k0 < kBlk; k0 += 4)
-        x = __builtin_amdgcn_mfma_f32_16x16x4f32(Y[16 * tc + (lane & 15)][k0 + (lane >> 4)],
-                                                 RiW[wave][k0 + (lane >> 4)][lane & 15], x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(buf[16 * t + ln][k0 + lg], L.RiW[wave][k0 + lg][ln], x, 0, 0, 0);
+      wave_lds_sync();  // every lane's reads of the tile are done before it is overwritten
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * tc + 4 * (lane >> 4) + i;
-        X[row][lane & 15] = dcol ? hash_unit((uint32_t)row, (uint32_t)(lane & 15), salt) : x[i];
+        const int row = 16 * t + 4 * lg + i;
+        buf[row][ln] = dcol ? hash_unit((uint32_t)row, (uint32_t)ln, salt) : x[i];
       }
     }
-    __syncthreads();  // X complete
+    __syncthreads();
+    return dead;
   };
 
-  // ---- 3. subspace iteration ----
-  f32x4_t yt[RTW];
+  // Y = M X for this wave's rows (wave < NB): lane (ln, lg) -> Y[16 wave + 4 lg + i][ln]
+  auto product = [&]() {
+    if (wave < NB) {
+      f32x4_t y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int t = 0; t < RTW; ++t) {
-    const int tc = wave * RTW + t;
+      for (int I = 0; I < NB; ++I)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      yt[t][i] = hash_unit((uint32_t)(16 * tc + 4 * (lane >> 4) + i), (uint32_t)(lane & 15), 1u);
-  }
-  cholqr(yt, 2u);
-  for (int it = 0; it < kBuildIters; ++it) {
-    matmul_hx(yt);
-    cholqr(yt, 3u + (uint32_t)it);
-  }
-  // second pass for orthonormality
-  load_x_tiles(yt);
-  cholqr(yt, 101u);
-
-  // ---- 4. Rayleigh-Ritz: T = X^T H X, diagonalised by cyclic Jacobi ----
-  int cur = 0;
-  {
-    f32x4_t xt[RTW];
-    load_x_tiles(xt);
-    matmul_hx(yt);
-    partial_gram(xt, yt);
-    __syncthreads();
-    reduce_gram();  // Ms[0] = T (symmetrised)
-    if (wave == 0) {
-      for (int e = lane; e < kBlk * kBlk; e += 64) Wm[0][e / kBlk][e % kBlk] = (e / kBlk == e % kBlk) ? 1.f : 0.f;
-      wave_lds_sync();
-      // Each round rotates 8 disjoint index pairs (round-robin schedule) at
-      // once: T <- R T R^T, W <- W R^T in one pass per element into the other
-      // buffer. A pair is rotated only while its off-diagonal entry is
-      // significant both against its own diagonal entries and against 1e-7
-      // of the trace (fp32 rounding leaves about one ulp of the largest
-      // eigenvalue behind); the sweeps stop after one in which no pair was.
-      float tr = lane < kBlk ? Ms[0][lane][lane] : 0.f;
+        for (int i = 0; i < 4; ++i)
+          y = __builtin_amdgcn_mfma_f32_16x16x4f32(hreg[I][i], L.X[16 * I + 4 * lg + i][ln], y, 0, 0, 0);
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o, 64);
-      const float floor_abs = 1e-7f * fabsf(tr);
-      const int ey = lane & 15;  // this lane's column in the update pass
-      for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
-        bool any = false;
-        for (int rnd = 0; rnd < kBlk - 1; ++rnd) {
-          if (lane < 8) {
-            int p, q;
-            if (lane == 0) { p = kBlk - 1; q = rnd; }
-            else { p = (rnd + lane) % (kBlk - 1); q = (rnd - lane + (kBlk - 1)) % (kBlk - 1); }
-            const float apq = Ms[cur][p][q];
-            const float app = Ms[cur][p][p], aqq = Ms[cur][q][q];
-            float c = 1.f, sn = 0.f;
-            if (fabsf(apq) > floor_abs && fabsf(apq) > 1e-6f * sqrtf(fabsf(app * aqq))) {
-              any = true;
-              const float theta = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
-              const float tt = (theta >= 0.f ? 1.f : -1.f) *
-                               __builtin_amdgcn_rcpf(fabsf(theta) + sqrtf(theta * theta + 1.f));
-              c = __builtin_amdgcn_rsqf(tt * tt + 1.f);
-              sn = tt * c;
-            }
-            jsc[p] = c; joc[p] = -sn; jpt[p] = q;
-            jsc[q] = c; joc[q] = sn;  jpt[q] = p;
-          }
-          wave_lds_sync();
-          {
-            const int py = jpt[ey];
-            const float sy = jsc[ey], oy = joc[ey];
-#pragma unroll
-            for (int k = 0; k < kBlk * kBlk / 64; ++k) {
-              const int x = (lane >> 4) + 4 * k;
-              const int px = jpt[x];
-              const float sx = jsc[x], ox = joc[x];
-              Ms[cur ^ 1][x][ey] = sx * (sy * Ms[cur][x][ey] + oy * Ms[cur][x][py]) +
-                                   ox * (sy * Ms[cur][px][ey] + oy * Ms[cur][px][py]);
-              Wm[cur ^ 1][x][ey] = sy * Wm[cur][x][ey] + oy * Wm[cur][x][py];
-            }
-          }
-          wave_lds_sync();
-          cur ^= 1;
-        }
-        if (!__builtin_amdgcn_ballot_w64(any)) break;
-      }
-      // descending order of the Ritz values, ties by index
-      if (lane < kBlk) {
-        const float v = Ms[cur][lane][lane];
-        int rank = 0;
-        for (int j = 0; j < kBlk; ++j) {
-          const float u = Ms[cur][j][j];
-          rank += (u > v || (u == v && j < lane)) ? 1 : 0;
-        }
-        order[rank] = lane;
-      }
+      for (int i = 0; i < 4; ++i) L.Y[16 * wave + 4 * lg + i][ln] = y[i];
     }
-    if (tid == 0) cur_s = cur;
-    __syncthreads();
-  }
-  const int cw = cur_s;
-  // V = X W[:, order[0..r-1]] into Y[:, 0..r-1]
-  for (int e = tid; e < D * kBlk; e += 256) {
-    const int row = e / kBlk, rho = e % kBlk;
-    if (rho < r) {
-      const int col = order[rho];
-      float s = 0.f;
+  };
+
+  // Parallel cyclic Jacobi on the 16 x 16 T in Ms[0] (all 256 threads,
+  // thread (x, y) owns T[x][y] and W[x][y]): round t rotates the 8 disjoint
+  // pairs {p, p ^ t}, T <- J^T T J and W <- W J in one pass per element into
+  // the other buffer. The 8 threads owning the next round's off-diagonal
+  // entries also form the three entries of their pair that the next rotation
+  // needs and publish it with their own update, so a round costs one barrier.
+  // A pair is rotated only while its off-diagonal entry exceeds kJacobiRel of
+  // sqrt(|t_pp t_qq|) and 2^-20 of the trace (below that the entries are fp32
+  // rounding of the rotations and move no eigenvector whose eigen-gap is
+  // significant); the sweeps stop after one whose largest rotated relative
+  // entry is below kJacobiStop (the next sweep's would be of its square).
+  // Then Wo = W in descending order of eigenvalue, th = those eigenvalues.
+  auto jacobi = [&]() {
+    const int jx = tid >> 4, jy = tid & 15;
+    float tr = 0.f;
 #pragma unroll
-      for (int j = 0; j < kBlk; ++j) s += X[row][j] * Wm[cw][j][col];
-      Y[row][rho] = s;
+    for (int i = 0; i < kBlk; ++i) tr += L.Ms[0][i][i];
+    const float floor_abs = 0x1p-20f * fabsf(tr);
+    // rotation of the pair (p, q = p ^ t), p < q, from entries app, aqq, apq
+    auto publish = [&](int buf, int p, int q, float app, float aqq, float apq, int sb) {
+      float c = 1.f, sn = 0.f;
+      if (fabsf(apq) > floor_abs && fabsf(apq) > kJacobiRel * __builtin_amdgcn_sqrtf(fabsf(app * aqq))) {
+        const float theta = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
+        const float tt = (theta >= 0.f ? 1.f : -1.f) *
+                         __builtin_amdgcn_rcpf(fabsf(theta) + __builtin_amdgcn_sqrtf(theta * theta + 1.f));
+        c = __builtin_amdgcn_rsqf(tt * tt + 1.f);
+        sn = tt * c;
+        const float rel = fabsf(apq) * __builtin_amdgcn_rsqf(fmaxf(fabsf(app * aqq), 1e-30f));
+        atomicMax(&L.swmax[sb], __float_as_uint(fminf(rel, 1e30f)));
+      }
+      L.jc[buf][p] = c; L.jo[buf][p] = -sn;
+      L.jc[buf][q] = c; L.jo[buf][q] = sn;
+    };
+    L.Wm[0][jx][jy] = jx == jy ? 1.f : 0.f;
+    if (tid < 2) L.swmax[tid] = 0u;
+    __syncthreads();
+    if ((jy == (jx ^ 1)) && jx < jy) publish(0, jx, jy, L.Ms[0][jx][jx], L.Ms[0][jy][jy], L.Ms[0][jx][jy], 0);
+    __syncthreads();
+    int cur = 0, cb = 0;
+    for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
+      const int sb = sweep & 1;
+#pragma unroll
+      for (int t = 1; t < kBlk; ++t) {
+        const float (*A)[kBlk + 1] = L.Ms[cur];
+        const float* jcc = L.jc[cb];
+        const float* joc = L.jo[cb];
+        auto rotated = [&](int x, int y) {
+          const int px = x ^ t, py = y ^ t;
+          const float sx = jcc[x], ox = joc[x], sy = jcc[y], oy = joc[y];
+          return sx * (sy * A[x][y] + oy * A[x][py]) + ox * (sy * A[px][y] + oy * A[px][py]);
+        };
+        const float v = rotated(jx, jy);
+        const float w = jcc[jy] * L.Wm[cur][jx][jy] + joc[jy] * L.Wm[cur][jx][jy ^ t];
+        // the next round's pair of this thread's entry, when it is that pair's off-diagonal
+        const int tn = t == kBlk - 1 ? 1 : t + 1;
+        const int sbn = t == kBlk - 1 ? sb ^ 1 : sb;
+        if ((jy == (jx ^ tn)) && jx < jy)
+          publish(cb ^ 1, jx, jy, rotated(jx, jx), rotated(jy, jy), v, sbn);
+        L.Ms[cur ^ 1][jx][jy] = v;
+        L.Wm[cur ^ 1][jx][jy] = w;
+        // the next sweep's maximum starts at 0: cleared in round 2, after every
+        // thread has read this slot for the previous sweep's stop test, and
+        // before round 15 publishes into it
+        if (t == 2 && tid == 0) L.swmax[sb ^ 1] = 0u;
+        __syncthreads();
+        cur ^= 1;
+        cb ^= 1;
+      }
+      // uniform: every thread reads the same word after the barrier
+      if (__uint_as_float(L.swmax[sb]) < kJacobiStop) break;
+    }
+    // descending order of the eigenvalues, ties by index
+    if (tid < kBlk) {
+      const float v = L.Ms[cur][tid][tid];
+      int rank = 0;
+      for (int j = 0; j < kBlk; ++j) {
+        const float u = L.Ms[cur][j][j];
+        rank += (u > v || (u == v && j < tid)) ? 1 : 0;
+      }
+      L.order[rank] = tid;
+      L.th[rank] = v;
+    }
+    __syncthreads();
+    L.Wo[jx][jy] = L.Wm[cur][jx][L.order[jy]];
+  };
+
+  // ---- 3. top-r eigenvectors of M into X ----
+  int products = 0;
+  bool converged = false;
+  if constexpr (NB == 1) {
+    for (int e = tid; e < kBlk * kBlk; e += 256) L.X[e / kBlk][e % kBlk] = (e / kBlk == e % kBlk) ? 1.f : 0.f;
+  } else {
+    // an orthonormal start without a factorisation: 16 columns of the
+    // P x P Sylvester-Hadamard matrix, rows with pseudo-random signs, / sqrt(P)
+    const float inv = 1.0f / sqrtf((float)P);
+    for (int e = tid; e < P * kBlk; e += 256) {
+      const int i = e / kBlk, j = e % kBlk;
+      const float sg = hash_unit((uint32_t)i, 0u, 1u) < 0.f ? -inv : inv;
+      L.X[i][j] = (__builtin_popcount(i & j) & 1) ? -sg : sg;
     }
   }
   __syncthreads();
+  const int first_rr = NB == 1 ? 1 : kFirstRitzCheck;
+  while (true) {
+    product();
+    ++products;
+    if (products < first_rr) {
+      __syncthreads();
+      for (int e = tid; e < P * kBlk; e += 256) L.X[e / kBlk][e % kBlk] = L.Y[e / kBlk][e % kBlk];
+      __syncthreads();
+      cholqr(L.X, P, 3u + (uint32_t)products);
+      continue;
+    }
+    // Rayleigh-Ritz: T = X^T Y (waves < NB each its rows), summed and symmetrised by wave 0
+    {
+      f32x4_t m = {0.f, 0.f, 0.f, 0.f};
+      if (wave < NB) {
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          m = __builtin_amdgcn_mfma_f32_16x16x4f32(L.X[16 * wave + 4 * lg + i][ln], L.Y[16 * wave + 4 * lg + i][ln], m,
+                                                   0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.Gp[wave][4 * lg + i][ln] = m[i];
+    }
+    __syncthreads();
+    {
+      const int i = tid >> 4, j = tid & 15;
+      const float v = (L.Gp[0][i][j] + L.Gp[1][i][j]) + (L.Gp[2][i][j] + L.Gp[3][i][j]);
+      const float vt = (L.Gp[0][j][i] + L.Gp[1][j][i]) + (L.Gp[2][j][i] + L.Gp[3][j][i]);
+      L.Ms[0][i][j] = 0.5f * (v + vt);
+    }
+    __syncthreads();
+    jacobi();
+    __syncthreads();
+    // Ritz vectors U = X Wo (into X) and M U = Y Wo (into Y); residual norms of the r leading pairs
+    {
+      float r2 = 0.f;
+      if (wave < NB) {
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < kBlk; k0 += 4) {
+          const float wo = L.Wo[k0 + lg][ln];
+          z = __builtin_amdgcn_mfma_f32_16x16x4f32(L.Y[16 * wave + ln][k0 + lg], wo, z, 0, 0, 0);
+          u = __builtin_amdgcn_mfma_f32_16x16x4f32(L.X[16 * wave + ln][k0 + lg], wo, u, 0, 0, 0);
+        }
+        const float thn = L.th[ln];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = z[i] - thn * u[i];
+          r2 = fmaf(e, e, r2);
+        }
+        wave_lds_sync();  // reads of the X and Y rows done before they are overwritten
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          L.X[16 * wave + 4 * lg + i][ln] = u[i];
+          L.Y[16 * wave + 4 * lg + i][ln] = z[i];
+        }
+      }
+      r2 += __shfl_xor(r2, 16, 64);
+      r2 += __shfl_xor(r2, 32, 64);
+      if (lane < kBlk) L.res[wave][lane] = r2;
+    }
+    __syncthreads();
+    {
+      // the same decision in every thread (uniform): every leading pair within
+      // the backward bound, and every leading subspace whose Ritz gap is
+      // significant within the sin-theta bound ||R_m||_F <= kSubspaceTol * gap
+      const float th0 = fmaxf(L.th[0], 0.f);
+      const float pair2 = (kRitzTol * th0) * (kRitzTol * th0);
+      float acc2 = 0.f;
+      bool ok = true;
+      for (int m = 1; m <= r; ++m) {
+        const float rm2 = (L.res[0][m - 1] + L.res[1][m - 1]) + (L.res[2][m - 1] + L.res[3][m - 1]);
+        acc2 += rm2;
+        ok = ok && rm2 <= pair2;
+        const float gap = L.th[m - 1] - L.th[m];
+        if (gap > kGapFloor * th0) ok = ok && acc2 <= (kSubspaceTol * gap) * (kSubspaceTol * gap);
+      }
+      converged = NB == 1 || ok;
+    }
+    if (converged || products >= kMaxProducts) break;
+    // continue from M U
+    for (int e = tid; e < P * kBlk; e += 256) L.X[e / kBlk][e % kBlk] = L.Y[e / kBlk][e % kBlk];
+    __syncthreads();
+    cholqr(L.X, P, 50u + (uint32_t)products);
+  }
+  if (tid == 0 && a.fit_info) a.fit_info[(int64_t)blockIdx.x * a.Hkv + h] = converged ? products : -products;
+
+  // ---- 4. V = D^T U (columns beyond r are Ritz vectors too and are carried along) ----
+  for (int b = wave; b < DB; b += 4) {
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = 0; s < P / 4; ++s)
+      v = __builtin_amdgcn_mfma_f32_16x16x4f32(L.dk.at(4 * s + lg, 16 * b + ln), L.X[4 * s + lg][ln], v, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L.Vb[16 * b + 4 * lg + i][ln] = v[i];
+  }
+  __syncthreads();
+  if (cholqr(L.Vb, D, 101u)) cholqr(L.Vb, D, 102u);  // a replaced column is orthonormalised by a second pass
   // sign: largest-magnitude entry positive (lowest index on ties)
   for (int rho = wave; rho < r; rho += 4) {
     float best = -1.f;
     int arg = D;
     for (int row = lane; row < D; row += 64) {
-      const float m = fabsf(Y[row][rho]);
+      const float m = fabsf(L.Vb[row][rho]);
       if (m > best) { best = m; arg = row; }
     }
     for (int o = 32; o > 0; o >>= 1) {
@@ -432,40 +574,42 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
       if (ob > best || (ob == best && oa < arg)) { best = ob; arg = oa; }
     }
     if (arg >= D) arg = 0;  // only when every entry is NaN
-    const float sg = Y[arg][rho] < 0.f ? -1.f : 1.f;
+    const float sg = L.Vb[arg][rho] < 0.f ? -1.f : 1.f;
     wave_lds_sync();
-    for (int row = lane; row < D; row += 64) Y[row][rho] *= sg;
+    for (int row = lane; row < D; row += 64) L.Vb[row][rho] *= sg;
   }
   __syncthreads();
 
-  // ---- 5. C = D V and the record ----
+  // ---- 5. C = D V (wave w < NB, rows 16 w ..), into Y; then the record ----
+  if (wave < NB) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int s = 0; s < D / 4; ++s)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(L.dk.at(16 * wave + ln, 4 * s + lg), L.Vb[4 * s + lg][ln], c, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L.Y[16 * wave + 4 * lg + i][ln] = c[i];
+  }
+  __syncthreads();
+
   if constexpr (I4) {
-    float* Cs = &X[0][0];      // C [P][r]; X is free from here on
-    float* sq = &Mp[0][0][0];  // scales in record order: basis vectors, centroid, tokens
-    for (int e = tid; e < P * r; e += 256) {
-      const int i = e / r, rho = e - i * r;
-      float s = 0.f;
-      for (int d0 = 0; d0 < D; ++d0) s = fmaf(Elem<T>::load(&kt[d0 * KT_STRIDE + i]) - mu[d0], Y[d0][rho], s);
-      Cs[e] = s;
-    }
-    __syncthreads();
+    float* sq = &L.Gp[0][0][0];  // scales in record order: basis vectors, centroid, tokens
     // group scales: the waves take the basis vectors and the centroid, the
     // first P threads their token's coefficient row
     for (int gi = wave; gi < r + 1; gi += 4) {
       float m = 0.f;
-      for (int row = lane; row < D; row += 64) m = fmaxf(m, fabsf(gi == r ? mu[row] : Y[row][gi]));
+      for (int row = lane; row < D; row += 64) m = fmaxf(m, fabsf(gi == r ? L.mu[row] : L.Vb[row][gi]));
       for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       if (lane == 0) sq[gi] = bf16_to_f32(f32_to_bf16(m / (gi == r ? 127.f : 7.f)));
     }
     if (tid < P) {
       float m = 0.f;
-      for (int rho = 0; rho < r; ++rho) m = fmaxf(m, fabsf(Cs[tid * r + rho]));
+      for (int rho = 0; rho < r; ++rho) m = fmaxf(m, fabsf(L.Y[tid][rho]));
       sq[r + 1 + tid] = bf16_to_f32(f32_to_bf16(m / 127.f));
     }
     __syncthreads();
-    auto code = [](float x, float s, float L) -> int {
+    auto code = [](float x, float s, float Lv) -> int {
       if (!(s > 0.f)) return 0;
-      return (int)fminf(fmaxf(__builtin_rintf(x / s), -L), L);
+      return (int)fminf(fmaxf(__builtin_rintf(x / s), -Lv), Lv);
     };
     uint8_t* rec = a.sum_pool + ((int64_t)blk * a.Hkv + h) * a.rec_bytes;
     constexpr int WPR = D / 8;  // 32-bit words per nibble row
@@ -478,9 +622,9 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
         const int el = st * 32 + kg * 8 + e;
         uint32_t nib;
         if (row < r) {
-          nib = (uint32_t)(code(Y[el][row], sq[row], 7.f) + 8);
+          nib = (uint32_t)(code(L.Vb[el][row], sq[row], 7.f) + 8);
         } else {
-          const uint32_t byte = (uint32_t)(code(mu[el], sq[r], 127.f) + 128);
+          const uint32_t byte = (uint32_t)(code(L.mu[el], sq[r], 127.f) + 128);
           nib = row == r ? byte >> 4 : byte & 15u;
         }
         word |= nib << (4 * ((e & 1) ? 4 + (e >> 1) : (e >> 1)));
@@ -488,42 +632,50 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
       *reinterpret_cast<uint32_t*>(rec + row * (D / 2) + wi * 4) = word;
     }
     uint8_t* crec = rec + (r + 2) * (D / 2);
-    for (int e = tid; e < P * r; e += 256) crec[e] = (uint8_t)(code(Cs[e], sq[r + 1 + e / r], 127.f) + 128);
+    for (int e = tid; e < P * r; e += 256) {
+      const int i = e / r, rho = e - i * r;
+      crec[e] = (uint8_t)(code(L.Y[i][rho], sq[r + 1 + i], 127.f) + 128);
+    }
     bf16_t* srec = reinterpret_cast<bf16_t*>(crec + P * r);
     for (int t = tid; t < 1 + r + P; t += 256) srec[t] = f32_to_bf16(sq[t]);
     for (int t = (r + 2) * (D / 2) + P * r + 2 * (1 + r + P) + tid; t < a.rec_bytes; t += 256) rec[t] = 0;
     return;
   }
   T* rec = reinterpret_cast<T*>(a.sum_pool) + ((int64_t)blk * a.Hkv + h) * a.rec_elems;
-  for (int d0 = tid; d0 < D; d0 += 256) rec[d0] = Elem<T>::from_f32(mu[d0]);
+  for (int d0 = tid; d0 < D; d0 += 256) rec[d0] = Elem<T>::from_f32(L.mu[d0]);
   for (int e = tid; e < r * D; e += 256) {
     const int rho = e / D, d0 = e - rho * D;
-    rec[D + e] = Elem<T>::from_f32(Y[d0][rho]);
+    rec[D + e] = Elem<T>::from_f32(L.Vb[d0][rho]);
   }
   T* crec = rec + (int64_t)D * (1 + r);
   for (int e = tid; e < P * r; e += 256) {
     const int i = e / r, rho = e - i * r;
-    float s = 0.f;
-    for (int d0 = 0; d0 < D; ++d0) {
-      float kv = Elem<T>::load(&kt[d0 * KT_STRIDE + i]);
-      if constexpr (sizeof(T) == 2) kv -= mu[d0];
-      s = fmaf(kv, Y[d0][rho], s);
-    }
-    crec[e] = Elem<T>::from_f32(s);
+    crec[e] = Elem<T>::from_f32(L.Y[i][rho]);
   }
 }
+
+namespace {
+template <typename T, int D, bool I4>
+void launch_p(const BuildArgs& a, dim3 grid, hipStream_t stream) {
+  switch (a.P) {
+    case 16: hipLaunchKernelGGL((build_kernel<T, D, 16, I4>), grid, dim3(256), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((build_kernel<T, D, 32, I4>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((build_kernel<T, D, 64, I4>), grid, dim3(256), 0, stream, a); break;
+  }
+}
+}  // namespace
 
 hipError_t launch_build(const BuildArgs& a, int dtype, int D, bool i4, hipStream_t stream) {
   dim3 grid(a.n, a.Hkv);
   if (dtype == 0 && i4) {
-    if (D == 64) hipLaunchKernelGGL((build_kernel<bf16_t, 64, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((build_kernel<bf16_t, 128, true>), grid, dim3(256), 0, stream, a);
+    if (D == 64) launch_p<bf16_t, 64, true>(a, grid, stream);
+    else launch_p<bf16_t, 128, true>(a, grid, stream);
   } else if (dtype == 0) {
-    if (D == 64) hipLaunchKernelGGL((build_kernel<bf16_t, 64, false>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((build_kernel<bf16_t, 128, false>), grid, dim3(256), 0, stream, a);
+    if (D == 64) launch_p<bf16_t, 64, false>(a, grid, stream);
+    else launch_p<bf16_t, 128, false>(a, grid, stream);
   } else {
-    if (D == 64) hipLaunchKernelGGL((build_kernel<float, 64, false>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((build_kernel<float, 128, false>), grid, dim3(256), 0, stream, a);
+    if (D == 64) launch_p<float, 64, false>(a, grid, stream);
+    else launch_p<float, 128, false>(a, grid, stream);
   }
   return hipGetLastError();
 }

@@ -54,6 +54,7 @@ struct BuildArgs {
   int64_t num_blocks;
   int64_t rec_elems;          // elements per record (bf16 / fp32 records)
   int64_t rec_bytes;          // bytes per record
+  int32_t* fit_info;          // [n][Hkv] products of the eigensolver (negative: bound not met), or null
   int Hkv, P, r, n;
 };
 

@@ -266,6 +266,12 @@ int locks_workspace_size(const locks_config_t* cfg, int32_t batch, int32_t max_p
 int locks_build_summaries(const locks_config_t* cfg, const void* k_pool, int64_t num_blocks,
                           const int32_t* block_ids, int32_t n_ids, void* summary_pool,
                           hipStream_t stream) {
+  return locks_build_summaries_ex(cfg, k_pool, num_blocks, block_ids, n_ids, summary_pool, nullptr, stream);
+}
+
+int locks_build_summaries_ex(const locks_config_t* cfg, const void* k_pool, int64_t num_blocks,
+                             const int32_t* block_ids, int32_t n_ids, void* summary_pool,
+                             int32_t* fit_info, hipStream_t stream) {
   int st = check_config(cfg);
   if (st != LOCKS_OK) return st;
   if (n_ids < 0 || num_blocks < 0) return LOCKS_E_INVALID_ARG;
@@ -279,6 +285,7 @@ int locks_build_summaries(const locks_config_t* cfg, const void* k_pool, int64_t
   a.num_blocks = num_blocks;
   a.rec_elems = rec_elems(cfg);
   a.rec_bytes = rec_bytes(cfg);
+  a.fit_info = fit_info;
   a.Hkv = cfg->num_kv_heads;
   a.P = cfg->page_size;
   a.r = cfg->rank;

@@ -26,7 +26,8 @@ LOCKS_I4 = 2  # summary dtype only: 4-bit basis, 8-bit centroid and coefficients
 
 # every exported entry point declared in include/locks.h
 EXPORTED = ("locks_status_string", "locks_version", "locks_summary_record_bytes",
-            "locks_workspace_size", "locks_build_summaries", "locks_page_score",
+            "locks_workspace_size", "locks_build_summaries", "locks_build_summaries_ex",
+            "locks_page_score",
             "locks_select_pages", "locks_score_select", "locks_sparse_decode",
             "locks_decode_step")
 
@@ -80,6 +81,7 @@ def lib():
         L.locks_summary_record_bytes.restype = sz
         L.locks_workspace_size.argtypes = [cp, i32, i32, ctypes.POINTER(sz)]
         L.locks_build_summaries.argtypes = [cp, vp, i64, vp, i32, vp, vp]
+        L.locks_build_summaries_ex.argtypes = [cp, vp, i64, vp, i32, vp, vp, vp]
         L.locks_page_score.argtypes = [cp, vp, vp, i64, vp, vp, i32, i32, vp, vp]
         L.locks_select_pages.argtypes = [cp, vp, vp, i32, i32, vp, vp, vp]
         L.locks_score_select.argtypes = [cp, vp, vp, i64, vp, vp, i32, i32, vp, vp, sz, vp]
@@ -87,7 +89,8 @@ def lib():
                                           sz, vp]
         L.locks_decode_step.argtypes = [cp, vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp, vp,
                                         sz, vp]
-        for name in ("locks_workspace_size", "locks_build_summaries", "locks_page_score",
+        for name in ("locks_workspace_size", "locks_build_summaries", "locks_build_summaries_ex",
+                     "locks_page_score",
                      "locks_select_pages", "locks_score_select", "locks_sparse_decode",
                      "locks_decode_step"):
             getattr(L, name).restype = ctypes.c_int
@@ -151,6 +154,14 @@ def locks_build_summaries(cfg, k_pool, num_blocks, block_ids, n_ids, summary_poo
            lib().locks_build_summaries(ctypes.byref(cfg), _ptr(k_pool), int(num_blocks),
                                        _ptr(block_ids), int(n_ids), _ptr(summary_pool),
                                        _stream(stream)))
+
+
+def locks_build_summaries_ex(cfg, k_pool, num_blocks, block_ids, n_ids, summary_pool, fit_info,
+                             stream=None):
+    _check("locks_build_summaries_ex",
+           lib().locks_build_summaries_ex(ctypes.byref(cfg), _ptr(k_pool), int(num_blocks),
+                                          _ptr(block_ids), int(n_ids), _ptr(summary_pool),
+                                          _ptr(fit_info), _stream(stream)))
 
 
 def locks_page_score(cfg, q, summary_pool, num_blocks, block_table, seq_lens, batch, max_pages,

@@ -105,7 +105,10 @@ def unit_records(wl, cfg, pool_cpu, bt, b, h, n):
 # --------------------------------------------------------------------------
 # GPU stages
 # --------------------------------------------------------------------------
-def gpu_build(wl, cfg, g, block_ids=None):
+def gpu_build(wl, cfg, g, block_ids=None, fits=None):
+    """GPU fit of the given block ids (default: every complete page). The fit
+    report of every tile must say converged; `fits` (a list) receives the
+    per-tile product counts."""
     pool = L.summary_pool_for(cfg, wl.num_blocks, DEV)
     pool.zero_()
     if block_ids is None:
@@ -114,7 +117,15 @@ def gpu_build(wl, cfg, g, block_ids=None):
             _, _, Jc = lens(wl, b)
             ids += g["block_table"][b, :Jc].tolist()
         block_ids = torch.tensor(ids, dtype=torch.int32, device=DEV)
-    L.locks_build_summaries(cfg, g["k_pool"], wl.num_blocks, block_ids, block_ids.numel(), pool)
+    info = torch.zeros((max(1, block_ids.numel()), wl.num_kv_heads), dtype=torch.int32, device=DEV)
+    L.locks_build_summaries_ex(cfg, g["k_pool"], wl.num_blocks, block_ids, block_ids.numel(), pool, info)
+    if block_ids.numel():
+        info = info[:block_ids.numel()].cpu()
+        valid = ((block_ids >= 0) & (block_ids < wl.num_blocks)).cpu()
+        got = info[valid]
+        assert bool((got > 0).all()), f"{int((got <= 0).sum())} fits did not meet the Ritz residual bound"
+        if fits is not None:
+            fits.extend(got.reshape(-1).tolist())
     return pool
 
 
@@ -305,8 +316,11 @@ def check_all_outputs(wl, data, out_c, sel_c, threads=HOST_THREADS):
 # App. A.2 Cor. 1: the top-r right singular subspace of the centred page)
 # --------------------------------------------------------------------------
 FIT_ENERGY_SLACK = 1e-3   # of the page's total centred energy
-FIT_SUBSPACE_TOL = 2e-2   # sine of the angles (Frobenius) to the oracle's leading subspace
-FIT_GAP = 0.2             # relative eigen-gap that makes a leading subspace well defined
+FIT_SUBSPACE_TOL = 3e-2   # sine of the angles (Frobenius) to the oracle's leading subspace
+FIT_GAP = 0.2             # relative eigen-gap that makes a leading subspace well defined ...
+FIT_GAP_ABS = 2.0 ** -6   # ... and its gap against the largest eigenvalue (the stored keys' own
+                          # bf16 rounding moves the Gram by ~2^-8 of it, so smaller gaps leave the
+                          # subspace undetermined by the data)
 
 
 def check_fit(keys, vt_stored, ev_o, vt_o, r, energy_slack=FIT_ENERGY_SLACK, subspace_tol=FIT_SUBSPACE_TOL):
@@ -315,8 +329,9 @@ def check_fit(keys, vt_stored, ev_o, vt_o, r, energy_slack=FIT_ENERGY_SLACK, sub
     its basis. With Q an orthonormal basis of the stored span (QR):
       * Eckart-Young: ||D - D Q Q^T||_F^2 <= sum_{l > r} ev_l + slack * sum ev;
       * every leading oracle subspace of size m <= r that is separated from
-        the next eigenvalue by a relative gap lies in span(Q) up to the
-        tolerance (||(I - Q Q^T) V_o[:m]||_F).
+        the next eigenvalue by a gap both relative to its own eigenvalue and
+        against the largest one lies in span(Q) up to the tolerance
+        (||(I - Q Q^T) V_o[:m]||_F).
     Returns the number of leading subspaces checked."""
     keys = np.asarray(keys, dtype=np.float64)
     D = keys - keys.mean(0)
@@ -329,7 +344,8 @@ def check_fit(keys, vt_stored, ev_o, vt_o, r, energy_slack=FIT_ENERGY_SLACK, sub
         f"residual {resid:.6g} > optimum {opt:.6g} + {energy_slack} x {total:.6g}"
     checked = 0
     for m in range(1, r + 1):
-        if ev[m - 1] <= 0 or (ev[m - 1] - ev[m]) / ev[m - 1] <= FIT_GAP:
+        gap = ev[m - 1] - ev[m]
+        if ev[m - 1] <= 0 or gap <= FIT_GAP * ev[m - 1] or gap <= FIT_GAP_ABS * ev[0]:
             continue
         Vm = np.asarray(vt_o[:m], dtype=np.float64).T
         off = float(np.linalg.norm(Vm - Q @ (Q.T @ Vm)))
