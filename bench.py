@@ -336,149 +336,116 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-FULL_STEP = dict(layers=32, batch=16, kv_heads=8, group=4, head_dim=128, page_size=64, rank=4,
-                 budget_pages=32, base_len=65536, stagger=4)
-
-
 def full_step(args):
-    """The decode step of a whole model: `layers` attention layers of a batch of
-    16 sequences of ~64K tokens (sequence s is 4 s tokens longer, so one
-    sequence completes a page every 4 steps), r = 4, k = 32. All layers' K/V
-    live in one paged pool (~138 GB) and their summaries in one summary pool,
-    layer l owning blocks [l nb, (l + 1) nb) in a random order, so the pages
-    that complete in a step are built for all layers in one launch. A step =
-    locks_decode_step for every layer, the build of the pages completing at
-    that step, and the length increment, on one stream. Timed eagerly and with
-    the per-layer steps replayed from one captured HIP graph."""
-    import numpy as np
+    """The decode step of a whole model (sparse_kv_page_amd.synth.FULL_STEP:
+    32 attention layers of a batch of 16 sequences of ~64K tokens, sequence s
+    4 s tokens longer, so one sequence completes a page every 4 steps; r = 4,
+    k = 32). Keys and values of every layer come from the low-rank generator;
+    all layers' K/V live in one paged pool (~138 GB) and their summaries in one
+    summary pool. A step = locks_decode_step for every layer, the build of the
+    page the step's token completes in every layer (block ids gathered from a
+    step table by a step counter kept on the device, so the step's launches
+    are the same every step), and the length increment, on one stream. Timed
+    eagerly, then replayed from one captured HIP graph that holds the whole
+    step, builds included."""
     import torch
 
     from sparse_kv_page_amd import locks as L
+    from sparse_kv_page_amd import synth
 
-    c = FULL_STEP
-    nl, B, Hkv, G, d, P, r, k = (c["layers"], c["batch"], c["kv_heads"], c["group"], c["head_dim"],
-                                 c["page_size"], c["rank"], c["budget_pages"])
+    sh = synth.FULL_STEP
+    nl, B, Hkv, G, d, P, r, k = (sh["layers"], sh["batch"], sh["kv_heads"], sh["group"], sh["head_dim"],
+                                 sh["page_size"], sh["rank"], sh["budget_pages"])
     Hq = Hkv * G
     steps, warm = args.steps, args.warmup
-    total = warm + 2 * steps  # eager warm-up and timed steps, then the same with the graph
+    total = 2 * warm + 2 * steps + 2  # eager warm-up and timed steps, capture warm-up, graph warm-up and timed
     torch.cuda.set_device(0)
     dev = "cuda"
-    cfg = L.make_config(d, P, r, Hq, Hkv, k, "bf16", "bf16", 1.0 / math.sqrt(d))
-    lens0 = [c["base_len"] + c["stagger"] * s for s in range(B)]
-    max_pages = -(-(max(lens0) + total + P) // P)
-    nb = B * max_pages
-    NB = nl * nb
-    g = torch.Generator(device=dev)
-    g.manual_seed(args.seed)
     t0 = time.perf_counter()
-    # K/V pools: random 1-layer slabs copied over every layer's blocks
-    pools = []
-    for name in ("K", "V"):
-        pool = torch.empty((NB, Hkv, P, d), dtype=torch.bfloat16, device=dev)
-        slab = torch.randn((nb, Hkv, P, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        for layer in range(nl):
-            pool[layer * nb:(layer + 1) * nb].copy_(slab if name == "K" else slab.flip(0))
-        del slab
-        torch.cuda.synchronize()
-        pools.append(pool)
-        print(f"[full] {name} pool {pool.numel() * 2 / 2**30:.1f} GiB filled ({time.perf_counter() - t0:.0f} s)",
-              file=sys.stderr, flush=True)
-    kp, vp = pools
-    # block tables: layer l's pages are a random permutation of its blocks
-    bt = torch.empty((nl, B, max_pages), dtype=torch.int32, device=dev)
-    for layer in range(nl):
-        perm = torch.randperm(nb, generator=g, device=dev).to(torch.int32) + layer * nb
-        bt[layer] = perm.view(B, max_pages)
-    q = torch.randn((nl, B, Hq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    seq = torch.tensor(lens0, dtype=torch.int32, device=dev)
+    inp = synth.full_step_inputs(total, seed=args.seed, device=dev,
+                                 log=lambda m: print(f"[full] {m} ({time.perf_counter() - t0:.0f} s)",
+                                                     file=sys.stderr, flush=True))
+    NB, maxp, lens0 = inp["num_blocks"], inp["max_pages"], inp["lens0"]
+    cfg = L.make_config(d, P, r, Hq, Hkv, k, "bf16", "bf16", 1.0 / math.sqrt(d))
+    kp, vp, bt, q = inp["k_pool"], inp["v_pool"], inp["block_table"], inp["q"]
     spool = L.summary_pool_for(cfg, NB, dev)
-    # prefill: every complete page of every layer
     full_ids = torch.cat([bt[layer, s, :lens0[s] // P] for layer in range(nl) for s in range(B)]).contiguous()
     L.locks_build_summaries(cfg, kp, NB, full_ids, full_ids.numel(), spool)
     torch.cuda.synchronize()
     print(f"[full] prefill build of {full_ids.numel() * Hkv} tiles done ({time.perf_counter() - t0:.0f} s)",
           file=sys.stderr, flush=True)
-    # pages completing at each step (every layer), precomputed
-    bt_c = bt.cpu()
-    build_ids = []
-    for t in range(total):
-        ids = []
-        for s in range(B):
-            T = lens0[s] + t + 1  # length after this step's token
-            if T % P == 0:
-                ids += [int(bt_c[layer, s, T // P - 1]) for layer in range(nl)]
-        build_ids.append(torch.tensor(ids, dtype=torch.int32, device=dev) if ids else None)
-    ws_bytes = L.locks_workspace_size(cfg, B, max_pages)
+    ws_bytes = L.locks_workspace_size(cfg, B, maxp)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     sel = torch.empty((nl, B, Hkv, k), dtype=torch.int32, device=dev)
     out = torch.empty((nl, B, Hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((nl, B, Hq), dtype=torch.float32, device=dev)
+    seq = torch.tensor(lens0, dtype=torch.int32, device=dev)
+    step_idx = torch.zeros(1, dtype=torch.int64, device=dev)
+    ids_buf = torch.full((1, nl), -1, dtype=torch.int32, device=dev)
+    done = [0]  # steps taken (host count, so the step table is never read past its end)
 
-    def layers_step():
+    def step():
         for layer in range(nl):
-            L.locks_decode_step(cfg, q[layer], spool, kp, vp, NB, bt[layer], seq, B, max_pages, sel[layer],
-                                out[layer], lse[layer], ws, ws_bytes)
-
-    def finish(t):
-        # the token of this step completes pages: summarise them, then grow the lengths
-        ids = build_ids[t]
-        if ids is not None:
-            L.locks_build_summaries(cfg, kp, NB, ids, ids.numel(), spool)
+            L.locks_decode_step(cfg, q[layer], spool, kp, vp, NB, bt[layer], seq, B, maxp, sel[layer], out[layer],
+                                lse[layer], ws, ws_bytes)
+        torch.index_select(inp["build_ids"], 0, step_idx, out=ids_buf)
+        L.locks_build_summaries(cfg, kp, NB, ids_buf, ids_buf.numel(), spool)
         seq.add_(1)
+        step_idx.add_(1)
 
-    def run(t_first, n, graph=None):
+    def run(n, graph=None):
+        assert done[0] + n <= total, "step table exhausted"
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
-        for t in range(t_first, t_first + n):
-            if graph is None:
-                layers_step()
-            else:
-                graph.replay()
-            finish(t)
+        for _ in range(n):
+            step() if graph is None else graph.replay()
         e1.record()
         torch.cuda.synchronize()
+        done[0] += n
         return e0.elapsed_time(e1) * 1e3 / n
 
-    half = warm // 2
-    run(0, half)                                   # warm-up (eager)
-    eager_us = run(half, steps)
-    # graph of the per-layer steps (lengths are read from device memory)
+    run(warm)                                      # warm-up (eager)
+    eager_us = run(steps)
+    # graph of the whole step, builds included
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        layers_step()
+        step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    done[0] += 1
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        layers_step()
-    run(half + steps, warm - half, graph)          # warm-up (graph)
-    graph_us = run(warm + steps, steps, graph)
-    # the build share: the same builds alone
-    builds = [b for b in build_ids[half:half + steps] if b is not None]
+        step()
+    run(warm, graph)                               # warm-up (graph)
+    graph_us = run(steps, graph)
+    # the build share: the same steps' builds alone
+    ids_c = inp["build_ids"].cpu()
+    n_build = sum(1 for t in range(warm, warm + steps) if int(ids_c[t, 0]) >= 0)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for ids in builds:
-        L.locks_build_summaries(cfg, kp, NB, ids, ids.numel(), spool)
+    for t in range(warm, warm + steps):
+        L.locks_build_summaries(cfg, kp, NB, inp["build_ids"][t], nl, spool)
     e1.record()
     torch.cuda.synchronize()
     build_us = e0.elapsed_time(e1) * 1e3 / steps
-    wl = __import__("sparse_kv_page_amd.synth", fromlist=["Workload"]).Workload(
-        "full_step", B, Hkv, G, d, P, tuple(lens0), r, k, "bf16", "bf16")
+    wl = synth.Workload("full_step", B, Hkv, G, d, P, tuple(lens0), r, k, "bf16", "bf16")
     sb, kb = algorithmic_bytes(wl, L.locks_summary_record_bytes(cfg))
     step_bytes = nl * (sb + kb)
     res = {"metric": "full decode step µs (32 layers, builds of completing pages interleaved)",
            "value": round(eager_us, 1), "unit": "us", "n_gpus": 1, "steps": steps, "warmup": warm,
-           "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+           "higher_is_better": False, "dtype": "bf16", "data": "synthetic (low-rank key generator)",
            "config": {"workload": "full_step", "layers": nl, "batch": B, "context_tokens": lens0[0],
                       "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "page_size": P, "rank": r,
                       "budget_tokens": k * P, "kv_bytes_resident": 2 * kp.numel() * 2},
            "step_algorithmic_bytes": step_bytes,
            "hbm_roofline_frac_step": round(step_bytes / (eager_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
            "graph_us_per_step": round(graph_us, 1),
-           "build_us_per_step": round(build_us, 1), "build_share": round(build_us / eager_us, 4)}
+           "graph_holds": "every layer's decode step, the step's builds and the length increment",
+           "build_us_per_step": round(build_us, 1), "build_share": round(build_us / eager_us, 4),
+           "steps_with_a_completing_page": n_build}
     print(json.dumps(res), flush=True)
 
 

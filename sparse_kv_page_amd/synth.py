@@ -231,3 +231,62 @@ def random_i4_codes(wl: Workload, seed: int = 0, device="cpu"):
     return dict(mu_code=codes((n, H, d), 127), vt_code=codes((n, H, r, d), 7),
                 coef_code=codes((n, H, P, r), 127), mu_scale=scales((n, H), 0.004, 0.016),
                 vt_scale=scales((n, H, r), 0.02, 0.07), coef_scale=scales((n, H, P), 0.004, 0.05))
+
+
+# The whole-model decode step: `layers` attention layers of a batch whose
+# sequence s holds base_len + stagger * s tokens, each step appending one token
+# to every sequence (so with stagger 4 and 16 sequences at most one sequence
+# completes a page per step).
+FULL_STEP = dict(layers=32, batch=16, kv_heads=8, group=4, head_dim=128, page_size=64, rank=4,
+                 budget_pages=32, base_len=65536, stagger=4)
+
+
+def full_step_inputs(steps: int, seed: int = 0, device="cuda", slabs: int = 2, log=None, **over):
+    """Inputs of `steps` whole-model decode steps (FULL_STEP shape unless
+    overridden). Keys and values of each layer come from generate() with the
+    128K batch-8 generator (six signal directions plus noise, AR(1) centroids,
+    needle tokens): `slabs` independently drawn slabs of the whole batch, layer
+    l holding slab l % slabs under its own random block permutation inside
+    the layer's block range [l nb, (l + 1) nb), so every layer's pages sit at
+    different physical blocks. Queries are drawn per layer.
+
+    Returns dict: k_pool, v_pool [layers * nb][H_kv][P][d] bf16; block_table
+    [layers][B][max_pages] int32; q [layers][B][H_q][d] bf16; lens0 (list of
+    initial lengths); build_ids [steps][layers] int32 (device): the block of
+    every layer of the page that the token of step t completes, -1 when no
+    page completes; num_blocks, max_pages."""
+    c = dict(FULL_STEP, **over)
+    nl, B, Hkv, G, d, P = c["layers"], c["batch"], c["kv_heads"], c["group"], c["head_dim"], c["page_size"]
+    lens0 = [c["base_len"] + c["stagger"] * s for s in range(B)]
+    lens_end = tuple(x + steps for x in lens0)
+    wl = Workload("full_step_slab", B, Hkv, G, d, P, lens_end, c["rank"], c["budget_pages"], "bf16", "bf16",
+                  centroid_std=0.5, ar_rho=0.99, n_needles=8)
+    maxp, nb = wl.max_pages, wl.num_blocks
+    NB = nl * nb
+    dev = torch.device(device)
+    k_pool = torch.empty((NB, Hkv, P, d), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.empty((NB, Hkv, P, d), dtype=torch.bfloat16, device=dev)
+    bt = torch.empty((nl, B, maxp), dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed) + 31)
+    for si in range(slabs):
+        slab = generate(wl, int(seed) * 1000 + si, dev)
+        for layer in range(si, nl, slabs):
+            # physical block of slab block x in this layer
+            perm = torch.randperm(nb, generator=g, device=dev)
+            k_pool[layer * nb + perm] = slab["k_pool"]
+            v_pool[layer * nb + perm] = slab["v_pool"]
+            bt[layer] = (layer * nb + perm[slab["block_table"].long()]).to(torch.int32)
+        del slab
+        if log:
+            log(f"slab {si + 1}/{slabs} placed")
+    q = torch.randn((nl, B, Hkv * G, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    bt_c = bt.cpu()
+    ids = torch.full((max(1, steps), nl), -1, dtype=torch.int32)
+    for t in range(steps):
+        for s in range(B):
+            T = lens0[s] + t + 1  # length once the token of step t is in
+            if T % P == 0:
+                ids[t] = bt_c[:, s, T // P - 1]
+    return dict(k_pool=k_pool, v_pool=v_pool, block_table=bt, q=q, lens0=lens0, build_ids=ids.to(dev),
+                num_blocks=NB, max_pages=maxp, shape=c)

@@ -910,110 +910,142 @@ def test_decode_with_host_resident_kv():
 # --------------------------------------------------------------------------
 # the whole-model step at its full size: 32 layers x 16 sequences of ~64K
 # tokens (all layers' K/V in one ~138 GB pool, block offsets past 4 GiB),
-# r = 4, k = 32, with the builds of completing pages interleaved; sampled
-# (layer, sequence, KV head) units against the oracle
+# r = 4, k = 32, keys from the low-rank generator. One step (every layer's
+# decode step, the build of the pages the step's token completes, the length
+# increment) is captured into one HIP graph and replayed step after step;
+# after every replay sampled (layer, sequence, KV head) units are checked
+# against the oracle, and the pages built inside the graph against the
+# oracle's fit.
 # --------------------------------------------------------------------------
-def _full_step_check():
-    nl, B, Hkv, G, d, P, r, k = 32, 16, 8, 4, 128, 64, 4, 32
-    Hq = Hkv * G
-    lens0 = [65536 + 4 * s for s in range(B)]
-    steps = 5
-    max_pages = -(-(max(lens0) + steps + P) // P)
-    nb = B * max_pages
-    NB = nl * nb
-    cfg = L.make_config(d, P, r, Hq, Hkv, k, "bf16", "bf16", 1.0 / np.sqrt(d))
-    dev = gg.DEV
-    g = torch.Generator(device=dev)
-    g.manual_seed(5)
-    kp = torch.empty((NB, Hkv, P, d), dtype=torch.bfloat16, device=dev)
-    vp = torch.empty((NB, Hkv, P, d), dtype=torch.bfloat16, device=dev)
-    for pool, flip in ((kp, False), (vp, True)):
-        slab = torch.randn((nb, Hkv, P, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+FULL_STEPS = 6
+
+
+def full_step_graph(cfg, inp, spool, seq, sel, out, lse, ws, ws_bytes, step_idx, ids_buf):
+    """The step function that is captured: every layer's locks_decode_step,
+    the build of the page this step's token completes (block ids gathered from
+    the step table by a step counter kept on the device, -1 = none), then the
+    lengths and the counter advance."""
+    nl = inp["q"].shape[0]
+    B = inp["q"].shape[1]
+    NB, maxp = inp["num_blocks"], inp["max_pages"]
+
+    def step():
         for layer in range(nl):
-            pool[layer * nb:(layer + 1) * nb].copy_(slab.flip(0) if flip else slab)
-        del slab
-    bt = torch.empty((nl, B, max_pages), dtype=torch.int32, device=dev)
-    for layer in range(nl):
-        bt[layer] = (torch.randperm(nb, generator=g, device=dev).to(torch.int32) + layer * nb).view(B, max_pages)
-    q = torch.randn((nl, B, Hq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    seq = torch.tensor(lens0, dtype=torch.int32, device=dev)
+            L.locks_decode_step(cfg, inp["q"][layer], spool, inp["k_pool"], inp["v_pool"], NB,
+                                inp["block_table"][layer], seq, B, maxp, sel[layer], out[layer], lse[layer], ws,
+                                ws_bytes)
+        torch.index_select(inp["build_ids"], 0, step_idx, out=ids_buf)
+        L.locks_build_summaries(cfg, inp["k_pool"], NB, ids_buf, ids_buf.numel(), spool)
+        seq.add_(1)
+        step_idx.add_(1)
+    return step
+
+
+def _full_step_check():
+    sh = synth.FULL_STEP
+    nl, B, Hkv, G, d, P, r, k = (sh["layers"], sh["batch"], sh["kv_heads"], sh["group"], sh["head_dim"],
+                                 sh["page_size"], sh["rank"], sh["budget_pages"])
+    Hq = Hkv * G
+    dev = gg.DEV
+    inp = synth.full_step_inputs(FULL_STEPS + 1, seed=5, device=dev,
+                                 log=lambda m: print(f"[full step] {m}", flush=True))
+    NB, maxp, lens0 = inp["num_blocks"], inp["max_pages"], inp["lens0"]
+    cfg = L.make_config(d, P, r, Hq, Hkv, k, "bf16", "bf16", 1.0 / np.sqrt(d))
+    kp, vp, bt = inp["k_pool"], inp["v_pool"], inp["block_table"]
     spool = L.summary_pool_for(cfg, NB, dev)
     full_ids = torch.cat([bt[layer, s, :lens0[s] // P] for layer in range(nl) for s in range(B)]).contiguous()
     L.locks_build_summaries(cfg, kp, NB, full_ids, full_ids.numel(), spool)
     torch.cuda.synchronize()
     print(f"[full step] {NB} blocks filled, {full_ids.numel() * Hkv} tiles built", flush=True)
-    ws_bytes = L.locks_workspace_size(cfg, B, max_pages)
+    ws_bytes = L.locks_workspace_size(cfg, B, maxp)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
-    sel = torch.empty((nl, B, Hkv, k), dtype=torch.int32, device=dev)
+    sel = torch.full((nl, B, Hkv, k), -7, dtype=torch.int32, device=dev)
     out = torch.empty((nl, B, Hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((nl, B, Hq), dtype=torch.float32, device=dev)
-    bt_c = bt.cpu()
-    built = []
-    for t in range(steps):
-        for layer in range(nl):
-            L.locks_decode_step(cfg, q[layer], spool, kp, vp, NB, bt[layer], seq, B, max_pages, sel[layer],
-                                out[layer], lse[layer], ws, ws_bytes)
-        if t == steps - 1:
-            break
-        ids = []
-        for s in range(B):
-            T = lens0[s] + t + 1
-            if T % P == 0:
-                ids += [int(bt_c[layer, s, T // P - 1]) for layer in range(nl)]
-                built.append((s, T // P - 1))
-        if ids:
-            idt = torch.tensor(ids, dtype=torch.int32, device=dev)
-            L.locks_build_summaries(cfg, kp, NB, idt, idt.numel(), spool)
-        seq.add_(1)
+    seq = torch.tensor(lens0, dtype=torch.int32, device=dev)
+    step_idx = torch.zeros(1, dtype=torch.int64, device=dev)
+    ids_buf = torch.full((1, nl), -1, dtype=torch.int32, device=dev)
+    step = full_step_graph(cfg, inp, spool, seq, sel, out, lse, ws, ws_bytes, step_idx, ids_buf)
+    # warm-up on the capture stream, then back to the initial lengths and step
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    print(f"[full step] {steps} steps done, pages built during them: {built}", flush=True)
+    seq.copy_(torch.tensor(lens0, dtype=torch.int32))
+    step_idx.zero_()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    assert int(step_idx.item()) == 0 and seq.cpu().tolist() == lens0  # capture records, runs nothing
+    bt_c = bt.cpu()
+    q_c = inp["q"].cpu()
+    ids_c = inp["build_ids"].cpu()
+    rng = np.random.default_rng(5)
+    built = []  # (sequence, logical page) built inside the graph
+    checked = 0
+    for t in range(FULL_STEPS):
+        assert t < ids_c.shape[0]  # the step table covers every replay
+        graph.replay()
+        torch.cuda.synchronize()
+        lens_t = [x + t for x in lens0]  # lengths this step's decode saw
+        sel_c = sel.cpu()
+        out_c = gg.f64(out.cpu())
+        # units: the sequence whose page the previous replay built (its summary
+        # is now a candidate), and random others
+        units = [(int(rng.integers(nl)), int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(3)]
+        if built:
+            units.append((int(rng.integers(nl)), built[-1][0], int(rng.integers(Hkv))))
+        for layer, s, h in units:
+            T = lens_t[s]
+            J, Jc = -(-T // P), T // P
+            idx = bt_c[layer, s, :Jc].long().to(dev)
+            mu, vt, cf = (gg.f64(x) for x in L.split_records(cfg, spool[idx, h].cpu()))
+            qu = gg.f64(q_c[layer, s, h * G:(h + 1) * G])
+            s_o = oracle.page_scores(qu, mu, vt, cf, cfg.softmax_scale)
+            if J <= k:
+                sel_o, sigma_o = oracle.select(np.zeros(0), Jc, J, k), None
+            else:
+                _, sigma_o = oracle.combine(s_o)
+                sel_o = oracle.select(sigma_o, Jc, J, k)
+            wl_u = synth.Workload("full_unit", 1, Hkv, G, d, P, (T,), r, k, "bf16", "bf16")
+            gg.check_selection(wl_u, 0, sel_c[layer, s, h].tolist(), sel_o.tolist(), sigma_o)
+            ks, vs = [], []
+            for j in sel_c[layer, s, h].tolist():
+                if j < 0:
+                    continue
+                blk = int(bt_c[layer, s, j])
+                nt = min(P, T - j * P)
+                ks.append(gg.f64(kp[blk, h, :nt].cpu()))
+                vs.append(gg.f64(vp[blk, h, :nt].cpu()))
+            o_ref, _ = oracle.attend(qu, np.concatenate(ks), np.concatenate(vs), cfg.softmax_scale)
+            err = float(np.max(np.abs(out_c[layer, s, h * G:(h + 1) * G] - o_ref)))
+            assert err <= 2e-2, f"step {t} unit {(layer, s, h)}: output error {err}"
+            checked += 1
+        # the page this replay's token completed, built inside the graph
+        if int(ids_c[t, 0]) >= 0:
+            s_done = [s for s in range(B) if (lens0[s] + t + 1) % P == 0][0]
+            built.append((s_done, (lens0[s_done] + t + 1) // P - 1))
+        print(f"[full step] replay {t}: {len(units)} units match the oracle; pages built so far {built}",
+              flush=True)
+    assert int(step_idx.item()) == FULL_STEPS and seq.cpu().tolist() == [x + FULL_STEPS for x in lens0]
     assert built, "a page completes during the steps"
-    lens_now = [x + steps - 1 for x in lens0]
-    q_c = q.cpu()
-    sel_c = sel.cpu()
-    out_c = gg.f64(out.cpu())
-    units = [(0, 0, 0), (31, 15, 7), (17, built[0][0], 3)]
-    for layer, s, h in units:
-        T = lens_now[s]
-        J, Jc = -(-T // P), T // P
-        idx = bt_c[layer, s, :Jc].long().to(dev)
-        mu, vt, cf = (gg.f64(x) for x in L.split_records(cfg, spool[idx, h].cpu()))
-        qu = gg.f64(q_c[layer, s, h * G:(h + 1) * G])
-        s_o = oracle.page_scores(qu, mu, vt, cf, cfg.softmax_scale)
-        if J <= k:
-            sel_o, sigma_o = oracle.select(np.zeros(0), Jc, J, k), None
-        else:
-            _, sigma_o = oracle.combine(s_o)
-            sel_o = oracle.select(sigma_o, Jc, J, k)
-        wl_u = synth.Workload("full_unit", 1, Hkv, G, d, P, (T,), r, k, "bf16", "bf16")
-        gg.check_selection(wl_u, 0, sel_c[layer, s, h].tolist(), sel_o.tolist(), sigma_o)
-        # attention over the GPU's own selection, original K/V
-        ks, vs = [], []
-        for j in sel_c[layer, s, h].tolist():
-            if j < 0:
-                continue
+    # the pages built inside the graph: rank-4 fits checked against the oracle's
+    for s, j in built:
+        for layer in (0, nl - 1):
             blk = int(bt_c[layer, s, j])
-            nt = min(P, T - j * P)
-            ks.append(gg.f64(kp[blk, h, :nt].cpu()))
-            vs.append(gg.f64(vp[blk, h, :nt].cpu()))
-        o_ref, _ = oracle.attend(qu, np.concatenate(ks), np.concatenate(vs), cfg.softmax_scale)
-        assert np.max(np.abs(out_c[layer, s, h * G:(h + 1) * G] - o_ref)) <= 2e-2
-    # the pages built during the steps: a rank-4 fit within the Eckart-Young residual
-    s, j = built[0]
-    for layer in (0, nl - 1):
-        blk = int(bt_c[layer, s, j])
-        keys = np.stack([gg.f64(kp[blk, h].cpu()) for h in range(Hkv)])
-        _, _, _, ev, _ = oracle.build_pages(keys, r)
-        _, vt_g, _ = L.split_records(cfg, spool[blk].cpu())
-        for h in range(Hkv):
-            D = keys[h] - keys[h].mean(0)
-            vt = gg.f64(vt_g[h])
-            tau = float(np.sum(np.clip(ev[h, r:], 0, None)))
-            resid = float(np.linalg.norm(D - D @ vt.T @ vt) ** 2)
-            assert resid <= tau + 2e-2 * float(np.sum(np.clip(ev[h], 0, None)))
+            keys = np.stack([gg.f64(kp[blk, h].cpu()) for h in range(Hkv)])
+            _, vt_o, _, ev, _ = oracle.build_pages(keys, r)
+            _, vt_g, _ = L.split_records(cfg, spool[blk].cpu())
+            for h in range(Hkv):
+                gg.check_fit(keys[h], gg.f64(vt_g[h]), ev[h], vt_o[h], r)
+    assert checked >= 3 * FULL_STEPS
 
 
-def test_full_step_sampled():
+def test_full_step_graph_against_oracle():
     try:
         _full_step_check()  # its ~150 GB of device buffers are released on return
     finally:
