@@ -58,6 +58,11 @@ def parse():
     ap.add_argument("--full-step", action="store_true",
                     help="instead of the 128K batch-8 layer step: the 32-layer decode step of a 16 x 64K batch "
                          "with the builds of completing pages interleaved (its own JSON line)")
+    ap.add_argument("--hot-cache", type=float, default=None, metavar="MULT",
+                    help="instead of the layer step: the step with the K/V pools in pinned host memory read "
+                         "through the GPU hot-page cache of MULT steps' tiles (its own JSON line)")
+    ap.add_argument("--query-rho", type=float, default=0.9,
+                    help="--hot-cache: correlation of consecutive steps' queries (AR(1) sequence)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: turn the rocprofv3 outputs of the commands in profiles/*.md into "
                          "profiles/traffic_<workload>.json and the two summaries")
@@ -93,11 +98,11 @@ def main():
     if args.summarize_profiles:
         summarize_profiles(resolve_workload(args), bench_flags(args), *args.summarize_profiles)
         return
-    if args.full_step:
+    if args.full_step or args.hot_cache is not None:
         if args.gpus != 1:
             print("bench.py measures one GPU only", file=sys.stderr)
             sys.exit(2)
-        full_step(args)
+        full_step(args) if args.full_step else hot_cache_step(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -446,6 +451,137 @@ def full_step(args):
            "graph_holds": "every layer's decode step, the step's builds and the length increment",
            "build_us_per_step": round(build_us, 1), "build_share": round(build_us / eager_us, 4),
            "steps_with_a_completing_page": n_build}
+    print(json.dumps(res), flush=True)
+
+
+def hot_cache_step(args):
+    """The decode step with the K/V pools in pinned host memory, read through
+    the GPU hot-page cache (locks_decode_step_cached, a clock cache of
+    (block, KV head) tiles; [Locks] §5.3 Table 3 and App. B.4.2 keep the full
+    K/V in host memory and the pages used often in a smaller GPU cache). The
+    queries of consecutive steps form an AR(1) sequence (--query-rho), the
+    cache holds --hot-cache times one step's tiles. Timed beside the same
+    steps without the cache (every selected tile over the host link) and with
+    device-resident pools; the hit share is counted over the timed steps, and
+    for a few other query correlations over shorter runs."""
+    import torch
+
+    from sparse_kv_page_amd import locks as L
+    from sparse_kv_page_amd import synth
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    wl = resolve_workload(args)
+    cfg = L.config_for(wl)
+    B, Hkv, Hq, d, P, k = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim, wl.page_size, wl.budget_pages
+    data = synth.generate(wl, args.seed, dev)
+    q, kp, vp, bt, sl = (data[x] for x in ("q", "k_pool", "v_pool", "block_table", "seq_lens"))
+    maxp, NB = wl.max_pages, wl.num_blocks
+    pool = L.summary_pool_for(cfg, NB, dev)
+    ids = torch.cat([bt[b, :int(wl.seq_lens[b]) // P] for b in range(B)]).contiguous()
+    L.locks_build_summaries(cfg, kp, NB, ids, ids.numel(), pool)
+    kh, kdev = host_pool(kp)
+    vh, vdev = host_pool(vp)
+    n = B * Hkv * k
+    capacity = int(round(args.hot_cache * n))
+    cache = L.HotCache(cfg, NB, capacity, dev)
+    tile_bytes = P * d * (2 if wl.kv_dtype == "bf16" else 4)
+    print(f"[hot-cache] {wl.name}: K/V in host memory ({2 * kh.numel() * kh.element_size() / 2**30:.1f} GiB), "
+          f"cache of {capacity} tiles ({2 * capacity * tile_bytes / 2**30:.2f} GiB)", file=sys.stderr, flush=True)
+    sel = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, d), dtype=synth.torch_dtype(wl.kv_dtype), device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws_bytes = L.locks_workspace_size(cfg, B, maxp)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    warm, steps = args.warmup, args.steps
+    qs = synth.query_sequence(q, warm + steps, args.query_rho, args.seed)
+
+    def cached(t, qseq=qs):
+        L.locks_decode_step_cached(cfg, qseq[t], pool, kdev, vdev, NB, bt, sl, B, maxp, sel, out, lse, cache.buf,
+                                   capacity, ws, ws_bytes)
+
+    def uncached(t):
+        L.locks_decode_step(cfg, qs[t], pool, kdev, vdev, NB, bt, sl, B, maxp, sel, out, lse, ws, ws_bytes)
+
+    def device(t):
+        L.locks_decode_step(cfg, qs[t], pool, kp, vp, NB, bt, sl, B, maxp, sel, out, lse, ws, ws_bytes)
+
+    def timed(fn):
+        for t in range(warm):
+            fn(t)
+        torch.cuda.synchronize()
+        per = []
+        for w in range(3):  # three windows over consecutive steps
+            lo, hi = warm + w * steps // 3, warm + (w + 1) * steps // 3
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for t in range(lo, hi):
+                fn(t)
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / (hi - lo))
+        return per
+
+    cache.reset()
+    for t in range(warm):
+        cached(t)
+    torch.cuda.synchronize()
+    s0 = cache.stats()
+    cache_win = []
+    for w in range(3):
+        lo, hi = warm + w * steps // 3, warm + (w + 1) * steps // 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(lo, hi):
+            cached(t)
+        e1.record()
+        torch.cuda.synchronize()
+        cache_win.append(e0.elapsed_time(e1) * 1e3 / (hi - lo))
+    s1 = cache.stats()
+    st = {key: s1[key] - s0[key] for key in s1}
+    served = st["hits"] + st["misses"] + st["refreshes"] + st["shared"]
+    hit_share = st["hits"] / served if served else None
+    copied = (st["misses"] + st["refreshes"]) / max(1, st["steps"])
+    host_win = timed(uncached)
+    dev_win = timed(device)
+    print(f"[hot-cache] cached {statistics.median(cache_win):.1f} us, uncached host "
+          f"{statistics.median(host_win):.1f} us, device {statistics.median(dev_win):.1f} us, hit share "
+          f"{hit_share:.3f}", file=sys.stderr, flush=True)
+
+    # hit share for other query correlations (shorter runs, untimed)
+    by_rho = {}
+    for rho in (0.0, 0.5, 0.9, 0.97):
+        qr = synth.query_sequence(q, 96, rho, args.seed + 5)
+        cache.reset()
+        for t in range(32):
+            cached(t, qr)
+        torch.cuda.synchronize()
+        a = cache.stats()
+        for t in range(32, 96):
+            cached(t, qr)
+        torch.cuda.synchronize()
+        b_ = cache.stats()
+        srv = sum(b_[x] - a[x] for x in ("hits", "misses", "refreshes", "shared"))
+        by_rho[str(rho)] = round((b_["hits"] - a["hits"]) / srv, 4)
+    del kh, vh
+    med = statistics.median(cache_win)
+    res = {"metric": "decode step us, K/V in host memory through the GPU hot-page cache",
+           "value": round(statistics.mean(cache_win), 3), "unit": "us", "n_gpus": 1, "steps": steps,
+           "warmup": warm, "higher_is_better": False, "dtype": wl.kv_dtype,
+           "data": "synthetic (AR(1) queries across steps)",
+           "config": {"workload": wl.name + "_hotcache", "batch": B, "context_tokens": int(wl.seq_lens[0]),
+                      "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "page_size": P, "rank": wl.rank,
+                      "budget_tokens": k * P, "capacity_tiles": capacity,
+                      "capacity_steps": args.hot_cache, "cache_GiB": round(2 * capacity * tile_bytes / 2**30, 3),
+                      "query_rho": args.query_rho},
+           "windows_us": [round(x, 3) for x in cache_win], "median_us": round(med, 3),
+           "hit_share": round(hit_share, 4) if hit_share is not None else None,
+           "counts_over_timed_steps": st,
+           "tiles_copied_per_step": round(copied, 2),
+           "host_link_bytes_per_step": int(copied * 2 * tile_bytes),
+           "uncached_host_step_us": round(statistics.median(host_win), 3),
+           "device_resident_step_us": round(statistics.median(dev_win), 3),
+           "hit_share_by_query_rho": by_rho}
     print(json.dumps(res), flush=True)
 
 

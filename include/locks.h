@@ -220,6 +220,83 @@ int locks_decode_step(const locks_config_t* cfg, const void* q, const void* summ
                       int32_t max_pages, int32_t* selected, void* out, float* lse, void* ws,
                       size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * (f4) Hot-page cache for K/V held in host memory, [Locks] §5.3 Table 3 and
+ * App. B.4.2: the full K/V stays in host memory and the pages used often are
+ * kept in a smaller cache in GPU memory. The pages specify no cache policy;
+ * this library's is second-chance (clock) replacement over (block, KV head)
+ * tiles of P x d keys and values, the unit one selection reads:
+ *   - a selected tile resident in the cache is a hit: its slot is marked used
+ *     this step and referenced. A tile that was copied while its page was
+ *     incomplete (page J-1 with T % P != 0) is copied again on its next use
+ *     (a refresh), since tokens may have been appended since.
+ *   - each selected tile that is not resident (the first page slot naming it,
+ *     in (sequence, KV head, slot) order, when several page slots name one
+ *     tile) takes the next evictable slot of a clock hand that walks the
+ *     slots cyclically: slots used this step (taken ones included) are
+ *     skipped, a referenced slot
+ *     loses its reference mark and is passed, an unreferenced one is taken
+ *     (its old tile leaves the cache); the hand stops just past the last
+ *     slot taken.
+ *   - taken and refreshed tiles are copied from the K/V pools into their
+ *     slots, then the decode reads every selected tile from the cache.
+ * Cache buffer (device memory the caller allocates and owns; its layout from
+ * locks_hot_cache_layout; fields in this order, each 256-byte aligned):
+ *   STATS    int64[8]: hits, misses, refreshes, shared (page slots served by
+ *            a tile another page slot of the step named), failed (page slots
+ *            left unserved: a cache initialised for another capacity or pool),
+ *            steps; accumulated by every call
+ *   META     int64[2]: capacity and num_blocks * H_kv it was initialised for
+ *   CLOCK    int32[2]: hand, step number
+ *   SLOT_OF  int32[num_blocks * H_kv]: slot holding tile blk * H_kv + h, or -1
+ *   TILE_OF, STAMP, FLAGS  int32[capacity]: tile held (or -1), last step
+ *            that used the slot, flags (1 referenced, 2 copied incomplete)
+ *   K, V     [capacity][P][d] kv_dtype: the cached tiles
+ */
+enum {
+  LOCKS_HOT_CACHE_STATS = 0,
+  LOCKS_HOT_CACHE_META,
+  LOCKS_HOT_CACHE_CLOCK,
+  LOCKS_HOT_CACHE_SLOT_OF,
+  LOCKS_HOT_CACHE_TILE_OF,
+  LOCKS_HOT_CACHE_STAMP,
+  LOCKS_HOT_CACHE_FLAGS,
+  LOCKS_HOT_CACHE_K,
+  LOCKS_HOT_CACHE_V,
+  LOCKS_HOT_CACHE_FIELDS
+};
+
+/* Byte offsets of the LOCKS_HOT_CACHE_FIELDS fields (offsets may be NULL)
+ * and the total size (*bytes) of the cache buffer of a pool of num_blocks
+ * blocks with `capacity` tile slots (both >= 1; num_blocks * H_kv < 2^31 - 1).
+ * Host only. */
+int locks_hot_cache_layout(const locks_config_t* cfg, int64_t num_blocks, int32_t capacity,
+                           int64_t* offsets, size_t* bytes);
+
+/* Empty the cache buffer (no tile resident, counters zero, hand at slot 0)
+ * and record capacity and num_blocks in it. Required before the first
+ * locks_decode_step_cached call on the buffer, and whenever the pool's blocks
+ * get new contents other than tokens appended to incomplete pages. */
+int locks_hot_cache_init(const locks_config_t* cfg, void* cache, int64_t num_blocks, int32_t capacity,
+                         hipStream_t stream);
+
+/* locks_decode_step with the K/V pools read through the hot-page cache:
+ * locks_score_select, then the cache admission (above) of the selected tiles
+ * and the copies of the missing and refreshed ones from k_pool / v_pool, then
+ * the sparse decode over the cached tiles. Results (selected, out, lse) equal
+ * locks_decode_step's on the same inputs bit for bit. k_pool / v_pool are
+ * normally host memory the device can read (pinned, hipHostMalloc); they are
+ * only read for the copied tiles. capacity >= batch * H_kv * budget_pages
+ * (else LOCKS_E_INVALID_ARG), and every call on one cache buffer passes the
+ * cfg, num_blocks and capacity it was initialised with. ws as for
+ * locks_decode_step; calls that share a cache buffer must not overlap in
+ * time. */
+int locks_decode_step_cached(const locks_config_t* cfg, const void* q, const void* summary_pool,
+                             const void* k_pool, const void* v_pool, int64_t num_blocks,
+                             const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                             int32_t max_pages, int32_t* selected, void* out, float* lse, void* cache,
+                             int32_t capacity, void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

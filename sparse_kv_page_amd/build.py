@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["locks_api.cpp", "page_score.hip", "page_score_i4.hip", "select.hip", "sparse_decode.hip",
-           "build_summaries.hip"]
+           "build_summaries.hip", "hot_cache.hip"]
 HEADERS = ["common.h", "kernels.h", "score_lds.h", "select_unit.h", "decode_split.h",
            os.path.join("..", "..", "include", "locks.h")]
 

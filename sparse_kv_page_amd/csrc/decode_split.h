@@ -140,13 +140,16 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
   int ntok[TPW];
   int64_t tile_off[TPW];
   int jsel[TPW];
+  int slots[TPW];
   const int slot_end = min((split + 1) * a.pages_per_split, a.k);
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int ti = wave_u + kDecWaves * i;
     const int slot = split * a.pages_per_split + ti / tiles_per_page;
+    slots[i] = slot;
     jsel[i] = slot < slot_end ? sel[slot] : -1;
   }
+  const int32_t* tmap = a.tile_map ? a.tile_map + unit * a.k : nullptr;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int ti = wave_u + kDecWaves * i;
@@ -155,11 +158,18 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int split, int
     int nt = 0;
     int64_t off = 0;
     if (j >= 0 && j < J) {
-      const int blk = bt[j];
-      if (blk >= 0 && (int64_t)blk < a.num_blocks) {
+      int64_t tile = -1;
+      if (tmap) {
+        const int m = tmap[slots[i]];
+        if (m >= 0 && (int64_t)m < a.map_tiles) tile = m;
+      } else {
+        const int blk = bt[j];
+        if (blk >= 0 && (int64_t)blk < a.num_blocks) tile = (int64_t)blk * a.Hkv + h;
+      }
+      if (tile >= 0) {
         nt = min(P, Tl - j * P) - sub * kDecTile;
         nt = nt < 0 ? 0 : (nt > kDecTile ? kDecTile : nt);
-        off = (((int64_t)blk * a.Hkv + h) * P + sub * kDecTile) * D;
+        off = (tile * P + sub * kDecTile) * D;
       }
     }
     ntok[i] = nt;

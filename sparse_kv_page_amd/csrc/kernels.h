@@ -41,7 +41,13 @@ struct DecodeArgs {
   int32_t* counters;          // [B][Hkv] arrival counters, zero between calls
   void* out;                  // [B][Hq][D] kv dtype
   float* lse;                 // [B][Hq] or null
+  // [B][Hkv][k] tile per page slot, or null. Null: slot j of (b, h) reads
+  // tile block_table[b][j] * Hkv + h of the pools. Else: it reads tile
+  // tile_map[(b Hkv + h) k + slot] of pools of map_tiles [P][D] tiles (a
+  // negative entry contributes nothing).
+  const int32_t* tile_map;
   int64_t num_blocks;
+  int64_t map_tiles;
   int Hkv, G, P, k, max_pages;
   int pages_per_split, splits;
   float scale;
@@ -57,6 +63,37 @@ struct BuildArgs {
   int32_t* fit_info;          // [n][Hkv] products of the eigensolver (negative: bound not met), or null
   int Hkv, P, r, n;
 };
+
+// Hot-page cache of host-resident K/V tiles in device memory: persistent
+// state in the caller's cache buffer, per-call lists in the workspace.
+struct CacheArgs {
+  const int32_t* selected;    // [B][Hkv][k] logical pages of this step
+  const int32_t* block_table; // [B][max_pages]
+  const int32_t* seq_lens;    // [B]
+  long long* stats;           // [kCacheStats] counters, accumulated
+  long long* meta;            // [2] capacity, tiles: what the state was initialised for
+  int32_t* state;             // [2] clock hand, step
+  int32_t* slot_of;           // [tiles] cache slot holding a (block, head) tile, or -1
+  int32_t* tile_of;           // [C] tile held by a slot, or -1
+  int32_t* stamp;             // [C] last step that used the slot
+  int32_t* flags;             // [C] kCacheRef | kCachePartial
+  int32_t* tile_e;            // [n] workspace: tile of each page slot, or -1
+  int32_t* map;               // [n] workspace: cache slot of each page slot (the decode's tile map)
+  int32_t* fill;              // [n][2] workspace: (slot, tile) copies of this step
+  int32_t* victims;           // [n] workspace
+  int32_t* fill_count;        // [1] workspace
+  const void* k_src;          // K / V pools, [tiles][P][D] (normally in host memory)
+  const void* v_src;
+  void* k_slots;              // [C][P][D] cached tiles
+  void* v_slots;
+  int64_t num_blocks;
+  int64_t tile_bytes;         // P * D * element bytes
+  int Hkv, P, k, max_pages, batch, capacity;
+};
+constexpr int kCacheRef = 1;      // used since the clock hand last passed the slot
+constexpr int kCachePartial = 2;  // copied while its page was incomplete: copied again on its next use
+// counters: hits, misses, refreshes, shared, failed, steps
+constexpr int kCacheStats = 8;
 
 // Quantized ("i4") summary record of one (block, KV head), bytes:
 //   r + 2 nibble rows of d/2 bytes: the basis vectors' 4-bit codes (excess 8),
@@ -83,6 +120,12 @@ int decode_tiles_per_wave(int64_t units, int k, int page_size, bool f32);
 int decode_max_splits(int k, int page_size);
 // dtype: 0 bf16, 1 fp32 keys; i4: write quantized records (bf16 keys only)
 hipError_t launch_build(const BuildArgs& a, int dtype, int D, bool i4, hipStream_t s);
+// cache state for `tiles` tiles and `capacity` slots: empty, counters zero
+hipError_t launch_cache_init(const CacheArgs& a, int64_t tiles, hipStream_t s);
+// look up this step's tiles, evict, list the copies, write the tile map
+hipError_t launch_cache_admit(const CacheArgs& a, hipStream_t s);
+// copy the listed tiles from the pools into their slots
+hipError_t launch_cache_fill(const CacheArgs& a, hipStream_t s);
 // page scores from quantized records (bf16 q)
 hipError_t launch_page_score_i4(const ScoreArgs& a, int D, int batch, hipStream_t s);
 

@@ -209,10 +209,71 @@ int enqueue_sparse_decode(const locks_config_t* cfg, const void* q, const void* 
   return hip_status(locks::launch_sparse_decode(a, cfg->kv_dtype, cfg->head_dim, batch, stream));
 }
 
+// per-call lists of the cached decode step (page-slot tiles, tile map,
+// copies, victims, copy count); they sit just below the decode scratch, which
+// is written after them, and may overlap the score scratch, consumed before
+size_t cache_ws_bytes(const locks_config_t* cfg, int32_t batch) {
+  const size_t n = (size_t)batch * cfg->num_kv_heads * cfg->budget_pages;
+  return n ? 5 * align_up(n * sizeof(int32_t)) + kAlign : 0;
+}
+
 size_t step_ws_bytes(const locks_config_t* cfg, int32_t batch, int32_t max_pages) {
   const size_t a = score_ws_bytes(cfg, batch, max_pages);
-  const size_t b = decode_ws_bytes(cfg, batch);
+  const size_t b = decode_ws_bytes(cfg, batch) + cache_ws_bytes(cfg, batch);
   return a > b ? a : b;
+}
+
+// Hot-page cache buffer: counters, what it was initialised for, clock state,
+// then the maps and the cached K and V tiles, each region 256-byte aligned.
+struct CacheLayout {
+  size_t off[LOCKS_HOT_CACHE_FIELDS];
+  size_t bytes;
+};
+
+CacheLayout cache_layout(const locks_config_t* cfg, int64_t num_blocks, int32_t capacity) {
+  const size_t tiles = (size_t)num_blocks * cfg->num_kv_heads;
+  const size_t tile_bytes = (size_t)cfg->page_size * cfg->head_dim * elem_bytes(cfg->kv_dtype);
+  const size_t sizes[LOCKS_HOT_CACHE_FIELDS] = {
+      locks::kCacheStats * sizeof(int64_t), 2 * sizeof(int64_t), 2 * sizeof(int32_t), tiles * sizeof(int32_t),
+      (size_t)capacity * sizeof(int32_t), (size_t)capacity * sizeof(int32_t), (size_t)capacity * sizeof(int32_t),
+      (size_t)capacity * tile_bytes, (size_t)capacity * tile_bytes};
+  CacheLayout L{};
+  size_t at = 0;
+  for (int i = 0; i < LOCKS_HOT_CACHE_FIELDS; ++i) {
+    L.off[i] = at;
+    at += align_up(sizes[i]);
+  }
+  L.bytes = at;
+  return L;
+}
+
+int check_cache(const locks_config_t* cfg, int64_t num_blocks, int32_t capacity) {
+  if (num_blocks < 1 || capacity < 1) return LOCKS_E_INVALID_ARG;
+  // tile ids and page-slot claims are int32
+  if (num_blocks * cfg->num_kv_heads >= (int64_t)0x7fffffff) return LOCKS_E_UNSUPPORTED;
+  return LOCKS_OK;
+}
+
+locks::CacheArgs cache_args(const locks_config_t* cfg, void* cache, int64_t num_blocks, int32_t capacity) {
+  const CacheLayout L = cache_layout(cfg, num_blocks, capacity);
+  uint8_t* c = static_cast<uint8_t*>(cache);
+  locks::CacheArgs a{};
+  a.stats = reinterpret_cast<long long*>(c + L.off[LOCKS_HOT_CACHE_STATS]);
+  a.meta = reinterpret_cast<long long*>(c + L.off[LOCKS_HOT_CACHE_META]);
+  a.state = reinterpret_cast<int32_t*>(c + L.off[LOCKS_HOT_CACHE_CLOCK]);
+  a.slot_of = reinterpret_cast<int32_t*>(c + L.off[LOCKS_HOT_CACHE_SLOT_OF]);
+  a.tile_of = reinterpret_cast<int32_t*>(c + L.off[LOCKS_HOT_CACHE_TILE_OF]);
+  a.stamp = reinterpret_cast<int32_t*>(c + L.off[LOCKS_HOT_CACHE_STAMP]);
+  a.flags = reinterpret_cast<int32_t*>(c + L.off[LOCKS_HOT_CACHE_FLAGS]);
+  a.k_slots = c + L.off[LOCKS_HOT_CACHE_K];
+  a.v_slots = c + L.off[LOCKS_HOT_CACHE_V];
+  a.num_blocks = num_blocks;
+  a.tile_bytes = (int64_t)cfg->page_size * cfg->head_dim * elem_bytes(cfg->kv_dtype);
+  a.Hkv = cfg->num_kv_heads;
+  a.P = cfg->page_size;
+  a.k = cfg->budget_pages;
+  a.capacity = capacity;
+  return a;
 }
 
 // argument checks shared by the two whole-step entry points
@@ -373,6 +434,78 @@ int locks_decode_step(const locks_config_t* cfg, const void* q, const void* summ
   if (st != LOCKS_OK) return st;
   return enqueue_sparse_decode(cfg, q, k_pool, v_pool, num_blocks, block_table, seq_lens, selected, batch,
                                max_pages, out, lse, ws, ws_bytes, stream);
+}
+
+int locks_hot_cache_layout(const locks_config_t* cfg, int64_t num_blocks, int32_t capacity,
+                           int64_t* offsets, size_t* bytes) {
+  int st = check_config(cfg);
+  if (st != LOCKS_OK) return st;
+  st = check_cache(cfg, num_blocks, capacity);
+  if (st != LOCKS_OK) return st;
+  if (!bytes) return LOCKS_E_INVALID_ARG;
+  const CacheLayout L = cache_layout(cfg, num_blocks, capacity);
+  if (offsets)
+    for (int i = 0; i < LOCKS_HOT_CACHE_FIELDS; ++i) offsets[i] = (int64_t)L.off[i];
+  *bytes = L.bytes;
+  return LOCKS_OK;
+}
+
+int locks_hot_cache_init(const locks_config_t* cfg, void* cache, int64_t num_blocks, int32_t capacity,
+                         hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != LOCKS_OK) return st;
+  st = check_cache(cfg, num_blocks, capacity);
+  if (st != LOCKS_OK) return st;
+  if (!cache) return LOCKS_E_INVALID_ARG;
+  locks::CacheArgs a = cache_args(cfg, cache, num_blocks, capacity);
+  return hip_status(locks::launch_cache_init(a, num_blocks * cfg->num_kv_heads, stream));
+}
+
+int locks_decode_step_cached(const locks_config_t* cfg, const void* q, const void* summary_pool,
+                             const void* k_pool, const void* v_pool, int64_t num_blocks,
+                             const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                             int32_t max_pages, int32_t* selected, void* out, float* lse, void* cache,
+                             int32_t capacity, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_step(cfg, q, summary_pool, k_pool, v_pool, num_blocks, block_table, seq_lens, batch, max_pages,
+                      selected, out);
+  if (st != LOCKS_OK || batch == 0) return st;
+  st = check_cache(cfg, num_blocks, capacity);
+  if (st != LOCKS_OK) return st;
+  if (!cache) return LOCKS_E_INVALID_ARG;
+  const int64_t n = (int64_t)batch * cfg->num_kv_heads * cfg->budget_pages;
+  if (n > capacity) return LOCKS_E_INVALID_ARG;  // one step's tiles must fit
+  if (!ws || ws_bytes < step_ws_bytes(cfg, batch, max_pages)) return LOCKS_E_WORKSPACE;
+  st = enqueue_score_select(cfg, q, summary_pool, num_blocks, block_table, seq_lens, batch, max_pages, selected, ws,
+                            ws_bytes, stream);
+  if (st != LOCKS_OK) return st;
+  // the lists sit below the decode scratch
+  const size_t dec_scratch = decode_ws_bytes(cfg, batch) - ctl_bytes(cfg, batch);
+  uint8_t* lists = scratch_base(ws, ws_bytes, dec_scratch) - cache_ws_bytes(cfg, batch);
+  const size_t list = align_up((size_t)n * sizeof(int32_t));
+  locks::CacheArgs a = cache_args(cfg, cache, num_blocks, capacity);
+  a.selected = selected;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.tile_e = reinterpret_cast<int32_t*>(lists);
+  a.map = reinterpret_cast<int32_t*>(lists + list);
+  a.fill = reinterpret_cast<int32_t*>(lists + 2 * list);
+  a.victims = reinterpret_cast<int32_t*>(lists + 4 * list);
+  a.fill_count = reinterpret_cast<int32_t*>(lists + 5 * list);
+  a.k_src = k_pool;
+  a.v_src = v_pool;
+  a.max_pages = max_pages;
+  a.batch = batch;
+  if (locks::launch_cache_admit(a, stream) != hipSuccess) return LOCKS_E_HIP;
+  if (locks::launch_cache_fill(a, stream) != hipSuccess) return LOCKS_E_HIP;
+  const size_t rows = (size_t)batch * cfg->num_q_heads * locks::decode_max_splits(cfg->budget_pages, cfg->page_size);
+  uint8_t* region = scratch_base(ws, ws_bytes, dec_scratch);
+  locks::DecodeArgs d = decode_args(cfg, q, a.k_slots, a.v_slots, num_blocks, block_table, seq_lens, selected,
+                                    batch, max_pages, out, lse, static_cast<int32_t*>(ws),
+                                    reinterpret_cast<float*>(region),
+                                    reinterpret_cast<float*>(region + align_up(rows * cfg->head_dim * sizeof(float))));
+  d.tile_map = a.map;
+  d.map_tiles = capacity;
+  return hip_status(locks::launch_sparse_decode(d, cfg->kv_dtype, cfg->head_dim, batch, stream));
 }
 
 }  // extern "C"

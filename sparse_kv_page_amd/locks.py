@@ -29,7 +29,12 @@ EXPORTED = ("locks_status_string", "locks_version", "locks_summary_record_bytes"
             "locks_workspace_size", "locks_build_summaries", "locks_build_summaries_ex",
             "locks_page_score",
             "locks_select_pages", "locks_score_select", "locks_sparse_decode",
-            "locks_decode_step")
+            "locks_decode_step", "locks_hot_cache_layout", "locks_hot_cache_init",
+            "locks_decode_step_cached")
+
+# fields of the hot-page cache buffer, in order (locks_hot_cache_layout)
+HOT_CACHE_FIELDS = ("stats", "meta", "clock", "slot_of", "tile_of", "stamp", "flags", "k", "v")
+HOT_CACHE_STATS = ("hits", "misses", "refreshes", "shared", "failed", "steps")
 
 
 class LocksError(RuntimeError):
@@ -89,10 +94,15 @@ def lib():
                                           sz, vp]
         L.locks_decode_step.argtypes = [cp, vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp, vp,
                                         sz, vp]
+        L.locks_hot_cache_layout.argtypes = [cp, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(sz)]
+        L.locks_hot_cache_init.argtypes = [cp, vp, i64, i32, vp]
+        L.locks_decode_step_cached.argtypes = [cp, vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp, vp,
+                                               i32, vp, sz, vp]
         for name in ("locks_workspace_size", "locks_build_summaries", "locks_build_summaries_ex",
                      "locks_page_score",
                      "locks_select_pages", "locks_score_select", "locks_sparse_decode",
-                     "locks_decode_step"):
+                     "locks_decode_step", "locks_hot_cache_layout", "locks_hot_cache_init",
+                     "locks_decode_step_cached"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -207,6 +217,30 @@ def locks_decode_step(cfg, q, summary_pool, k_pool, v_pool, num_blocks, block_ta
                                    _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
+def locks_hot_cache_layout(cfg: Config, num_blocks: int, capacity: int):
+    """(offsets dict by HOT_CACHE_FIELDS name, total bytes) of a hot-page cache buffer."""
+    offs = (ctypes.c_int64 * len(HOT_CACHE_FIELDS))()
+    nb = ctypes.c_size_t(0)
+    _check("locks_hot_cache_layout",
+           lib().locks_hot_cache_layout(ctypes.byref(cfg), int(num_blocks), int(capacity), offs, ctypes.byref(nb)))
+    return dict(zip(HOT_CACHE_FIELDS, list(offs))), nb.value
+
+
+def locks_hot_cache_init(cfg, cache, num_blocks, capacity, stream=None):
+    _check("locks_hot_cache_init",
+           lib().locks_hot_cache_init(ctypes.byref(cfg), _ptr(cache), int(num_blocks), int(capacity),
+                                      _stream(stream)))
+
+
+def locks_decode_step_cached(cfg, q, summary_pool, k_pool, v_pool, num_blocks, block_table, seq_lens, batch,
+                             max_pages, selected, out, lse, cache, capacity, ws, ws_bytes, stream=None):
+    _check("locks_decode_step_cached",
+           lib().locks_decode_step_cached(ctypes.byref(cfg), _ptr(q), _ptr(summary_pool), _ptr(k_pool),
+                                          _ptr(v_pool), int(num_blocks), _ptr(block_table), _ptr(seq_lens),
+                                          int(batch), int(max_pages), _ptr(selected), _ptr(out), _ptr(lse),
+                                          _ptr(cache), int(capacity), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
 # --------------------------------------------------------------------------
 # Convenience layer over torch tensors (allocation of outputs / workspace)
 # --------------------------------------------------------------------------
@@ -221,6 +255,38 @@ def summary_pool_for(cfg: Config, num_blocks: int, device) -> torch.Tensor:
     dt = torch.bfloat16 if cfg.summary_dtype == LOCKS_BF16 else torch.float32
     el = rb // (2 if dt == torch.bfloat16 else 4)
     return torch.empty((num_blocks, cfg.num_kv_heads, el), dtype=dt, device=device)
+
+
+class HotCache:
+    """A hot-page cache buffer on `device` for a pool of num_blocks blocks with
+    `capacity` tile slots, emptied on creation; views of its state."""
+
+    def __init__(self, cfg: Config, num_blocks: int, capacity: int, device, stream=None):
+        self.cfg, self.num_blocks, self.capacity = cfg, int(num_blocks), int(capacity)
+        self.offsets, self.bytes = locks_hot_cache_layout(cfg, num_blocks, capacity)
+        self.buf = torch.empty(self.bytes, dtype=torch.uint8, device=device)
+        locks_hot_cache_init(cfg, self.buf, num_blocks, capacity, stream)
+
+    def reset(self, stream=None):
+        locks_hot_cache_init(self.cfg, self.buf, self.num_blocks, self.capacity, stream)
+
+    def field(self, name: str, dtype, count: int) -> torch.Tensor:
+        o = self.offsets[name]
+        return self.buf[o:o + count * torch.tensor([], dtype=dtype).element_size()].view(dtype)
+
+    def stats(self) -> dict:
+        """Counters (host ints): hits, misses, refreshes, shared, failed, steps."""
+        v = self.field("stats", torch.int64, len(HOT_CACHE_STATS)).cpu().tolist()
+        return dict(zip(HOT_CACHE_STATS, v))
+
+    def state(self) -> dict:
+        """Host copies of the clock state and maps (int32 tensors; hand and step as ints)."""
+        tiles = self.num_blocks * self.cfg.num_kv_heads
+        hand, step = self.field("clock", torch.int32, 2).cpu().tolist()
+        return dict(hand=hand, step=step, slot_of=self.field("slot_of", torch.int32, tiles).cpu(),
+                    tile_of=self.field("tile_of", torch.int32, self.capacity).cpu(),
+                    stamp=self.field("stamp", torch.int32, self.capacity).cpu(),
+                    flags=self.field("flags", torch.int32, self.capacity).cpu())
 
 
 def split_records(cfg: Config, pool: torch.Tensor):

@@ -237,6 +237,24 @@ def random_i4_codes(wl: Workload, seed: int = 0, device="cpu"):
 # sequence s holds base_len + stagger * s tokens, each step appending one token
 # to every sequence (so with stagger 4 and 16 sequences at most one sequence
 # completes a page per step).
+def query_sequence(q0: torch.Tensor, steps: int, rho: float, seed: int = 0) -> torch.Tensor:
+    """Queries of `steps` consecutive decode steps, [steps][*q0.shape] in
+    q0's dtype on q0's device: an AR(1) sequence per element,
+    q_0 = q0, q_{t+1} = rho q_t + sqrt(1 - rho^2) eps_t, eps_t iid standard
+    normal, so each step's queries keep the N(0, 1) marginal of generate()'s q
+    while consecutive steps stay correlated (rho = 0: independent queries)."""
+    g = torch.Generator(device=q0.device)
+    g.manual_seed(int(seed) + 77)
+    out = torch.empty((steps,) + tuple(q0.shape), dtype=q0.dtype, device=q0.device)
+    cur = q0.float()
+    s = math.sqrt(max(0.0, 1.0 - rho * rho))
+    for t in range(steps):
+        out[t] = cur.to(q0.dtype)
+        eps = torch.randn(cur.shape, generator=g, device=q0.device, dtype=torch.float32)
+        cur = rho * cur + s * eps
+    return out
+
+
 FULL_STEP = dict(layers=32, batch=16, kv_heads=8, group=4, head_dim=128, page_size=64, rank=4,
                  budget_pages=32, base_len=65536, stagger=4)
 

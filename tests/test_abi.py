@@ -144,6 +144,10 @@ def test_config_errors(kw, status):
                                       None, fake, 1 << 30, stream=0),
         lambda: L.locks_decode_step(cfg, fake, fake, fake, fake, 10, fake, fake, 1, 4, fake, fake,
                                     None, fake, 1 << 30, stream=0),
+        lambda: L.locks_hot_cache_layout(cfg, 10, 1000),
+        lambda: L.locks_hot_cache_init(cfg, fake, 10, 1000, stream=0),
+        lambda: L.locks_decode_step_cached(cfg, fake, fake, fake, fake, 10, fake, fake, 1, 4, fake, fake,
+                                           None, fake, 1000, fake, 1 << 30, stream=0),
     ]
     for c in calls:
         with pytest.raises(L.LocksError) as ei:
@@ -226,6 +230,57 @@ def test_workspace_monotone_and_empty_calls():
                           stream=0)
     L.locks_decode_step(cfg, None, None, None, None, 0, None, None, 0, 0, None, None, None, None, 0,
                         stream=0)
+    L.locks_decode_step_cached(cfg, None, None, None, None, 0, None, None, 0, 0, None, None, None, None, 0,
+                               None, 0, stream=0)
+
+
+def test_hot_cache_layout():
+    """Fields in the header's order, 256-byte aligned, each as large as the
+    header states: 8 + 2 int64, 2 int32, one int32 per (block, KV head) tile,
+    three int32 per slot, and a P x d K and V tile per slot."""
+    cfg = _cfg()
+    nb, cap = 1000, 300
+    offs, nbytes = L.locks_hot_cache_layout(cfg, nb, cap)
+    o = [offs[f] for f in L.HOT_CACHE_FIELDS]
+    assert o[0] == 0 and all(x % 256 == 0 for x in o) and o == sorted(o)
+    tile = 64 * 128 * 2
+    sizes = [64, 16, 8, nb * 8 * 4, cap * 4, cap * 4, cap * 4, cap * tile, cap * tile]
+    for i, sz in enumerate(sizes):
+        end = o[i + 1] if i + 1 < len(o) else nbytes
+        assert sz <= end - o[i] < sz + 256, L.HOT_CACHE_FIELDS[i]
+    f32 = _cfg(kv_dtype="f32")
+    _, nb32 = L.locks_hot_cache_layout(f32, nb, cap)
+    assert nb32 - nbytes == 2 * cap * tile
+
+
+def test_hot_cache_argument_errors():
+    """Reported on the host before anything is enqueued."""
+    cfg = _cfg()
+    fake = 1 << 20
+    need = L.locks_workspace_size(cfg, 2, 64)
+    n = 2 * 8 * 32  # batch * H_kv * k tiles in one step
+    cases = [
+        (lambda: L.locks_hot_cache_layout(cfg, 0, 10), L.LOCKS_E_INVALID_ARG),
+        (lambda: L.locks_hot_cache_layout(cfg, 10, 0), L.LOCKS_E_INVALID_ARG),
+        (lambda: L.locks_hot_cache_layout(cfg, 1 << 28, 10), L.LOCKS_E_UNSUPPORTED),
+        (lambda: L.locks_hot_cache_init(cfg, None, 10, 10, stream=0), L.LOCKS_E_INVALID_ARG),
+        (lambda: L.locks_hot_cache_init(cfg, fake, 10, -1, stream=0), L.LOCKS_E_INVALID_ARG),
+        # capacity below one step's tiles
+        (lambda: L.locks_decode_step_cached(cfg, fake, fake, fake, fake, 10, fake, fake, 2, 64, fake, fake,
+                                            None, fake, n - 1, fake, need, stream=0), L.LOCKS_E_INVALID_ARG),
+        (lambda: L.locks_decode_step_cached(cfg, fake, fake, fake, fake, 10, fake, fake, 2, 64, fake, fake,
+                                            None, None, n, fake, need, stream=0), L.LOCKS_E_INVALID_ARG),
+        (lambda: L.locks_decode_step_cached(cfg, fake, fake, None, fake, 10, fake, fake, 2, 64, fake, fake,
+                                            None, fake, n, fake, need, stream=0), L.LOCKS_E_INVALID_ARG),
+        (lambda: L.locks_decode_step_cached(cfg, fake, fake, fake, fake, 10, fake, fake, 2, 64, fake, fake,
+                                            None, fake, n, fake, need - 1, stream=0), L.LOCKS_E_WORKSPACE),
+        (lambda: L.locks_decode_step_cached(cfg, fake, fake, fake, fake, 10, fake, fake, 2, 64, fake, fake,
+                                            None, fake, n, None, need, stream=0), L.LOCKS_E_WORKSPACE),
+    ]
+    for c, status in cases:
+        with pytest.raises(L.LocksError) as ei:
+            c()
+        assert ei.value.status == status
 
 
 def test_binding_refuses_host_tensors():

@@ -917,7 +917,7 @@ def test_decode_with_host_resident_kv():
 # against the oracle, and the pages built inside the graph against the
 # oracle's fit.
 # --------------------------------------------------------------------------
-FULL_STEPS = 6
+FULL_STEPS = 16
 
 
 def full_step_graph(cfg, inp, spool, seq, sel, out, lse, ws, ws_bytes, step_idx, ids_buf):
