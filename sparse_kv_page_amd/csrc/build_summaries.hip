@@ -36,9 +36,12 @@
 //     iteration continues from M U. The number of products, and whether the
 //     bounds were met within the cap, are reported by
 //     locks_build_summaries_ex.
-//  4. V = D^T U_r (matrix cores), orthonormalised by Cholesky-QR (a second
-//     pass when a column vanished and was replaced), each column sign-fixed so
-//     its largest-magnitude entry is positive (lowest index on ties).
+//  4. V = D^T U_r (matrix cores), normalised and made orthonormal to fp32
+//     level by one Newton-Schulz step (the columns of Ritz vectors are already
+//     nearly orthogonal), or, when the r-th Ritz value is tiny against the
+//     first, by Cholesky-QR (a second pass when a column vanished and was
+//     replaced); each column sign-fixed so its largest-magnitude entry is
+//     positive (lowest index on ties).
 //  5. C = D V in fp32 from the unrounded V (matrix cores); mu, V, C are rounded
 //     to the summary dtype independently. Quantized ("i4") records, [Locks] §4
 //     and App. C.7: per group (the centroid, each basis vector, each token's
@@ -57,8 +60,8 @@ constexpr float kRitzTol = 1.0f / 1024.0f;  // residual bound of every pair, rel
 constexpr float kGapFloor = 1.0f / 128.0f;  // a Ritz gap above this fraction of the largest value is significant
 constexpr float kSubspaceTol = 1.0f / 64.0f;   // residual bound of a leading subspace, relative to its gap
 constexpr int kMaxSweeps = 12;              // Jacobi sweeps of one Rayleigh-Ritz step
-constexpr float kJacobiRel = 0x1p-12f;      // off-diagonal entries below this relative size are converged
-constexpr float kJacobiStop = 0x1p-8f;      // a sweep whose largest rotated relative entry is below this is the last
+constexpr float kJacobiAbs = 0x1p-20f;      // off-diagonal entries below this fraction of the largest diagonal are converged
+constexpr float kJacobiStop = 0x1p-10f;     // a sweep whose largest rotated entry is below this fraction is the last
 
 namespace {
 
@@ -345,6 +348,52 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
     return dead;
   };
 
+  // One Newton-Schulz step towards orthonormal columns for the first r
+  // columns of the NR x 16 rows in `buf` (columns r.. become zero):
+  // buf <- buf S (3/2 I - 1/2 S G S), G = buf^T buf, S = diag(G)^-1/2, which
+  // takes columns whose pairwise cosines are at most e to at most about
+  // 3/2 e^2 (the same two barriers as cholqr, no serial factorisation).
+  // Returns the largest cosine it started from (uniform: every wave forms
+  // the same value from the same sums).
+  auto ns_orth = [&](float (*buf)[kBlk], int NR, int ncols) -> float {
+    f32x4_t m = {0.f, 0.f, 0.f, 0.f};
+    for (int t = wave; t < NR / 16; t += 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = buf[16 * t + 4 * lg + i][ln];
+        m = __builtin_amdgcn_mfma_f32_16x16x4f32(v, v, m, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L.Gp[wave][4 * lg + i][ln] = m[i];
+    __syncthreads();
+    auto gsum = [&](int x, int y) { return (L.Gp[0][x][y] + L.Gp[1][x][y]) + (L.Gp[2][x][y] + L.Gp[3][x][y]); };
+    const float sj = ln < ncols ? __builtin_amdgcn_rsqf(gsum(ln, ln)) : 0.f;
+    float cmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * lg + i;
+      const float si = row < ncols ? __builtin_amdgcn_rsqf(gsum(row, row)) : 0.f;
+      const float cs = si * gsum(row, ln) * sj;  // cosine of columns row, ln
+      cmax = row != ln ? fmaxf(cmax, fabsf(cs)) : cmax;
+      L.RiW[wave][row][ln] = si * ((row == ln ? 1.5f : 0.f) - 0.5f * cs);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, o, 64));
+    wave_lds_sync();  // RiW[wave] visible to the wave
+    for (int t = wave; t < NR / 16; t += 4) {
+      f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < kBlk; k0 += 4)
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(buf[16 * t + ln][k0 + lg], L.RiW[wave][k0 + lg][ln], x, 0, 0, 0);
+      wave_lds_sync();  // every lane's reads of the tile are done before it is overwritten
+#pragma unroll
+      for (int i = 0; i < 4; ++i) buf[16 * t + 4 * lg + i][ln] = x[i];
+    }
+    __syncthreads();
+    return __shfl(cmax, 0, 64);
+  };
+
   // Y = M X for this wave's rows (wave < NB): lane (ln, lg) -> Y[16 wave + 4 lg + i][ln]
   auto product = [&]() {
     if (wave < NB) {
@@ -365,29 +414,35 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
   // the other buffer. The 8 threads owning the next round's off-diagonal
   // entries also form the three entries of their pair that the next rotation
   // needs and publish it with their own update, so a round costs one barrier.
-  // A pair is rotated only while its off-diagonal entry exceeds kJacobiRel of
-  // sqrt(|t_pp t_qq|) and 2^-20 of the trace (below that the entries are fp32
-  // rounding of the rotations and move no eigenvector whose eigen-gap is
-  // significant); the sweeps stop after one whose largest rotated relative
-  // entry is below kJacobiStop (the next sweep's would be of its square).
+  // (One wave doing all 256 elements with wave-level waits instead of
+  // barriers measured slower: 0.85 against 0.46 us per round.)
+  // A pair is rotated only while its off-diagonal entry exceeds 2^-20 of the
+  // largest diagonal entry t_max (about the largest eigenvalue): a smaller
+  // entry moves an eigenvector by at most 2^-20 t_max / gap, and the Ritz
+  // pairs are only used where the gap is a sizeable fraction of t_max. Pairs
+  // of two small eigenvalues therefore stop rotating as soon as their
+  // coupling is small against t_max. The sweeps stop after one whose largest
+  // rotated entry is below 2^-10 t_max (the next sweep's would be of about
+  // its square). Stopping at 2^-7 saved a sweep in half the tiles but not its
+  // time, and cost fp32 fits their accuracy.
   // Then Wo = W in descending order of eigenvalue, th = those eigenvalues.
   auto jacobi = [&]() {
     const int jx = tid >> 4, jy = tid & 15;
-    float tr = 0.f;
+    float tmax = 0.f;
 #pragma unroll
-    for (int i = 0; i < kBlk; ++i) tr += L.Ms[0][i][i];
-    const float floor_abs = 0x1p-20f * fabsf(tr);
+    for (int i = 0; i < kBlk; ++i) tmax = fmaxf(tmax, fabsf(L.Ms[0][i][i]));
+    const float floor_abs = kJacobiAbs * tmax;
+    const float inv_tmax = tmax > 0.f ? 1.0f / tmax : 0.f;
     // rotation of the pair (p, q = p ^ t), p < q, from entries app, aqq, apq
     auto publish = [&](int buf, int p, int q, float app, float aqq, float apq, int sb) {
       float c = 1.f, sn = 0.f;
-      if (fabsf(apq) > floor_abs && fabsf(apq) > kJacobiRel * __builtin_amdgcn_sqrtf(fabsf(app * aqq))) {
+      if (fabsf(apq) > floor_abs) {
         const float theta = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
         const float tt = (theta >= 0.f ? 1.f : -1.f) *
                          __builtin_amdgcn_rcpf(fabsf(theta) + __builtin_amdgcn_sqrtf(theta * theta + 1.f));
         c = __builtin_amdgcn_rsqf(tt * tt + 1.f);
         sn = tt * c;
-        const float rel = fabsf(apq) * __builtin_amdgcn_rsqf(fmaxf(fabsf(app * aqq), 1e-30f));
-        atomicMax(&L.swmax[sb], __float_as_uint(fminf(rel, 1e30f)));
+        atomicMax(&L.swmax[sb], __float_as_uint(fminf(fabsf(apq) * inv_tmax, 1e30f)));
       }
       L.jc[buf][p] = c; L.jo[buf][p] = -sn;
       L.jc[buf][q] = c; L.jo[buf][q] = sn;
@@ -559,7 +614,18 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
     for (int i = 0; i < 4; ++i) L.Vb[16 * b + 4 * lg + i][ln] = v[i];
   }
   __syncthreads();
-  if (cholqr(L.Vb, D, 101u)) cholqr(L.Vb, D, 102u);  // a replaced column is orthonormalised by a second pass
+  // The columns D^T u_i of Ritz vectors are orthogonal up to the Jacobi
+  // sweeps' remaining coupling (about 2^-20 theta_1) against norms
+  // sqrt(theta_i), so unless the r-th Ritz value is tiny against the first,
+  // a Newton-Schulz step makes them orthonormal (a second one when the
+  // first found cosines above 2^-10); otherwise (a page of nearly lower rank)
+  // Cholesky-QR, which also replaces vanishing columns.
+  const float th0 = L.th[0], thr = L.th[r - 1];
+  if (th0 > 0.f && thr > 0x1p-16f * th0 && th0 < 3.0e38f) {
+    if (ns_orth(L.Vb, D, r) > 0x1p-10f) ns_orth(L.Vb, D, r);
+  } else if (cholqr(L.Vb, D, 101u)) {
+    cholqr(L.Vb, D, 102u);  // a replaced column is orthonormalised by a second pass
+  }
   // sign: largest-magnitude entry positive (lowest index on ties)
   for (int rho = wave; rho < r; rho += 4) {
     float best = -1.f;
