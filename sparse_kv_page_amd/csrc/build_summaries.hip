@@ -276,14 +276,22 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
 #pragma unroll
     for (int j = 0; j < kBlk; ++j) {
       const float vjj = rdl(am[j], j);
-      const bool ok = vjj > 1e-12f && !((dead >> j) & 1u);
+      const bool ok = vjj > 1e-12f && !((dead >> j) & 1u);  // uniform
       const float rj = ok ? __builtin_amdgcn_rsqf(vjj) : 1.0f;
       invd[j] = rj;
-      const float lij = row > j ? (ok ? am[j] * rj : 0.f) : (row == j ? (ok ? vjj * rj : 1.0f) : 0.f);
+      // L[row][j]: below the pivot am * rj, on it sqrt(v) (1 for a dead
+      // column), above it 0; per-lane selects, no branch
+      const float below = ok ? am[j] * rj : 0.f;
+      const float diag = ok ? vjj * rj : 1.0f;
+      const float lij = row > j ? below : (row == j ? diag : 0.f);
       am[j] = lij;
       dead |= ok ? 0u : 1u << j;
+      // the column's entries as scalars first, then the updates
+      float lk[kBlk];
 #pragma unroll
-      for (int k = j + 1; k < kBlk; ++k) am[k] = fmaf(-lij, rdl(lij, k), am[k]);
+      for (int k = j + 1; k < kBlk; ++k) lk[k] = rdl(lij, k);
+#pragma unroll
+      for (int k = j + 1; k < kBlk; ++k) am[k] = fmaf(-lij, lk[k], am[k]);
     }
     // li[i] = (L^-1)[i][row]
     float li[kBlk];

@@ -24,10 +24,12 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(
 
 // float -> bfloat16 bits, round to nearest, ties to even; NaN stays NaN.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  // round to nearest even; a NaN keeps its top bits and becomes quiet. Both
+  // results are formed and one selected, so no branch is generated.
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t nan = (u >> 16) | 0x40u;
+  return (bf16_t)((u & 0x7fffffffu) > 0x7f800000u ? nan : rne);
 }
 
 // Storage element helpers: T is bf16_t or float.
