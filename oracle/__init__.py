@@ -23,7 +23,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "locks_oracle.cpp")
-_LIB = os.path.join(_HERE, "liblocks_oracle.so")
+_LIB_DEFAULT = os.path.join(_HERE, "liblocks_oracle.so")
+# LOCKS_ORACLE_LIB names another build of the same source to load instead
+# (the sanitizer test uses one); it is taken as it is, never rebuilt
+_LIB = os.environ.get("LOCKS_ORACLE_LIB") or _LIB_DEFAULT
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
@@ -32,6 +35,8 @@ _ip = ctypes.POINTER(ctypes.c_int)
 
 def build(force: bool = False) -> str:
     """Compile the oracle with g++ (plain -O2, no fast-math)."""
+    if _LIB != _LIB_DEFAULT:
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
         subprocess.check_call(

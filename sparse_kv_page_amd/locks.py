@@ -13,7 +13,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblocks.so")
+# LOCKS_LIB names another build of the same sources to load instead (the
+# sanitizer test loads a build whose host code carries ASan and UBSan)
+LIB_PATH = os.environ.get("LOCKS_LIB") or os.path.join(_HERE, "liblocks.so")
 
 LOCKS_OK = 0
 LOCKS_E_INVALID_ARG = -1
