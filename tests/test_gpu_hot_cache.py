@@ -162,3 +162,76 @@ def test_cached_step_128k_batch8():
     total = s["hits"] + s["misses"] + s["refreshes"] + s["shared"]
     print(f"[cache] 128K batch 8: hit share {s['hits'] / total:.3f} over {s['steps']} steps: {s}")
     assert s["failed"] == 0 and s["shared"] == 0
+
+
+def test_cached_step_in_a_graph():
+    """The cached step captured into a HIP graph (queries and lengths read
+    from buffers the program refills between replays) and replayed over 8
+    steps, with eager work in between: every replay's selection, output and
+    the cache's whole state equal those of the same steps run eagerly on a
+    second cache."""
+    wl = GROW
+    cfg = _cfg(wl)
+    steps = 8
+    n = wl.batch * wl.num_kv_heads * wl.budget_pages
+    capacity = n + n // 4
+    g = synth.generate(wl, 11, gg.DEV)
+    P, NB, Hkv = wl.page_size, wl.num_blocks, wl.num_kv_heads
+    lens0 = [int(x) - (steps - 1) for x in wl.seq_lens]
+    pool = gg.gpu_build(wl, cfg, g)  # every page complete at the end; earlier steps see only their own
+    kh, kdev = gg.host_pool(g["k_pool"])
+    vh, vdev = gg.host_pool(g["v_pool"])
+    qs = synth.query_sequence(g["q"], steps, 0.8, 11)
+    nbytes = L.locks_workspace_size(cfg, wl.batch, wl.max_pages)
+    dt = synth.torch_dtype(wl.kv_dtype)
+
+    def buffers():
+        return (torch.zeros(nbytes, dtype=torch.uint8, device=gg.DEV),
+                torch.empty((wl.batch, Hkv, wl.budget_pages), dtype=torch.int32, device=gg.DEV),
+                torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=dt, device=gg.DEV),
+                torch.empty((wl.batch, wl.num_q_heads), device=gg.DEV))
+
+    # eager reference on cache A
+    cache_a = L.HotCache(cfg, NB, capacity, gg.DEV)
+    ws_a, sel_a, out_a, lse_a = buffers()
+    ref = []
+    for t in range(steps):
+        seq = torch.tensor([x + t for x in lens0], dtype=torch.int32, device=gg.DEV)
+        L.locks_decode_step_cached(cfg, qs[t], pool, kdev, vdev, NB, g["block_table"], seq, wl.batch, wl.max_pages,
+                                   sel_a, out_a, lse_a, cache_a.buf, capacity, ws_a, nbytes)
+        torch.cuda.synchronize()
+        ref.append((sel_a.clone(), out_a.clone(), lse_a.clone(), cache_a.state(), cache_a.stats()))
+    # the same steps replayed from one graph on cache B
+    cache_b = L.HotCache(cfg, NB, capacity, gg.DEV)
+    ws_b, sel_b, out_b, lse_b = buffers()
+    q_buf = qs[0].clone()
+    seq_buf = torch.tensor(lens0, dtype=torch.int32, device=gg.DEV)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            L.locks_decode_step_cached(cfg, q_buf, pool, kdev, vdev, NB, g["block_table"], seq_buf, wl.batch,
+                                       wl.max_pages, sel_b, out_b, lse_b, cache_b.buf, capacity, ws_b, nbytes)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    st0 = cache_b.stats()
+    assert st0["steps"] == 0, "capturing must not run the step"
+    for t in range(steps):
+        q_buf.copy_(qs[t])
+        seq_buf.copy_(torch.tensor([x + t for x in lens0], dtype=torch.int32))
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = torch.randn(1024, device=gg.DEV).sum().item()  # eager work between replays
+        s_ref, o_ref, l_ref, state_ref, stats_ref = ref[t]
+        assert torch.equal(sel_b, s_ref), f"replay {t}: selection"
+        assert torch.equal(out_b.view(torch.int16), o_ref.view(torch.int16)), f"replay {t}: output"
+        assert torch.equal(lse_b, l_ref), f"replay {t}: lse"
+        st = cache_b.state()
+        for key in ("hand", "step"):
+            assert st[key] == state_ref[key], f"replay {t}: {key}"
+        for key in ("slot_of", "tile_of", "stamp", "flags"):
+            assert torch.equal(st[key], state_ref[key]), f"replay {t}: {key}"
+        assert cache_b.stats() == stats_ref, f"replay {t}: counters"
+    del kh, vh
