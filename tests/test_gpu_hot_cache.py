@@ -96,13 +96,17 @@ GROW = synth.Workload("cache_grow", 3, 4, 2, 128, 64, (64 * 30 + 4, 64 * 25 + 40
                       "bf16", "bf16", centroid_std=0.5, ar_rho=0.99, n_needles=4)
 
 
-@pytest.mark.parametrize("capacity_mult,rho", [(1.25, 0.7), (3.0, 0.9), (1.0, 0.0)])
-def test_cached_step_against_oracle(capacity_mult, rho):
+GROW_F32 = synth.Workload("cache_grow_f32", 2, 2, 2, 64, 16, (16 * 40 + 3, 16 * 23 + 9), 4, 6, "f32", "f32")
+
+
+@pytest.mark.parametrize("wl,capacity_mult,rho", [(GROW, 1.25, 0.7), (GROW, 3.0, 0.9), (GROW, 1.0, 0.0),
+                                                   (GROW_F32, 1.5, 0.8)],
+                         ids=["bf16-x1.25", "bf16-x3", "bf16-x1-indep", "f32-p16-x1.5"])
+def test_cached_step_against_oracle(wl, capacity_mult, rho):
     """Growing lengths over 14 steps (every sequence's current page is
-    incomplete at first, two complete during the run): every unit of every
+    incomplete at first, pages complete during the run): every unit of every
     step against the oracle, bits against the uncached step, state against the
-    policy model."""
-    wl = GROW
+    policy model; bf16 at 64-token pages and fp32 at 16-token pages."""
     steps = 14
     n = wl.batch * wl.num_kv_heads * wl.budget_pages
     capacity = int(n * capacity_mult)
