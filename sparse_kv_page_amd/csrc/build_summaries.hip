@@ -119,8 +119,8 @@ struct alignas(16) BuildLds {
   float Wm[2][kBlk][kBlk + 1];  // its accumulated rotations, ping-pong
   float Wo[kBlk][kBlk];    // eigenvectors of T, descending eigenvalue order
   float th[kBlk];          // Ritz values, descending
-  float jc[2][kBlk], jo[2][kBlk];  // rotation of a Jacobi round (this one, the next): self / other coefficient
-  uint32_t swmax[2];       // largest relative off-diagonal rotated in a sweep (float bits), alternating
+  float2 jr[2][kBlk];      // rotation of a Jacobi round (this one, the next): (self, other) coefficients
+  uint32_t swbig[2];       // a sweep rotated an entry above kJacobiStop t_max (alternating by sweep)
   float res[4][kBlk];      // partial squared residual norms
   int order[kBlk];
   int flag;
@@ -429,9 +429,9 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
   // entry moves an eigenvector by at most 2^-20 t_max / gap, and the Ritz
   // pairs are only used where the gap is a sizeable fraction of t_max. Pairs
   // of two small eigenvalues therefore stop rotating as soon as their
-  // coupling is small against t_max. The sweeps stop after one whose largest
-  // rotated entry is below 2^-10 t_max (the next sweep's would be of about
-  // its square). Stopping at 2^-7 saved a sweep in half the tiles but not its
+  // coupling is small against t_max. The sweeps stop after one that rotated
+  // no entry above 2^-10 t_max (the next sweep's would be of about its
+  // square). Stopping at 2^-7 saved a sweep in half the tiles but not its
   // time, and cost fp32 fits their accuracy.
   // Then Wo = W in descending order of eigenvalue, th = those eigenvalues.
   auto jacobi = [&]() {
@@ -440,23 +440,25 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
 #pragma unroll
     for (int i = 0; i < kBlk; ++i) tmax = fmaxf(tmax, fabsf(L.Ms[0][i][i]));
     const float floor_abs = kJacobiAbs * tmax;
-    const float inv_tmax = tmax > 0.f ? 1.0f / tmax : 0.f;
-    // rotation of the pair (p, q = p ^ t), p < q, from entries app, aqq, apq
+    const float stop_abs = kJacobiStop * tmax;
+    // rotation of the pair (p, q = p ^ t), p < q, from entries app, aqq, apq:
+    // tan(phi) = sign(d) e / (|d| + sqrt(d^2 + e^2)), d = aqq - app, e = 2 apq
+    // (|tan| <= 1), c = cos(phi), s = sin(phi)
     auto publish = [&](int buf, int p, int q, float app, float aqq, float apq, int sb) {
       float c = 1.f, sn = 0.f;
       if (fabsf(apq) > floor_abs) {
-        const float theta = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
-        const float tt = (theta >= 0.f ? 1.f : -1.f) *
-                         __builtin_amdgcn_rcpf(fabsf(theta) + __builtin_amdgcn_sqrtf(theta * theta + 1.f));
-        c = __builtin_amdgcn_rsqf(tt * tt + 1.f);
+        const float d = aqq - app, e = 2.f * apq;
+        const float rt = __builtin_amdgcn_sqrtf(fmaf(d, d, e * e));
+        const float tt = (d >= 0.f ? e : -e) * __builtin_amdgcn_rcpf(fabsf(d) + rt);
+        c = __builtin_amdgcn_rsqf(fmaf(tt, tt, 1.f));
         sn = tt * c;
-        atomicMax(&L.swmax[sb], __float_as_uint(fminf(fabsf(apq) * inv_tmax, 1e30f)));
+        if (fabsf(apq) > stop_abs) L.swbig[sb] = 1u;  // every writer stores the same word
       }
-      L.jc[buf][p] = c; L.jo[buf][p] = -sn;
-      L.jc[buf][q] = c; L.jo[buf][q] = sn;
+      L.jr[buf][p] = make_float2(c, -sn);
+      L.jr[buf][q] = make_float2(c, sn);
     };
     L.Wm[0][jx][jy] = jx == jy ? 1.f : 0.f;
-    if (tid < 2) L.swmax[tid] = 0u;
+    if (tid < 2) L.swbig[tid] = 0u;
     __syncthreads();
     if ((jy == (jx ^ 1)) && jx < jy) publish(0, jx, jy, L.Ms[0][jx][jx], L.Ms[0][jy][jy], L.Ms[0][jx][jy], 0);
     __syncthreads();
@@ -466,15 +468,15 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
 #pragma unroll
       for (int t = 1; t < kBlk; ++t) {
         const float (*A)[kBlk + 1] = L.Ms[cur];
-        const float* jcc = L.jc[cb];
-        const float* joc = L.jo[cb];
+        const float2* jrc = L.jr[cb];
         auto rotated = [&](int x, int y) {
           const int px = x ^ t, py = y ^ t;
-          const float sx = jcc[x], ox = joc[x], sy = jcc[y], oy = joc[y];
-          return sx * (sy * A[x][y] + oy * A[x][py]) + ox * (sy * A[px][y] + oy * A[px][py]);
+          const float2 rx = jrc[x], ry = jrc[y];
+          return rx.x * (ry.x * A[x][y] + ry.y * A[x][py]) + rx.y * (ry.x * A[px][y] + ry.y * A[px][py]);
         };
         const float v = rotated(jx, jy);
-        const float w = jcc[jy] * L.Wm[cur][jx][jy] + joc[jy] * L.Wm[cur][jx][jy ^ t];
+        const float2 ry = jrc[jy];
+        const float w = ry.x * L.Wm[cur][jx][jy] + ry.y * L.Wm[cur][jx][jy ^ t];
         // the next round's pair of this thread's entry, when it is that pair's off-diagonal
         const int tn = t == kBlk - 1 ? 1 : t + 1;
         const int sbn = t == kBlk - 1 ? sb ^ 1 : sb;
@@ -485,13 +487,13 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
         // the next sweep's maximum starts at 0: cleared in round 2, after every
         // thread has read this slot for the previous sweep's stop test, and
         // before round 15 publishes into it
-        if (t == 2 && tid == 0) L.swmax[sb ^ 1] = 0u;
+        if (t == 2 && tid == 0) L.swbig[sb ^ 1] = 0u;
         __syncthreads();
         cur ^= 1;
         cb ^= 1;
       }
       // uniform: every thread reads the same word after the barrier
-      if (__uint_as_float(L.swmax[sb]) < kJacobiStop) break;
+      if (L.swbig[sb] == 0u) break;
     }
     // descending order of the eigenvalues, ties by index
     if (tid < kBlk) {
