@@ -39,13 +39,17 @@ def _check_state(cache, model):
     assert cache.stats() == model.stats
 
 
-def _run_cached_steps(wl, steps, capacity, rho, seed, check_units, log=print):
+def _run_cached_steps(wl, steps, capacity, rho, seed, check_units, log=print, share_prefix=0):
     """Decode steps 0..steps-1 at lengths lens_end - (steps - 1) + t through
     the cache (pages that complete get their summaries before the next step);
     after each: bitwise equality with the uncached step on device pools, the
-    policy model, and check_units(t, wl_t, g_t, pool, sel, out)."""
+    policy model, and check_units(t, wl_t, g_t, pool, sel, out).
+    share_prefix > 0: sequence 1's first share_prefix pages use sequence 0's
+    blocks (a shared prompt), so page slots of one step name the same tiles."""
     cfg = _cfg(wl)
     g = synth.generate(wl, seed, gg.DEV)
+    if share_prefix:
+        g["block_table"][1, :share_prefix] = g["block_table"][0, :share_prefix]
     lens_end = [int(x) for x in wl.seq_lens]
     lens0 = [x - (steps - 1) for x in lens_end]
     P, NB, Hkv = wl.page_size, wl.num_blocks, wl.num_kv_heads
@@ -132,6 +136,33 @@ def test_cached_step_against_oracle(wl, capacity_mult, rho):
     assert s["misses"] > 0 and s["refreshes"] > 0
     if capacity_mult > 1.0:
         assert s["hits"] > 0
+
+
+def test_cached_step_shared_prefix():
+    """Two sequences share their first 12 pages' blocks (a common prompt):
+    the sink page and any shared page both select name one tile, which takes
+    one slot (the later page slot is served as shared); every unit against the
+    oracle, bits against the uncached step, state against the policy model."""
+    wl = GROW
+    cfg = _cfg(wl)
+    n = wl.batch * wl.num_kv_heads * wl.budget_pages
+
+    def check_units(t, wl_t, g_t, pool, sel_c, out_c):
+        data_c = {"q": g_t["q"].cpu(), "block_table": g_t["block_table"].cpu()}
+        hs = gg.gpu_scores(wl, cfg, g_t, pool).cpu()
+        mu_c, vt_c, cf_c = L.split_records(cfg, pool.cpu())
+        bt = data_c["block_table"]
+
+        def unit_summaries(b, h, Jc):
+            idx = bt[b, :Jc].long()
+            return gg.f64(mu_c[idx, h]), gg.f64(vt_c[idx, h]), gg.f64(cf_c[idx, h])
+
+        gg.check_all_units(wl_t, data_c, hs, sel_c, unit_summaries)
+        gg.check_all_outputs(wl_t, dict(g_t, q=data_c["q"]), out_c, sel_c)
+
+    cache, model = _run_cached_steps(wl, 10, n + n // 2, 0.8, seed=4, check_units=check_units, share_prefix=12)
+    s = cache.stats()
+    assert s["shared"] > 0 and s["failed"] == 0
 
 
 def test_cached_step_128k_batch8():
