@@ -695,10 +695,12 @@ def summarize_profiles(wl, flags, stats_dir, fetch_dir, write_dir):
                 v = float(row["Counter_Value"])
                 name = _clean(row["Kernel_Name"])
                 if "copyBuffer" in name:
-                    copies.append(v)
+                    copies.append((int(row["Dispatch_Id"]), v))
                 elif name.startswith("locks::"):
                     per_kernel.setdefault(name, []).append(v)
-        copies = sorted(copies)[-3:]  # the three calibration copies are the largest
+        # the three calibration copies are the run's last copy dispatches (the
+        # copy-bandwidth measurement before them moves larger buffers)
+        copies = [v for _, v in sorted(copies)[-3:]]
         return {n: sum(v) / len(v) for n, v in per_kernel.items()}, sum(copies) / len(copies), \
             {n: len(v) for n, v in per_kernel.items()}
 
