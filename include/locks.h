@@ -106,9 +106,10 @@ int locks_version(void);
  * its per-token coefficients C_j. */
 size_t locks_summary_record_bytes(const locks_config_t* cfg);
 
-/* Workspace bytes needed by locks_score_select, locks_sparse_decode and
- * locks_decode_step for a batch of `batch` sequences of at most `max_pages`
- * pages (one buffer of this size serves all three, in any interleaving).
+/* Workspace bytes needed by locks_score_select, locks_sparse_decode,
+ * locks_decode_step and locks_decode_step_cached for a batch of `batch`
+ * sequences of at most `max_pages` pages (one buffer of this size serves all
+ * four, in any interleaving).
  * Writes *bytes; returns a status.
  * The workspace must be zero-filled once before its first use: its first
  * bytes hold control words (per-(sequence, KV head) arrival counters) that
