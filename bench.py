@@ -273,7 +273,10 @@ def main():
     summary_bytes, kv_bytes = algorithmic_bytes(wl, rec_bytes)
     step_bytes = summary_bytes + kv_bytes
     step_gbs = step_bytes / (step_ms * 1e-3) / 1e9
-    gram_flops = 2.0 * P * d * d * n_full * Hkv
+    # the dual Gram M = D D^T of each (page, KV head) tile on the matrix cores:
+    # three bf16 products (hi.hi, hi.lo, lo.hi of the centred keys) of 2 P^2 d
+    # flops each for bf16 keys, one fp32 product for fp32 keys
+    gram_flops = (3.0 if wl.kv_dtype == "bf16" else 1.0) * 2.0 * P * P * d * n_full * Hkv
     build_tflops = gram_flops / (prefill_build_ms * 1e-3) / 1e12
     copy = copy_bandwidth(dev)
 
