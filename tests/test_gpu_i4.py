@@ -229,6 +229,59 @@ def test_i4_decode_step_end_to_end():
     assert same >= units - 1
 
 
+def test_i4_gpu_build_end_to_end():
+    """GPU build (fit and quantization) -> GPU score -> GPU select -> GPU
+    decode against oracle fit -> oracle quantization -> oracle score ->
+    oracle select -> oracle attend, every unit. The two chains quantize two
+    valid fits independently, so a page's two scores may differ by as much as
+    their reconstructed keys do: the page LSE is 1-Lipschitz in the max norm,
+    so |s_gpu - s_oracle| <= max_i |q . (k_gpu,i - k_oracle,i)| * scale (keys
+    rebuilt from each chain's stored codes and scales) plus the score bar;
+    selections agree except for pages within twice the unit's largest such
+    difference of the (k-2)-th key; outputs on equal selections within the
+    output bar."""
+    wl = synth.Workload("e2e_i4_gpu_build", 3, 2, 4, 128, 64, (64 * 40 + 37, 64 * 24, 64 * 9 + 1), 8, 8,
+                        "bf16", "i4", n_needles=3, extra_blocks=3)
+    cfg = L.config_for(wl)
+    data, g = gg.make_inputs(wl, seed=9)
+    pool = gg.gpu_build(wl, cfg, g)
+    hs = gg.gpu_scores(wl, cfg, g, pool)
+    sel, out, _ = gg.gpu_decode_step(wl, cfg, g, pool)
+    torch.cuda.synchronize()
+    hs, sel, out = hs.cpu(), sel.cpu(), gg.f64(out.cpu())
+    rec_g = gg.unpack_i4(pool.cpu().numpy(), wl.head_dim, wl.rank, wl.page_size)
+    qs_o = _oracle_i4_codes(wl, data)
+    bt = data["block_table"]
+    G, scale = wl.group, wl.softmax_scale
+    same = units = 0
+    worst = 0.0
+    for b in range(wl.batch):
+        _, J, Jc = gg.lens(wl, b)
+        for h in range(wl.num_kv_heads):
+            units += 1
+            s_o, tol = None, gg.SCORE_TOL
+            if Jc > 0:
+                mu_g, vt_g, cf_g = gg.i4_unit_summaries(wl, rec_g, bt, b, h, Jc)
+                mu_o, vt_o, cf_o = gg.i4_unit_summaries(wl, qs_o, bt, b, h, Jc)
+                q = gg.f64(data["q"][b, h * G:(h + 1) * G])
+                dk = (mu_g - mu_o)[:, None, :] + cf_g @ vt_g - cf_o @ vt_o  # [Jc][P][d]
+                dz = np.abs(np.einsum("gd,jpd->gjp", q, dk)).max(axis=2) * scale  # [G][Jc]
+                s_o = gg.oracle_unit_scores(wl, data, b, h, mu_o, vt_o, cf_o)
+                s_g = gg.f64(hs[b, h * G:(h + 1) * G, :Jc])
+                bar = dz + gg.SCORE_TOL * np.maximum(1.0, np.abs(s_o))
+                assert np.all(np.abs(s_g - s_o) <= bar), f"unit {(b, h)}: scores beyond the quantization bound"
+                worst = max(worst, float(dz.max()))
+                tol = gg.SCORE_TOL + 2.0 * float(dz.max())
+            sel_o, sigma_o = gg.oracle_unit_select(wl, b, s_o if J > wl.budget_pages else None)
+            if gg.check_selection(wl, b, sel[b, h].tolist(), sel_o.tolist(), sigma_o, tol=tol) == 0:
+                same += 1
+                o_ref, _ = gg.oracle_unit_attend(wl, data, b, h, sel_o)
+                sl = slice(h * G, (h + 1) * G)
+                assert np.max(np.abs(out[b, sl] - o_ref)) <= gg.out_tol(wl)
+    print(f"[i4 e2e] largest score bound {worst:.4g}; {same}/{units} selections equal")
+    assert same >= units - 1
+
+
 # --------------------------------------------------------------------------
 # full-size shapes: every unit scored and selected on the GPU, sampled units
 # against the oracle; the full-size i4 build sampled for validity
