@@ -20,6 +20,11 @@
 // A capacity of at least batch * Hkv * k slots guarantees a slot for every
 // missing tile: at most that many slots are used in one step.
 //
+// Page slots of one step that name the same tile (blocks shared between
+// sequences) are served by one slot. When such a tile is resident and was
+// copied while incomplete, each of them may see the incomplete mark and
+// list the copy (the same bytes twice) and count a refresh.
+//
 // The admission runs in one workgroup of 1024 threads (a step selects a few
 // thousand tiles); the state its threads share lives in global memory,
 // accessed with workgroup-scope atomics, so that each phase sees the previous
