@@ -48,6 +48,8 @@
 //     coefficient row) scale = bf16(max|x| / L), L = 127 for the 8-bit centroid
 //     and coefficients and 7 for the 4-bit basis, and code =
 //     round-half-even(x / scale), all in fp32 (correctly rounded division).
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -75,6 +77,125 @@ __device__ __forceinline__ float hash_unit(uint32_t a, uint32_t b, uint32_t salt
 
 __device__ __forceinline__ float rdl(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// v of lane `src` of the wave
+__device__ __forceinline__ float lane_at(int src, float v) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
+// v of lane (lane ^ X), X known at compile time: DPP where a quad or row
+// permutation expresses it (quad_perm [1,0,3,2], [2,3,0,1], [3,2,1,0],
+// row_half_mirror, row_ror:8, row_mirror), the LDS swizzle inside 32 lanes,
+// a permute beyond
+template <int X>
+__device__ __forceinline__ float lane_xor(float v) {
+  static_assert(X > 0 && X < 64, "lane xor");
+  const int iv = __float_as_int(v);
+  int r;
+  if constexpr (X == 1) r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);
+  else if constexpr (X == 2) r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);
+  else if constexpr (X == 3) r = __builtin_amdgcn_mov_dpp(iv, 0x1B, 0xF, 0xF, true);
+  else if constexpr (X == 7) r = __builtin_amdgcn_mov_dpp(iv, 0x141, 0xF, 0xF, true);
+  else if constexpr (X == 8) r = __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true);
+  else if constexpr (X == 15) r = __builtin_amdgcn_mov_dpp(iv, 0x140, 0xF, 0xF, true);
+  else if constexpr (X < 32) r = __builtin_amdgcn_ds_swizzle(iv, (X << 10) | 0x1F);  // and 31, xor X
+  else r = __builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 63) ^ X) << 2), iv);
+  return __int_as_float(r);
+}
+
+// v of lane N of the lane's row of 16 (DPP row_newbcast)
+template <int N>
+__device__ __forceinline__ float row_lane(float v) {
+  static_assert(N >= 0 && N < 16, "row lane");
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + N, 0xF, 0xF, true));
+}
+
+// a[k] for a per-lane k in 0..3, as a two-level select on the bits of k
+// (an indexed form is compiled to a store and load through LDS)
+__device__ __forceinline__ float pick4(const float (&a)[4], int k) {
+  const float l = (k & 1) ? a[1] : a[0];
+  const float u = (k & 1) ? a[3] : a[2];
+  return (k & 2) ? u : l;
+}
+
+// One round of parallel cyclic Jacobi on a 16 x 16 symmetric T held by one
+// wave: lane (g, j) = (lane >> 4, lane & 15) owns column n = j ^ 4 g (every
+// row of 16 lanes holds all columns, the column that equals one of the lane
+// row's own rows 4 g + i sitting at position i) and holds t4[i] = T[4 g + i][n],
+// w4[i] = W[4 g + i][n] and dg = T[n][n]. Round t rotates the 8 disjoint
+// pairs {p, p ^ t}: T <- J^T T J, W <- W J, with J[p][p] = J[q][q] = c,
+// J[p][q] = s, J[q][p] = -s for p < q. Every lane forms the rotation of its
+// own column's pair {lo, hi} from the diagonal entries (its own and lane
+// lane ^ t's, which owns column n ^ t) and T[hi][lo] read from column lo, so
+// the two columns of a pair form the same rotation. The entries the two-sided
+// update combines, T[x][q], T[x ^ t][n] and T[x ^ t][q] for q = n ^ t, sit in
+// lanes lane ^ t, lane ^ 16 (t >> 2) ^ (t & 12) and lane ^ 16 (t >> 2) ^ (t & 3)
+// and are requested at the start, as none depends on this round's rotation;
+// the rotation (c, J[x ^ t][x]) of row x = 4 g + i is broadcast from position
+// i of the lane's row. A pair rotates only while |T[hi][lo]| exceeds
+// floor_abs; the tangent is sign(d) e / (|d| + sqrt(d^2 + e^2)),
+// d = T[hi][hi] - T[lo][lo], e = 2 T[hi][lo] (|tan| <= 1), and the diagonal
+// moves by -/+ tan T[hi][lo] (the annihilated entry's exact effect on the
+// pair's diagonal); `big` records an entry above stop_abs.
+template <int t>
+__device__ __forceinline__ void jacobi_round(float (&t4)[4], float (&w4)[4], float& dg, float floor_abs,
+                                             float stop_abs, bool& big) {
+  constexpr int hb = t >= 8 ? 8 : (t >= 4 ? 4 : (t >= 2 ? 2 : 1));  // p < p ^ t iff (p & hb) == 0
+  constexpr int gx = 16 * (t >> 2);  // lane offset of the row partners' row group
+  constexpr int it = t & 3;          // element offset of the row partners
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int n = (lane & 15) ^ (4 * g);
+  const bool first = (n & hb) == 0;  // n is the pair's lo
+  const int lo = first ? n : (n ^ t), hi = lo ^ t;
+  const float oself = pick4(t4, (n & 3) ^ it);                      // T[4 g + ((n ^ t) & 3)][n]
+  const float apq = lane_at(4 * (hi & 12) + (lo ^ (hi & 12)), oself);  // T[hi][lo]: column lo in row group hi >> 2
+  const float dq = lane_xor<t>(dg);                                   // T[n ^ t][n ^ t]
+  float xq[4], xr[4], xrq[4], wq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xq[i] = lane_xor<t>(t4[i]);  // T[4 g + i][n ^ t]
+    wq[i] = lane_xor<t>(w4[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (t < 4) {
+      xr[i] = t4[i ^ it];    // T[(4 g + i) ^ t][n]
+      xrq[i] = xq[i ^ it];   // T[(4 g + i) ^ t][n ^ t]
+    } else {
+      xr[i] = lane_xor<gx ^ (t & 12)>(t4[i ^ it]);
+      xrq[i] = lane_xor<gx ^ it>(t4[i ^ it]);
+    }
+  }
+  // every exchange is issued before the rotation waits for T[hi][lo]
+  __builtin_amdgcn_sched_barrier(0);
+  const float app = first ? dg : dq, aqq = first ? dq : dg;
+  const float d = aqq - app, e = 2.f * apq;
+  const float rt = __builtin_amdgcn_sqrtf(fmaf(d, d, e * e));
+  const float tr = (d >= 0.f ? e : -e) * __builtin_amdgcn_rcpf(fabsf(d) + rt);
+  const float tt = fabsf(apq) > floor_abs ? tr : 0.f;
+  big = big || fabsf(apq) > stop_abs;
+  const float c = __builtin_amdgcn_rsqf(fmaf(tt, tt, 1.f));
+  const float s = tt * c;
+  const float on = first ? -s : s;  // J[n ^ t][n]
+  const float ta = tt * apq;
+  dg = first ? dg - ta : dg + ta;
+  const float cx[4] = {row_lane<0>(c), row_lane<1>(c), row_lane<2>(c), row_lane<3>(c)};
+  const float ox[4] = {row_lane<0>(on), row_lane<1>(on), row_lane<2>(on), row_lane<3>(on)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a0 = c * t4[i] + on * xq[i];   // (T J)[x][n]
+    const float a1 = c * xr[i] + on * xrq[i];  // (T J)[x ^ t][n]
+    t4[i] = cx[i] * a0 + ox[i] * a1;
+    w4[i] = c * w4[i] + on * wq[i];
+  }
+}
+
+template <int... ts>
+__device__ __forceinline__ void jacobi_sweep(std::integer_sequence<int, ts...>, float (&t4)[4], float (&w4)[4],
+                                             float& dg, float floor_abs, float stop_abs, bool& big) {
+  (jacobi_round<ts + 1>(t4, w4, dg, floor_abs, stop_abs, big), ...);
 }
 
 // Centred keys in LDS: row-major [P][D], 16-byte chunks XOR-swizzled by row so
@@ -115,14 +236,10 @@ struct alignas(16) BuildLds {
   float Vb[D][kBlk];       // D^T U, then the orthonormal basis V
   float Gp[4][kBlk][kBlk]; // the waves' partial Gram matrices (and centroid partial sums)
   float RiW[4][kBlk][kBlk];  // each wave's R^-1 of the Cholesky-QR
-  float Ms[2][kBlk][kBlk + 1];  // Rayleigh quotient T, ping-pong
-  float Wm[2][kBlk][kBlk + 1];  // its accumulated rotations, ping-pong
   float Wo[kBlk][kBlk];    // eigenvectors of T, descending eigenvalue order
   float th[kBlk];          // Ritz values, descending
-  float2 jr[2][kBlk];      // rotation of a Jacobi round (this one, the next): (self, other) coefficients
-  uint32_t swbig[2];       // a sweep rotated an entry above kJacobiStop t_max (alternating by sweep)
+  float dg[kBlk];          // diagonal of the diagonalised T
   float res[4][kBlk];      // partial squared residual norms
-  int order[kBlk];
   int flag;
 };
 
@@ -416,101 +533,63 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
     }
   };
 
-  // Parallel cyclic Jacobi on the 16 x 16 T in Ms[0] (all 256 threads,
-  // thread (x, y) owns T[x][y] and W[x][y]): round t rotates the 8 disjoint
-  // pairs {p, p ^ t}, T <- J^T T J and W <- W J in one pass per element into
-  // the other buffer. The 8 threads owning the next round's off-diagonal
-  // entries also form the three entries of their pair that the next rotation
-  // needs and publish it with their own update, so a round costs one barrier.
-  // (Two single-wave forms measured slower: one wave doing all 256
-  // elements in LDS with wave-level waits instead of barriers, 0.85 against
-  // 0.46 us a round at the time; and one wave keeping T and W^T in registers
-  // in the MFMA layout, each round T <- R^T (T R), W^T <- R^T W^T as twelve
-  // v_mfma_f32_16x16x4_f32 with no data movement, 0.42 against 0.38 us.)
-  // A pair is rotated only while its off-diagonal entry exceeds 2^-20 of the
-  // largest diagonal entry t_max (about the largest eigenvalue): a smaller
-  // entry moves an eigenvector by at most 2^-20 t_max / gap, and the Ritz
-  // pairs are only used where the gap is a sizeable fraction of t_max. Pairs
-  // of two small eigenvalues therefore stop rotating as soon as their
-  // coupling is small against t_max. The sweeps stop after one that rotated
-  // no entry above 2^-10 t_max (the next sweep's would be of about its
-  // square). Stopping at 2^-7 saved a sweep in half the tiles but not its
-  // time, and cost fp32 fits their accuracy.
-  // Then Wo = W in descending order of eigenvalue, th = those eigenvalues.
+  // Rayleigh quotient T = (G + G^T) / 2 of the summed partials G in Gp,
+  // diagonalised by parallel cyclic Jacobi in one wave's registers (wave 0;
+  // jacobi_round): about 465 shader cycles a round (0.2 us). Measured slower:
+  // 256 threads each owning one entry of T and W in LDS with a barrier per
+  // round (0.38 us a round); one wave keeping T and W^T in the matrix-core
+  // layout, each round as twelve v_mfma_f32_16x16x4_f32 (0.42 us); this wave
+  // layout with the diagonal gathered every round and the rows' rotations
+  // recomputed from gathered tangents (0.38 us), then with the diagonal kept
+  // per lane and the rotations read by permute (0.28 us), then fetched by row
+  // broadcast (0.24 us) before the exchanges were issued ahead of the wait
+  // for T[hi][lo]. A pair is rotated only while its
+  // off-diagonal entry exceeds 2^-20 of the largest diagonal entry t_max
+  // (about the largest eigenvalue): a smaller entry moves an eigenvector by
+  // at most 2^-20 t_max / gap, and the Ritz pairs are only used where the
+  // gap is a sizeable fraction of t_max. Pairs of two small eigenvalues
+  // therefore stop rotating as soon as their coupling is small against
+  // t_max. The sweeps stop after one that rotated no entry above 2^-10 t_max
+  // (the next sweep's would be of about its square). Stopping at 2^-7 saved
+  // a sweep in half the tiles but not its time, and cost fp32 fits their
+  // accuracy. Then Wo = W in descending order of eigenvalue, th = those
+  // eigenvalues (ties by index).
   auto jacobi = [&]() {
-    const int jx = tid >> 4, jy = tid & 15;
-    float tmax = 0.f;
+    if (wave != 0) return;
+    const int cn = ln ^ (4 * lg);  // this lane's column
+    float t4[4], w4[4];
 #pragma unroll
-    for (int i = 0; i < kBlk; ++i) tmax = fmaxf(tmax, fabsf(L.Ms[0][i][i]));
+    for (int i = 0; i < 4; ++i) {
+      const int x = 4 * lg + i;
+      const float v = (L.Gp[0][x][cn] + L.Gp[1][x][cn]) + (L.Gp[2][x][cn] + L.Gp[3][x][cn]);
+      const float vt = (L.Gp[0][cn][x] + L.Gp[1][cn][x]) + (L.Gp[2][cn][x] + L.Gp[3][cn][x]);
+      t4[i] = 0.5f * (v + vt);
+      w4[i] = x == cn ? 1.f : 0.f;
+    }
+    // T[cn][cn] from the lane whose row group holds row cn and whose column is cn
+    float dg = lane_at(16 * (cn >> 2) + (cn & 3), pick4(t4, cn & 3));
+    float tmax = fabsf(dg);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 64));
     const float floor_abs = kJacobiAbs * tmax;
     const float stop_abs = kJacobiStop * tmax;
-    // rotation of the pair (p, q = p ^ t), p < q, from entries app, aqq, apq:
-    // tan(phi) = sign(d) e / (|d| + sqrt(d^2 + e^2)), d = aqq - app, e = 2 apq
-    // (|tan| <= 1), c = cos(phi), s = sin(phi)
-    auto publish = [&](int buf, int p, int q, float app, float aqq, float apq, int sb) {
-      float c = 1.f, sn = 0.f;
-      if (fabsf(apq) > floor_abs) {
-        const float d = aqq - app, e = 2.f * apq;
-        const float rt = __builtin_amdgcn_sqrtf(fmaf(d, d, e * e));
-        const float tt = (d >= 0.f ? e : -e) * __builtin_amdgcn_rcpf(fabsf(d) + rt);
-        c = __builtin_amdgcn_rsqf(fmaf(tt, tt, 1.f));
-        sn = tt * c;
-        if (fabsf(apq) > stop_abs) L.swbig[sb] = 1u;  // every writer stores the same word
-      }
-      L.jr[buf][p] = make_float2(c, -sn);
-      L.jr[buf][q] = make_float2(c, sn);
-    };
-    L.Wm[0][jx][jy] = jx == jy ? 1.f : 0.f;
-    if (tid < 2) L.swbig[tid] = 0u;
-    __syncthreads();
-    if ((jy == (jx ^ 1)) && jx < jy) publish(0, jx, jy, L.Ms[0][jx][jx], L.Ms[0][jy][jy], L.Ms[0][jx][jy], 0);
-    __syncthreads();
-    int cur = 0, cb = 0;
     for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-      const int sb = sweep & 1;
+      bool big = false;
+      jacobi_sweep(std::make_integer_sequence<int, kBlk - 1>{}, t4, w4, dg, floor_abs, stop_abs, big);
+      if (__ballot(big) == 0) break;  // uniform
+    }
+    const float dv = dg;
+    if (lane < kBlk) L.dg[cn] = dv;
+    wave_lds_sync();
+    int rank = 0;
 #pragma unroll
-      for (int t = 1; t < kBlk; ++t) {
-        const float (*A)[kBlk + 1] = L.Ms[cur];
-        const float2* jrc = L.jr[cb];
-        auto rotated = [&](int x, int y) {
-          const int px = x ^ t, py = y ^ t;
-          const float2 rx = jrc[x], ry = jrc[y];
-          return rx.x * (ry.x * A[x][y] + ry.y * A[x][py]) + rx.y * (ry.x * A[px][y] + ry.y * A[px][py]);
-        };
-        const float v = rotated(jx, jy);
-        const float2 ry = jrc[jy];
-        const float w = ry.x * L.Wm[cur][jx][jy] + ry.y * L.Wm[cur][jx][jy ^ t];
-        // the next round's pair of this thread's entry, when it is that pair's off-diagonal
-        const int tn = t == kBlk - 1 ? 1 : t + 1;
-        const int sbn = t == kBlk - 1 ? sb ^ 1 : sb;
-        if ((jy == (jx ^ tn)) && jx < jy)
-          publish(cb ^ 1, jx, jy, rotated(jx, jx), rotated(jy, jy), v, sbn);
-        L.Ms[cur ^ 1][jx][jy] = v;
-        L.Wm[cur ^ 1][jx][jy] = w;
-        // the next sweep's maximum starts at 0: cleared in round 2, after every
-        // thread has read this slot for the previous sweep's stop test, and
-        // before round 15 publishes into it
-        if (t == 2 && tid == 0) L.swbig[sb ^ 1] = 0u;
-        __syncthreads();
-        cur ^= 1;
-        cb ^= 1;
-      }
-      // uniform: every thread reads the same word after the barrier
-      if (L.swbig[sb] == 0u) break;
+    for (int j = 0; j < kBlk; ++j) {
+      const float u = L.dg[j];
+      rank += (u > dv || (u == dv && j < cn)) ? 1 : 0;
     }
-    // descending order of the eigenvalues, ties by index
-    if (tid < kBlk) {
-      const float v = L.Ms[cur][tid][tid];
-      int rank = 0;
-      for (int j = 0; j < kBlk; ++j) {
-        const float u = L.Ms[cur][j][j];
-        rank += (u > v || (u == v && j < tid)) ? 1 : 0;
-      }
-      L.order[rank] = tid;
-      L.th[rank] = v;
-    }
-    __syncthreads();
-    L.Wo[jx][jy] = L.Wm[cur][jx][L.order[jy]];
+    if (lane < kBlk) L.th[rank] = dv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L.Wo[4 * lg + i][rank] = w4[i];
   };
 
   // ---- 3. top-r eigenvectors of M into X ----
@@ -552,13 +631,6 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) L.Gp[wave][4 * lg + i][ln] = m[i];
-    }
-    __syncthreads();
-    {
-      const int i = tid >> 4, j = tid & 15;
-      const float v = (L.Gp[0][i][j] + L.Gp[1][i][j]) + (L.Gp[2][i][j] + L.Gp[3][i][j]);
-      const float vt = (L.Gp[0][j][i] + L.Gp[1][j][i]) + (L.Gp[2][j][i] + L.Gp[3][j][i]);
-      L.Ms[0][i][j] = 0.5f * (v + vt);
     }
     __syncthreads();
     jacobi();
