@@ -111,6 +111,37 @@ __device__ __forceinline__ float row_lane(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + N, 0xF, 0xF, true));
 }
 
+// row_lane<n> for an n that is a constant once loops are unrolled
+__device__ __forceinline__ float row_lane_at(float v, int n) {
+  switch (n) {
+    case 0: return row_lane<0>(v);
+    case 1: return row_lane<1>(v);
+    case 2: return row_lane<2>(v);
+    case 3: return row_lane<3>(v);
+    case 4: return row_lane<4>(v);
+    case 5: return row_lane<5>(v);
+    case 6: return row_lane<6>(v);
+    case 7: return row_lane<7>(v);
+    case 8: return row_lane<8>(v);
+    case 9: return row_lane<9>(v);
+    case 10: return row_lane<10>(v);
+    case 11: return row_lane<11>(v);
+    case 12: return row_lane<12>(v);
+    case 13: return row_lane<13>(v);
+    case 14: return row_lane<14>(v);
+    default: return row_lane<15>(v);
+  }
+}
+
+template <int... Ns>
+__device__ __forceinline__ void bcast_row16_impl(float v, float (&out)[16], std::integer_sequence<int, Ns...>) {
+  ((out[Ns] = row_lane<Ns>(v)), ...);
+}
+// out[N] = v of lane N of the lane's row of 16, N = 0..15
+__device__ __forceinline__ void bcast_row16(float v, float (&out)[16]) {
+  bcast_row16_impl(v, out, std::make_integer_sequence<int, 16>{});
+}
+
 // a[k] for a per-lane k in 0..3, as a two-level select on the bits of k
 // (an indexed form is compiled to a store and load through LDS)
 __device__ __forceinline__ float pick4(const float (&a)[4], int k) {
@@ -246,7 +277,7 @@ struct alignas(16) BuildLds {
 }  // namespace
 
 template <typename T, int D, int P, bool I4>
-__global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void build_kernel(BuildArgs a) {
   constexpr int NB = P / 16;  // 16-row blocks of M (and of X, Y, C)
   constexpr int DB = D / 16;  // 16-row blocks of V
   static_assert(P == 16 || P == 32 || P == 64, "page size");
@@ -360,71 +391,66 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
   }
 
   // ---- helpers ----
-  // Every wave, in registers (lane l holds row l & 15 of the block Gram M in
-  // am[]): column scaling S (columns with a vanishing norm are dead), Cholesky
-  // S M S = L L^T (right-looking; a column whose pivot vanishes is dead and
-  // gets L = unit column), then L^-1 column by column and Ri = S L^-T with dead
-  // columns zeroed, written to this wave's RiW. Returns the dead-column mask
-  // (uniform).
-  auto chol_rinv = [&](float* am) -> uint32_t {
-    const int row = ln;
-    float sd[kBlk];
-    float dmax = 0.f;
+  // Every wave, in registers, lane l taking column c = l & 15 of the block
+  // Gram G (am[r] = G[r][c], gd = G[c][c]; every row of 16 lanes holds the
+  // whole matrix, and entries of other columns come by row broadcast):
+  // column scaling S (columns with a vanishing norm are dead), Cholesky
+  // S G S = L L^T (right-looking: step j broadcasts column j, and lane c
+  // keeps row c of L in lrow[]; a column whose pivot is 1e-12 or less is dead
+  // and gets a zero column of L and a zero reciprocal pivot, so it neither
+  // updates the others nor survives the inverse), then column c of L^-1 by
+  // forward substitution and row c of Ri = S L^-T to this wave's RiW (dead
+  // columns zero). Returns the dead-column mask (uniform).
+  auto chol_rinv = [&](float* am, float gd) -> uint32_t {
+    const int col = ln;
+    float dmax = gd;
 #pragma unroll
-    for (int j = 0; j < kBlk; ++j) {
-      sd[j] = rdl(am[j], j);  // diagonal
-      dmax = fmaxf(dmax, sd[j]);
-    }
-    uint32_t dead = 0u;
+    for (int o = 1; o < kBlk; o <<= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, o, 64));
+    const bool live = gd > 1e-30f * fmaxf(dmax, 1e-30f);
+    const float sc = live ? __builtin_amdgcn_rsqf(gd) : 0.f;
+    float sr[kBlk];
+    bcast_row16(sc, sr);
 #pragma unroll
-    for (int j = 0; j < kBlk; ++j) {
-      const bool dd = !(sd[j] > 1e-30f * fmaxf(dmax, 1e-30f));
-      dead |= dd ? 1u << j : 0u;
-      sd[j] = dd ? 0.f : __builtin_amdgcn_rsqf(sd[j]);
-    }
-    float srow = 0.f;
-#pragma unroll
-    for (int j = 0; j < kBlk; ++j) srow = row == j ? sd[j] : srow;
-#pragma unroll
-    for (int c = 0; c < kBlk; ++c) am[c] *= srow * sd[c];
+    for (int r = 0; r < kBlk; ++r) am[r] *= sr[r] * sc;
     // the chain of pivots uses the hardware reciprocal square root (about
     // 1 ulp): the factor only has to orthonormalise the block to fp32 level
-    float invd[kBlk];  // 1 / L[j][j]
+    uint32_t dead = 0u;
+    float invd[kBlk];  // 1 / L[j][j], 0 for a dead column
+    float lrow[kBlk];  // L[c][j] for j <= c
 #pragma unroll
     for (int j = 0; j < kBlk; ++j) {
-      const float vjj = rdl(am[j], j);
-      const bool ok = vjj > 1e-12f && !((dead >> j) & 1u);  // uniform
-      const float rj = ok ? __builtin_amdgcn_rsqf(vjj) : 1.0f;
-      invd[j] = rj;
-      // L[row][j]: below the pivot am * rj, on it sqrt(v) (1 for a dead
-      // column), above it 0; per-lane selects, no branch
-      const float below = ok ? am[j] * rj : 0.f;
-      const float diag = ok ? vjj * rj : 1.0f;
-      const float lij = row > j ? below : (row == j ? diag : 0.f);
-      am[j] = lij;
+      const float vjj = row_lane_at(am[j], j);  // (S G S - ...)[j][j], from lane j
+      const bool ok = vjj > 1e-12f;                // the same in every lane; a dead row's entries are 0
+      invd[j] = ok ? __builtin_amdgcn_rsqf(vjj) : 0.f;
       dead |= ok ? 0u : 1u << j;
-      // the column's entries as scalars first, then the updates
-      float lk[kBlk];
+      lrow[j] = am[j] * invd[j];
+      const float f = -lrow[j] * invd[j];  // -L[c][j] / L[j][j]
+      // am[r] -= L[r][j] L[c][j] = column j's entry r times f
 #pragma unroll
-      for (int k = j + 1; k < kBlk; ++k) lk[k] = rdl(lij, k);
-#pragma unroll
-      for (int k = j + 1; k < kBlk; ++k) am[k] = fmaf(-lij, lk[k], am[k]);
+      for (int r = j + 1; r < kBlk; ++r) am[r] = fmaf(row_lane_at(am[r], j), f, am[r]);
     }
-    // li[i] = (L^-1)[i][row]
-    float li[kBlk];
+    // z = L^-1 e_c, column by column (L[i][k] is lane i's lrow[k]); the
+    // scheduling barriers keep the broadcasts of a step from being hoisted
+    // (all of them live at once would halve the waves a SIMD can hold)
+    __builtin_amdgcn_sched_barrier(0);
+    float z[kBlk];
 #pragma unroll
-    for (int i = 0; i < kBlk; ++i) {
-      float t = row == i ? 1.f : 0.f;
+    for (int i = 0; i < kBlk; ++i) z[i] = i == col ? 1.f : 0.f;
 #pragma unroll
-      for (int k = 0; k < i; ++k) t = fmaf(-rdl(am[k], i), li[k], t);
-      li[i] = t * invd[i];
+    for (int k = 0; k < kBlk; ++k) {
+      z[k] *= invd[k];
+      const float nz = -z[k];
+#pragma unroll
+      for (int i = k + 1; i < kBlk; ++i) z[i] = fmaf(row_lane_at(lrow[k], i), nz, z[i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // Ri[row][j] = s_row * (L^-1)[j][row] for j >= row, live j
+    // Ri[c][b] = s_c (L^-1)[b][c]
     if (lane < kBlk) {
 #pragma unroll
-      for (int j = 0; j < kBlk; ++j) L.RiW[wave][row][j] = (j >= row && !((dead >> j) & 1u)) ? srow * li[j] : 0.f;
+      for (int c = 0; c < kBlk; c += 4)
+        *reinterpret_cast<f32x4_t*>(&L.RiW[wave][col][c]) = f32x4_t{sc * z[c], sc * z[c + 1], sc * z[c + 2], sc * z[c + 3]};
     }
-    return dead;
+    return __builtin_amdgcn_readfirstlane(dead);
   };
 
   // Cholesky-QR of the NR x 16 rows in `buf` (LDS, row-major), in place: wave
@@ -454,7 +480,8 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
       }
       am[c] = v[0]; am[c + 1] = v[1]; am[c + 2] = v[2]; am[c + 3] = v[3];
     }
-    const uint32_t dead = chol_rinv(am);
+    const float gd = ((L.Gp[0][ln][ln] + L.Gp[1][ln][ln]) + L.Gp[2][ln][ln]) + L.Gp[3][ln][ln];
+    const uint32_t dead = chol_rinv(am, gd);
     wave_lds_sync();  // RiW[wave] visible to the wave
     const bool dcol = (dead >> ln) & 1u;
     for (int t = wave; t < NR / 16; t += 4) {
