@@ -404,8 +404,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   auto chol_rinv = [&](float* am, float gd) -> uint32_t {
     const int col = ln;
     float dmax = gd;
-#pragma unroll
-    for (int o = 1; o < kBlk; o <<= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, o, 64));
+    dmax = fmaxf(dmax, lane_xor<1>(dmax));
+    dmax = fmaxf(dmax, lane_xor<2>(dmax));
+    dmax = fmaxf(dmax, lane_xor<4>(dmax));
+    dmax = fmaxf(dmax, lane_xor<8>(dmax));
     const bool live = gd > 1e-30f * fmaxf(dmax, 1e-30f);
     const float sc = live ? __builtin_amdgcn_rsqf(gd) : 0.f;
     float sr[kBlk];
@@ -429,10 +431,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
       for (int r = j + 1; r < kBlk; ++r) am[r] = fmaf(row_lane_at(am[r], j), f, am[r]);
     }
-    // z = L^-1 e_c, column by column (L[i][k] is lane i's lrow[k]); the
-    // scheduling barriers keep the broadcasts of a step from being hoisted
-    // (all of them live at once would halve the waves a SIMD can hold)
-    __builtin_amdgcn_sched_barrier(0);
+    // z = L^-1 e_c, column by column (L[i][k] is lane i's lrow[k]). Step k
+    // broadcasts lrow[k] + 0 z[k], which cannot be formed before z[k]: the
+    // broadcasts of every step hoisted to the start were live at once and
+    // cost registers the second wave of a SIMD needs.
     float z[kBlk];
 #pragma unroll
     for (int i = 0; i < kBlk; ++i) z[i] = i == col ? 1.f : 0.f;
@@ -440,9 +442,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     for (int k = 0; k < kBlk; ++k) {
       z[k] *= invd[k];
       const float nz = -z[k];
+      const float lk = fmaf(0.f, z[k], lrow[k]);
 #pragma unroll
-      for (int i = k + 1; i < kBlk; ++i) z[i] = fmaf(row_lane_at(lrow[k], i), nz, z[i]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = k + 1; i < kBlk; ++i) z[i] = fmaf(row_lane_at(lk, i), nz, z[i]);
     }
     // Ri[c][b] = s_c (L^-1)[b][c]
     if (lane < kBlk) {
@@ -453,22 +455,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     return __builtin_amdgcn_readfirstlane(dead);
   };
 
-  // Cholesky-QR of the NR x 16 rows in `buf` (LDS, row-major), in place: wave
-  // w takes the 16-row tiles w, w + 4, ...; dead columns become pseudo-random
-  // vectors (call again to orthonormalise those). Two workgroup barriers;
-  // returns the dead-column mask (uniform).
-  auto cholqr = [&](float (*buf)[kBlk], int NR, uint32_t salt) -> uint32_t {
-    f32x4_t m = {0.f, 0.f, 0.f, 0.f};
-    for (int t = wave; t < NR / 16; t += 4) {
+  // Cholesky-QR of the NR x 16 rows in `src` (LDS, row-major) into `dst`
+  // (may be `src`): wave w takes the 16-row tiles w, w + 4, ...; dead columns
+  // become pseudo-random vectors (call again to orthonormalise those). The
+  // Gram partials are formed here unless the product that wrote `src` left
+  // them in Gp (`gram_ready`, after a workgroup barrier). Returns the
+  // dead-column mask (uniform).
+  auto cholqr = [&](const float (*src)[kBlk], float (*dst)[kBlk], int NR, uint32_t salt,
+                    bool gram_ready) -> uint32_t {
+    if (!gram_ready) {
+      f32x4_t m = {0.f, 0.f, 0.f, 0.f};
+      for (int t = wave; t < NR / 16; t += 4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = buf[16 * t + 4 * lg + i][ln];
-        m = __builtin_amdgcn_mfma_f32_16x16x4f32(v, v, m, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const float v = src[16 * t + 4 * lg + i][ln];
+          m = __builtin_amdgcn_mfma_f32_16x16x4f32(v, v, m, 0, 0, 0);
+        }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) L.Gp[wave][4 * lg + i][ln] = m[i];
-    __syncthreads();
+      for (int i = 0; i < 4; ++i) L.Gp[wave][4 * lg + i][ln] = m[i];
+      __syncthreads();
+    }
     float am[kBlk];
 #pragma unroll
     for (int c = 0; c < kBlk; c += 4) {
@@ -488,12 +495,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       f32x4_t x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k0 = 0; k0 < kBlk; k0 += 4)
-        x = __builtin_amdgcn_mfma_f32_16x16x4f32(buf[16 * t + ln][k0 + lg], L.RiW[wave][k0 + lg][ln], x, 0, 0, 0);
-      wave_lds_sync();  // every lane's reads of the tile are done before it is overwritten
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(src[16 * t + ln][k0 + lg], L.RiW[wave][k0 + lg][ln], x, 0, 0, 0);
+      wave_lds_sync();  // every lane's reads of the tile are done before it is overwritten (src == dst)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * t + 4 * lg + i;
-        buf[row][ln] = dcol ? hash_unit((uint32_t)row, (uint32_t)ln, salt) : x[i];
+        dst[row][ln] = dcol ? hash_unit((uint32_t)row, (uint32_t)ln, salt) : x[i];
       }
     }
     __syncthreads();
@@ -547,9 +554,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   };
 
   // Y = M X for this wave's rows (wave < NB): lane (ln, lg) -> Y[16 wave + 4 lg + i][ln]
-  auto product = [&]() {
+  // With `gram`, also this wave's partial Y^T Y of its rows into Gp (the
+  // Gram the Cholesky-QR of Y starts from; waves without rows write zeros).
+  auto product = [&](bool gram) {
+    f32x4_t y = {0.f, 0.f, 0.f, 0.f};
     if (wave < NB) {
-      f32x4_t y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int I = 0; I < NB; ++I)
 #pragma unroll
@@ -557,6 +566,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
           y = __builtin_amdgcn_mfma_f32_16x16x4f32(hreg[I][i], L.X[16 * I + 4 * lg + i][ln], y, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) L.Y[16 * wave + 4 * lg + i][ln] = y[i];
+    }
+    if (gram) {
+      f32x4_t m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = __builtin_amdgcn_mfma_f32_16x16x4f32(y[i], y[i], m, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.Gp[wave][4 * lg + i][ln] = m[i];
     }
   };
 
@@ -596,8 +612,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     // T[cn][cn] from the lane whose row group holds row cn and whose column is cn
     float dg = lane_at(16 * (cn >> 2) + (cn & 3), pick4(t4, cn & 3));
     float tmax = fabsf(dg);
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 64));
+    tmax = fmaxf(tmax, lane_xor<1>(tmax));
+    tmax = fmaxf(tmax, lane_xor<2>(tmax));
+    tmax = fmaxf(tmax, lane_xor<4>(tmax));
+    tmax = fmaxf(tmax, lane_xor<8>(tmax));
     const float floor_abs = kJacobiAbs * tmax;
     const float stop_abs = kJacobiStop * tmax;
     for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
@@ -637,13 +655,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   __syncthreads();
   const int first_rr = NB == 1 ? 1 : kFirstRitzCheck;
   while (true) {
-    product();
+    product(products + 1 < first_rr);
     ++products;
     if (products < first_rr) {
       __syncthreads();
-      for (int e = tid; e < P * kBlk; e += 256) L.X[e / kBlk][e % kBlk] = L.Y[e / kBlk][e % kBlk];
-      __syncthreads();
-      cholqr(L.X, P, 3u + (uint32_t)products);
+      cholqr(L.Y, L.X, P, 3u + (uint32_t)products, true);
       continue;
     }
     // Rayleigh-Ritz: T = X^T Y (waves < NB each its rows), summed and symmetrised by wave 0
@@ -710,9 +726,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
     if (converged || products >= kMaxProducts) break;
     // continue from M U
-    for (int e = tid; e < P * kBlk; e += 256) L.X[e / kBlk][e % kBlk] = L.Y[e / kBlk][e % kBlk];
-    __syncthreads();
-    cholqr(L.X, P, 50u + (uint32_t)products);
+    cholqr(L.Y, L.X, P, 50u + (uint32_t)products, false);
   }
   if (tid == 0 && a.fit_info) a.fit_info[(int64_t)blockIdx.x * a.Hkv + h] = converged ? products : -products;
 
@@ -735,26 +749,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   const float th0 = L.th[0], thr = L.th[r - 1];
   if (th0 > 0.f && thr > 0x1p-16f * th0 && th0 < 3.0e38f) {
     if (ns_orth(L.Vb, D, r) > 0x1p-10f) ns_orth(L.Vb, D, r);
-  } else if (cholqr(L.Vb, D, 101u)) {
-    cholqr(L.Vb, D, 102u);  // a replaced column is orthonormalised by a second pass
+  } else if (cholqr(L.Vb, L.Vb, D, 101u, false)) {
+    cholqr(L.Vb, L.Vb, D, 102u, false);  // a replaced column is orthonormalised by a second pass
   }
-  // sign: largest-magnitude entry positive (lowest index on ties)
-  for (int rho = wave; rho < r; rho += 4) {
-    float best = -1.f;
+  // sign: largest-magnitude entry positive (lowest index on ties). Wave 0:
+  // lane (q, c) = (lane >> 4, lane & 15) scans rows q, q + 4, ... of column
+  // c, the four quarters of a column (lanes c, c + 16, c + 32, c + 48) are
+  // combined, and each lane flips its own rows.
+  if (wave == 0) {
+    float vq[D / 4];
+#pragma unroll
+    for (int k = 0; k < D / 4; ++k) vq[k] = L.Vb[lg + 4 * k][ln];
+    float best = -1.f, bv = 1.f;
     int arg = D;
-    for (int row = lane; row < D; row += 64) {
-      const float m = fabsf(L.Vb[row][rho]);
-      if (m > best) { best = m; arg = row; }
+#pragma unroll
+    for (int k = 0; k < D / 4; ++k) {
+      const bool gt = fabsf(vq[k]) > best;
+      best = gt ? fabsf(vq[k]) : best;
+      arg = gt ? lg + 4 * k : arg;
+      bv = gt ? vq[k] : bv;
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ob = __shfl_xor(best, o, 64);
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+      const float ob = __shfl_xor(best, o, 64), ov = __shfl_xor(bv, o, 64);
       const int oa = __shfl_xor(arg, o, 64);
-      if (ob > best || (ob == best && oa < arg)) { best = ob; arg = oa; }
+      if (ob > best || (ob == best && oa < arg)) { best = ob; arg = oa; bv = ov; }
     }
-    if (arg >= D) arg = 0;  // only when every entry is NaN
-    const float sg = L.Vb[arg][rho] < 0.f ? -1.f : 1.f;
-    wave_lds_sync();
-    for (int row = lane; row < D; row += 64) L.Vb[row][rho] *= sg;
+    // (every entry NaN: no argument, the sign stays)
+    if (ln < r && bv < 0.f) {
+#pragma unroll
+      for (int k = 0; k < D / 4; ++k) L.Vb[lg + 4 * k][ln] = -vq[k];
+    }
   }
   __syncthreads();
 
