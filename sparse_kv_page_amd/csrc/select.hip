@@ -32,8 +32,11 @@ constexpr int kSelLdsKeys = 16384;  // sigma keys kept in LDS up to this many pa
 // query heads per KV head
 template <int NT, int NPT, int GQ>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
-  __shared__ SelectLds<NT, kSelLdsKeys> lds;
-  select_unit<NT, NPT, kSelLdsKeys, GQ>(a, blockIdx.y, blockIdx.x, lds);
+  // the register path keeps its keys in registers and needs the bitmap only
+  constexpr int kKeys = NPT > 0 ? 1 : kSelLdsKeys;
+  constexpr int kBits = NPT > 0 ? (NT * NPT + 31) / 32 : 1;
+  __shared__ SelectLds<NT, kKeys, kBits> lds;
+  select_unit<NT, NPT, kKeys, GQ, kBits>(a, blockIdx.y, blockIdx.x, lds);
 }
 
 namespace {

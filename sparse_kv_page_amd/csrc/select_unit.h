@@ -77,9 +77,10 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& tot) {
 
 }  // namespace sel_detail
 
-template <int NT, int KEYS>
+template <int NT, int KEYS, int BITS = 1>
 struct alignas(16) SelectLds {
   uint32_t keys[KEYS];
+  uint32_t bits[BITS];  // chosen-page bitmap of the register path (BITS words)
   uint32_t hist[2][kSelBins];
   float red_m[NT / 64][8];
   float red_s[NT / 64][8];
@@ -93,8 +94,8 @@ struct alignas(16) SelectLds {
 // straight-line code). NPT > 0 keeps pages tid, tid + NT, ... (NPT of them,
 // max_pages <= NT * NPT) in registers; NPT = 0 loops over global memory.
 // KEYS: page keys kept in LDS (longer contexts keep them in the sigma buffer).
-template <int NT, int NPT, int KEYS, int GQ>
-__device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, SelectLds<NT, KEYS>& L) {
+template <int NT, int NPT, int KEYS, int GQ, int BITS>
+__device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, SelectLds<NT, KEYS, BITS>& L) {
   using namespace sel_detail;
   constexpr int kSelThreads = NT;
   constexpr int kSelWaves = NT / 64;
@@ -116,14 +117,29 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   const float* srow = a.scores + ((int64_t)b * a.Hkv * G + (int64_t)h * G) * a.max_pages;
   // the register path loads its scores before the length is known (pages up
   // to max_pages are addressable), so both loads are in flight together
+  // (register page i of thread t is page 4 (t + NT (i / 4)) + i % 4: runs of
+  // four pages, read with 16-byte loads when rows are 16-byte aligned)
   constexpr int kRegs = NPT > 0 ? NPT : 1;
+  static_assert(NPT % 4 == 0, "register pages come in runs of four");
+  auto page_of = [&](int i) { return 4 * (tid + kSelThreads * (i >> 2)) + (i & 3); };
   float sc[kRegs][GQ];
   if constexpr (NPT > 0) {
+    const bool vec = (a.max_pages & 3) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int j = tid + kSelThreads * i;
+    for (int i4 = 0; i4 < NPT / 4; ++i4) {
+      const int j0 = page_of(4 * i4);
 #pragma unroll
-      for (int g = 0; g < GQ; ++g) sc[i][g] = (g < G && j < a.max_pages) ? srow[(int64_t)g * a.max_pages + j] : 0.f;
+      for (int g = 0; g < GQ; ++g) {
+        if (g < G && vec && j0 < a.max_pages) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(srow + (int64_t)g * a.max_pages + j0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[4 * i4 + e][g] = v[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sc[4 * i4 + e][g] = (g < G && j0 + e < a.max_pages) ? srow[(int64_t)g * a.max_pages + j0 + e] : 0.f;
+        }
+      }
     }
   }
   const int T = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.max_pages, P));
@@ -142,6 +158,10 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   uint32_t* keys = keys_in_lds ? keys_lds : reinterpret_cast<uint32_t*>(sig_row);
   auto is_cand = [&](int j) { return j >= 1 && j < Jc && j != J - 1; };
   for (int x = tid; x < kSelBins; x += kSelThreads) hist[0][x] = 0;
+  if constexpr (NPT > 0) {
+    static_assert(BITS * 32 >= NT * NPT, "bitmap covers the register pages");
+    for (int x = tid; x < BITS; x += kSelThreads) L.bits[x] = 0;
+  }
 
   // ---- per-head normaliser log Z_g: block max, then block sum of
   // 2^(s - max); each reduction is DPP inside the waves, one LDS exchange and
@@ -152,7 +172,7 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   if constexpr (NPT > 0) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int j = tid + kSelThreads * i;
+      const int j = page_of(i);
 #pragma unroll
       for (int g = 0; g < GQ; ++g) {
         if (!(g < G && j < Jc)) sc[i][g] = -INFINITY;
@@ -185,12 +205,19 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   float sm[GQ];
 #pragma unroll
   for (int g = 0; g < GQ; ++g) sm[g] = 0.f;
+  // the register path keeps ex[i][g] = exp(s_g(j) - max_g) for sigma
+  float ex[kRegs][GQ];
   if constexpr (NPT > 0) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i)
 #pragma unroll
-      for (int g = 0; g < GQ; ++g)
-        if (g < G && mx[g] > -INFINITY) sm[g] += exp2_fast((sc[i][g] - mx[g]) * kLog2e);
+      for (int g = 0; g < GQ; ++g) {
+        ex[i][g] = 0.f;
+        if (g < G && mx[g] > -INFINITY) {
+          ex[i][g] = exp2_fast((sc[i][g] - mx[g]) * kLog2e);
+          sm[g] += ex[i][g];
+        }
+      }
   } else {
     for (int j = tid; j < Jc; j += kSelThreads)
 #pragma unroll
@@ -205,15 +232,17 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     }
   }
   __syncthreads();
-  float lz[GQ];
+  float lz[GQ], inv_z[GQ];  // log Z_g, and 1 / sum_j exp(s_g(j) - max_g)
 #pragma unroll
   for (int g = 0; g < GQ; ++g) {
     lz[g] = -INFINITY;
+    inv_z[g] = 0.f;
     if (g < G && mx[g] > -INFINITY) {
       float r = red_s[0][g];
 #pragma unroll
       for (int w = 1; w < kSelWaves; ++w) r += red_s[w][g];
       lz[g] = mx[g] + log2_fast(r) * kLn2;
+      inv_z[g] = 1.f / r;
     }
   }
 
@@ -248,11 +277,49 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
       kmin = key < kmin ? key : kmin;
     }
   };
+  // register path: sigma_j = log(sum_g exp(s_g(j) - max_g) / Z'_g) - log G
+  // from the kept exponentials (one logarithm per page); a page whose sum
+  // falls below 2^-60 (terms near or below the fp32 range) takes the
+  // per-page-max form above on its scores read again. The key stays in a
+  // register.
+  uint32_t kreg[kRegs];
   if constexpr (NPT > 0) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int j = tid + kSelThreads * i;
-      if (j < Jc) sigma_key(j, sc[i]);
+      const int j = page_of(i);
+      kreg[i] = 0u;
+      if (j < Jc) {
+        float v = 0.f;
+#pragma unroll
+        for (int g = 0; g < GQ; ++g) v = fmaf(ex[i][g], inv_z[g], v);
+        float sigma;
+        if (v >= 0x1p-60f) {
+          sigma = (log2_fast(v) - log2G) * kLn2;
+        } else {
+          float tg[GQ];
+          float m = -INFINITY;
+#pragma unroll
+          for (int g = 0; g < GQ; ++g) {
+            tg[g] = -INFINITY;
+            if (g < G && lz[g] > -INFINITY) {
+              tg[g] = (srow[(int64_t)g * a.max_pages + j] - lz[g]) * kLog2e;  // (rare: reread)
+              m = fmaxf(m, tg[g]);
+            }
+          }
+          float su = 0.f;
+#pragma unroll
+          for (int g = 0; g < GQ; ++g)
+            if (g < G && m > -INFINITY) su += exp2_fast(tg[g] - m);
+          sigma = m > -INFINITY ? (m + log2_fast(su) - log2G) * kLn2 : -INFINITY;
+        }
+        const uint32_t key = float_key(sigma);
+        kreg[i] = key;
+        sig_row[j] = sigma;
+        if (is_cand(j)) {
+          kmax = key > kmax ? key : kmax;
+          kmin = key < kmin ? key : kmin;
+        }
+      }
     }
   } else {
     for (int j = tid; j < Jc; j += kSelThreads) {
@@ -294,11 +361,22 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     const int lo = hi > kSelDigit ? hi - kSelDigit : 0;
     const uint32_t dmask = (1u << (hi - lo)) - 1u;
     uint32_t* hc = hist[cur];
-    for (int j = tid; j < Jc; j += kSelThreads) {
-      if (!is_cand(j)) continue;
-      const uint64_t kv = key64(j);
-      if ((kv >> hi) != (prefix >> hi)) continue;
-      atomicAdd(&hc[(uint32_t)(kv >> lo) & dmask], 1u);
+    if constexpr (NPT > 0) {
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const int j = page_of(i);
+        if (j >= Jc || !is_cand(j)) continue;
+        const uint64_t kv = ((uint64_t)kreg[i] << idb) | (idmask - (uint64_t)j);
+        if ((kv >> hi) != (prefix >> hi)) continue;
+        atomicAdd(&hc[(uint32_t)(kv >> lo) & dmask], 1u);
+      }
+    } else {
+      for (int j = tid; j < Jc; j += kSelThreads) {
+        if (!is_cand(j)) continue;
+        const uint64_t kv = key64(j);
+        if ((kv >> hi) != (prefix >> hi)) continue;
+        atomicAdd(&hc[(uint32_t)(kv >> lo) & dmask], 1u);
+      }
     }
     __syncthreads();
     // bins in descending order, kPer per thread; the next pass's buffer is
@@ -344,6 +422,35 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     if (take_all) return true;
     return (key64(j) >> hi) >= (prefix >> hi);
   };
+  if constexpr (NPT > 0) {
+    // chosen pages set bits of an LDS bitmap; thread t then takes bits
+    // NPT t .. NPT t + NPT - 1 (one word holds them), and a block scan of the
+    // counts gives every thread its output positions (ascending ids)
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int j = page_of(i);
+      if (j >= J) continue;
+      bool c = j == 0 || j == J - 1;
+      if (!c && is_cand(j) && K != 0)
+        c = take_all || ((((uint64_t)kreg[i] << idb) | (idmask - (uint64_t)j)) >> hi) >= (prefix >> hi);
+      if (c) atomicOr(&L.bits[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    static_assert(32 % NPT == 0, "a thread's bits sit in one word");
+    const int b0 = NPT * tid;
+    const uint32_t mine = (L.bits[b0 >> 5] >> (b0 & 31)) & ((1u << NPT) - 1u);
+    int total;
+    int pos = block_excl_scan<kSelWaves>(__builtin_popcount(mine), wsum, total);
+#pragma unroll
+    for (int e = 0; e < NPT; ++e) {
+      if ((mine >> e) & 1u) {
+        if (pos < k) put(pos, b0 + e);
+        ++pos;
+      }
+    }
+    for (int t = total + tid; t < k; t += kSelThreads) put(t, -1);
+    return;
+  }
   const int ppt = (J + kSelThreads - 1) / kSelThreads;
   const int j0 = tid * ppt;
   const int j1 = min(J, j0 + ppt);
