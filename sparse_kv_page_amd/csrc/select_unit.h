@@ -82,11 +82,11 @@ struct alignas(16) SelectLds {
   uint32_t keys[KEYS];
   uint32_t bits[BITS];  // chosen-page bitmap of the register path (BITS words)
   uint32_t hist[2][kSelBins];
+  int pick_s[3];
   float red_m[NT / 64][8];
   float red_s[NT / 64][8];
   uint32_t redu[NT / 64][2];
   int wsum[NT / 64];
-  int pick_s[3];
 };
 
 // Combine and selection of the unit (b, h) by a workgroup of NT threads for
@@ -424,8 +424,8 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   };
   if constexpr (NPT > 0) {
     // chosen pages set bits of an LDS bitmap; thread t then takes bits
-    // NPT t .. NPT t + NPT - 1 (one word holds them), and a block scan of the
-    // counts gives every thread its output positions (ascending ids)
+    // NPT t .. NPT t + NPT - 1 (one word holds them) and writes them at the
+    // count of bits before them (ascending ids)
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int j = page_of(i);
@@ -437,10 +437,31 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     }
     __syncthreads();
     static_assert(32 % NPT == 0, "a thread's bits sit in one word");
+    // every wave counts the bits of all words (lane l takes words kWpl l ..)
+    // and prefix-sums them, so no block scan is needed
+    constexpr int kWpl = (BITS + 63) / 64;
+    int wex[kWpl];  // bits before each of the lane's words, within the lane
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < kWpl; ++u) {
+      const int x = lane * kWpl + u;
+      wex[u] = c;
+      c += x < BITS ? __builtin_popcount(L.bits[x]) : 0;
+    }
+    const int inc = wave_incl_scan(c);
+    const int total = __builtin_amdgcn_readlane(inc, 63);
     const int b0 = NPT * tid;
-    const uint32_t mine = (L.bits[b0 >> 5] >> (b0 & 31)) & ((1u << NPT) - 1u);
-    int total;
-    int pos = block_excl_scan<kSelWaves>(__builtin_popcount(mine), wsum, total);
+    const int wi = b0 >> 5;  // the word of this thread's bits, held by lane wi / kWpl
+    int wpre = 0;
+#pragma unroll
+    for (int u = 0; u < kWpl; ++u) {
+      const int v = __shfl(inc - c + wex[u], wi / kWpl, 64);
+      wpre = wi % kWpl == u ? v : wpre;
+    }
+    const uint32_t word = L.bits[wi];
+    const int off = b0 & 31;
+    const uint32_t mine = (word >> off) & ((1u << NPT) - 1u);
+    int pos = wpre + __builtin_popcount(word & ((1u << off) - 1u));
 #pragma unroll
     for (int e = 0; e < NPT; ++e) {
       if ((mine >> e) & 1u) {
