@@ -163,13 +163,17 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     for (int x = tid; x < BITS; x += kSelThreads) L.bits[x] = 0;
   }
 
-  // ---- per-head normaliser log Z_g: block max, then block sum of
-  // 2^(s - max); each reduction is DPP inside the waves, one LDS exchange and
-  // one barrier, with every thread combining the wave results itself ----
+  // ---- per-head normaliser log Z_g ----
   float mx[GQ];
 #pragma unroll
   for (int g = 0; g < GQ; ++g) mx[g] = -INFINITY;
+  float lz[GQ], inv_z[GQ];  // log Z_g, and the factor that turns a kept exponential into exp(s - log Z_g)
+  float ex[kRegs][GQ];      // register path: exp(s_g(j) - the wave's max_g), kept for sigma
   if constexpr (NPT > 0) {
+    // One barrier: every wave sums 2^(s - m_w) against its own maximum m_w
+    // (DPP inside the wave) and publishes (m_w, sum_w); then lane w of every
+    // row of 16 takes wave w's pair, and M = max m_w,
+    // Z = sum_w sum_w 2^(m_w - M) come from DPP over the row.
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int j = page_of(i);
@@ -179,70 +183,101 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
         mx[g] = fmaxf(mx[g], sc[i][g]);
       }
     }
-  } else {
-    for (int j = tid; j < Jc; j += kSelThreads)
+    float wm[GQ], sm[GQ];
 #pragma unroll
-      for (int g = 0; g < GQ; ++g)
-        if (g < G) mx[g] = fmaxf(mx[g], srow[(int64_t)g * a.max_pages + j]);
-  }
-#pragma unroll
-  for (int g = 0; g < GQ; ++g) {
-    if (g < G) {
-      const float r = wave_max(mx[g]);
-      if (lane == 0) red_m[wave][g] = r;
+    for (int g = 0; g < GQ; ++g) {
+      wm[g] = g < G ? wave_max(mx[g]) : -INFINITY;
+      sm[g] = 0.f;
     }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < GQ; ++g) {
-    if (g < G) {
-      float r = red_m[0][g];
-#pragma unroll
-      for (int w = 1; w < kSelWaves; ++w) r = fmaxf(r, red_m[w][g]);
-      mx[g] = r;
-    }
-  }
-  float sm[GQ];
-#pragma unroll
-  for (int g = 0; g < GQ; ++g) sm[g] = 0.f;
-  // the register path keeps ex[i][g] = exp(s_g(j) - max_g) for sigma
-  float ex[kRegs][GQ];
-  if constexpr (NPT > 0) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i)
 #pragma unroll
       for (int g = 0; g < GQ; ++g) {
         ex[i][g] = 0.f;
-        if (g < G && mx[g] > -INFINITY) {
-          ex[i][g] = exp2_fast((sc[i][g] - mx[g]) * kLog2e);
+        if (g < G && wm[g] > -INFINITY) {
+          ex[i][g] = exp2_fast((sc[i][g] - wm[g]) * kLog2e);
           sm[g] += ex[i][g];
         }
       }
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      if (g < G) {
+        const float r = wave_sum(sm[g]);
+        if (lane == 0) {
+          red_m[wave][g] = wm[g];
+          red_s[wave][g] = r;
+        }
+      }
+    }
+    __syncthreads();
+    static_assert(kSelWaves <= 16, "one row of lanes per wave pair");
+    const int wv = lane & 15;
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      lz[g] = -INFINITY;
+      inv_z[g] = 0.f;
+      if (g < G) {
+        const float m_w = wv < kSelWaves ? red_m[wv][g] : -INFINITY;
+        const float s_w = wv < kSelWaves ? red_s[wv][g] : 0.f;
+        const float M = group_max<16>(m_w);
+        const float z = group_sum<16>(m_w > -INFINITY ? s_w * exp2_fast((m_w - M) * kLog2e) : 0.f);
+        mx[g] = M;
+        if (M > -INFINITY) {
+          lz[g] = M + log2_fast(z) * kLn2;
+          inv_z[g] = wm[g] > -INFINITY ? exp2_fast((wm[g] - M) * kLog2e) / z : 0.f;
+        }
+      }
+    }
   } else {
+    // block max, then block sum of 2^(s - max); each reduction is DPP
+    // inside the waves, one LDS exchange and one barrier, with every thread
+    // combining the wave results itself
+    for (int j = tid; j < Jc; j += kSelThreads)
+#pragma unroll
+      for (int g = 0; g < GQ; ++g)
+        if (g < G) mx[g] = fmaxf(mx[g], srow[(int64_t)g * a.max_pages + j]);
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      if (g < G) {
+        const float r = wave_max(mx[g]);
+        if (lane == 0) red_m[wave][g] = r;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      if (g < G) {
+        float r = red_m[0][g];
+#pragma unroll
+        for (int w = 1; w < kSelWaves; ++w) r = fmaxf(r, red_m[w][g]);
+        mx[g] = r;
+      }
+    }
+    float sm[GQ];
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) sm[g] = 0.f;
     for (int j = tid; j < Jc; j += kSelThreads)
 #pragma unroll
       for (int g = 0; g < GQ; ++g)
         if (g < G && mx[g] > -INFINITY) sm[g] += exp2_fast((srow[(int64_t)g * a.max_pages + j] - mx[g]) * kLog2e);
-  }
 #pragma unroll
-  for (int g = 0; g < GQ; ++g) {
-    if (g < G) {
-      const float r = wave_sum(sm[g]);
-      if (lane == 0) red_s[wave][g] = r;
+    for (int g = 0; g < GQ; ++g) {
+      if (g < G) {
+        const float r = wave_sum(sm[g]);
+        if (lane == 0) red_s[wave][g] = r;
+      }
     }
-  }
-  __syncthreads();
-  float lz[GQ], inv_z[GQ];  // log Z_g, and 1 / sum_j exp(s_g(j) - max_g)
+    __syncthreads();
 #pragma unroll
-  for (int g = 0; g < GQ; ++g) {
-    lz[g] = -INFINITY;
-    inv_z[g] = 0.f;
-    if (g < G && mx[g] > -INFINITY) {
-      float r = red_s[0][g];
+    for (int g = 0; g < GQ; ++g) {
+      lz[g] = -INFINITY;
+      inv_z[g] = 0.f;
+      if (g < G && mx[g] > -INFINITY) {
+        float r = red_s[0][g];
 #pragma unroll
-      for (int w = 1; w < kSelWaves; ++w) r += red_s[w][g];
-      lz[g] = mx[g] + log2_fast(r) * kLn2;
-      inv_z[g] = 1.f / r;
+        for (int w = 1; w < kSelWaves; ++w) r += red_s[w][g];
+        lz[g] = mx[g] + log2_fast(r) * kLn2;
+      }
     }
   }
 
@@ -277,11 +312,11 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
       kmin = key < kmin ? key : kmin;
     }
   };
-  // register path: sigma_j = log(sum_g exp(s_g(j) - max_g) / Z'_g) - log G
-  // from the kept exponentials (one logarithm per page); a page whose sum
-  // falls below 2^-60 (terms near or below the fp32 range) takes the
-  // per-page-max form above on its scores read again. The key stays in a
-  // register.
+  // register path: sigma_j = log(sum_g e_g(j) f_g) - log G from the kept
+  // exponentials e_g(j) = exp(s_g(j) - m_w,g) and f_g = exp(m_w,g - log Z_g)
+  // (one logarithm per page); a page whose sum falls below 2^-60 (terms near
+  // or below the fp32 range) takes the per-page-max form above on its scores
+  // read again. The key stays in a register.
   uint32_t kreg[kRegs];
   if constexpr (NPT > 0) {
 #pragma unroll
