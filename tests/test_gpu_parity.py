@@ -121,6 +121,45 @@ def test_select_long_context_paths(G, lens):
     assert ndiff <= 2 * wl.batch * wl.num_kv_heads
 
 
+@pytest.mark.parametrize("G,lens", [(4, (64 * 2000 + 9, 64 * 1500)), (8, (64 * 1800, 64 * 900 + 3)),
+                                     (4, (64 * 7000 + 5, 64 * 5000))],
+                         ids=["g4_2000_pages", "g8_1800_pages", "g4_7000_pages"])
+def test_select_wide_score_spread(G, lens):
+    """Pages whose scores sit 100-250 below the head maxima in every head: the
+    register paths form sigma from exponentials kept against each wave's
+    maximum, and take the per-page-max form where those underflow. Sequence 0
+    has a third of its pages that far down (their sigma only is checked);
+    sequence 1 keeps 10 pages near the top, so most of its k - 2 slots go to
+    pages ranked by the per-page-max form. Sigma and selections against the
+    oracle."""
+    wl = synth.Workload("sel_spread", len(lens), 2, G, 128, 64, lens, 4, 32, "bf16", "bf16")
+    cfg = _cfg(wl)
+    gen = torch.Generator().manual_seed(71 + G)
+    hs = (torch.randn((wl.batch, wl.num_q_heads, wl.max_pages), generator=gen) * 2.5).float()
+    low = torch.rand((wl.batch, wl.max_pages), generator=gen)
+    drop = 100.0 + 150.0 * torch.rand((wl.batch, wl.max_pages), generator=gen)
+    down0 = low[0] < 1.0 / 3.0
+    down1 = torch.ones(wl.max_pages, dtype=torch.bool)
+    down1[torch.randperm(wl.max_pages, generator=gen)[:10]] = False
+    for b, down in ((0, down0), (1, down1)):
+        hs[b, :, down] -= drop[b, down]
+    g = {"seq_lens": torch.tensor(list(lens), dtype=torch.int32, device=gg.DEV)}
+    sel, sig = gg.gpu_select(wl, cfg, g, hs.to(gg.DEV))
+    torch.cuda.synchronize()
+    sel, sig = sel.cpu(), sig.cpu()
+    ndiff = 0
+    for b in range(wl.batch):
+        _, J, Jc = gg.lens(wl, b)
+        for h in range(wl.num_kv_heads):
+            s32 = hs[b, h * G:(h + 1) * G, :Jc].double().numpy()
+            sel_o, sigma_o = gg.oracle_unit_select(wl, b, s32)
+            ndiff += gg.check_selection(wl, b, sel[b, h].tolist(), sel_o.tolist(), sigma_o)
+            assert sigma_o is not None
+            assert gg.mixed_violation(gg.f64(sig[b, h, :Jc]), sigma_o) <= 1.0
+            assert np.isfinite(gg.f64(sig[b, h, :Jc])).all()
+    assert ndiff <= 2 * wl.batch * wl.num_kv_heads
+
+
 def test_select_ties_go_to_lower_page():
     """Equal keys: the lower page id wins (radix select resolves full 64-bit keys)."""
     wl = E2E.with_(batch=1, seq_lens=(64 * 40,), budget_pages=6)
