@@ -16,7 +16,7 @@
 //   key(j) = (order-preserving image of sigma_j) << idbits | (2^idbits - 1 - j)
 // which is unique and orders by (sigma desc, id asc). The bits above the
 // highest bit in which two candidates differ are common and skipped; the rest
-// is radix-selected with 11-bit digits (2048-bin LDS histogram, most
+// is radix-selected with 10-bit digits (1024-bin LDS histogram, most
 // significant digit first), stopping as soon as the bin holding the K-th key
 // is taken whole. The chosen pages are written in ascending order by a
 // block-wide scan over page flags.

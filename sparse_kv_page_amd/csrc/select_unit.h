@@ -7,8 +7,8 @@
 
 namespace locks {
 
-constexpr int kSelBins = 2048;
-constexpr int kSelDigit = 11;
+constexpr int kSelBins = 1024;
+constexpr int kSelDigit = 10;
 
 namespace sel_detail {
 
@@ -416,6 +416,7 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     __syncthreads();
     // bins in descending order, kPer per thread; the next pass's buffer is
     // cleared meanwhile
+    static_assert(kSelBins % kSelThreads == 0, "every thread scans the same number of bins");
     constexpr int kPer = kSelBins / kSelThreads;
     const int top = kSelBins - 1 - tid * kPer;
     int local = 0;
