@@ -25,6 +25,7 @@ struct SelectArgs {
   const int32_t* seq_lens;    // [B]
   int32_t* selected;          // [B][Hkv][k]
   float* sigma;               // [B][Hkv][max_pages]
+  int want_sigma;             // 0: sigma is scratch only (not left as an output)
   int Hkv, G, P, k, max_pages;
   int idbits;                 // bits that hold any page id < max_pages (>= 1)
 };

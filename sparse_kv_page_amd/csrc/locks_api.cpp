@@ -380,6 +380,7 @@ int locks_select_pages(const locks_config_t* cfg, const float* head_scores, cons
   if (batch == 0) return LOCKS_OK;
   if (!head_scores || !seq_lens || !selected || !page_sigma) return LOCKS_E_INVALID_ARG;
   locks::SelectArgs a = select_args(cfg, head_scores, seq_lens, max_pages, selected, page_sigma);
+  a.want_sigma = 1;
   return hip_status(locks::launch_select(a, batch, stream));
 }
 

@@ -32,9 +32,10 @@ constexpr int kSelLdsKeys = 16384;  // sigma keys kept in LDS up to this many pa
 // query heads per KV head
 template <int NT, int NPT, int GQ>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
-  // the register path keeps its keys in registers and needs the bitmap only
+  // the register path keeps its keys in registers; with eight pages per
+  // thread (not consecutive) its output goes through an LDS bitmap
   constexpr int kKeys = NPT > 0 ? 1 : kSelLdsKeys;
-  constexpr int kBits = NPT > 0 ? (NT * NPT + 31) / 32 : 1;
+  constexpr int kBits = NPT > 4 ? (NT * NPT + 31) / 32 : 1;
   __shared__ SelectLds<NT, kKeys, kBits> lds;
   select_unit<NT, NPT, kKeys, GQ, kBits>(a, blockIdx.y, blockIdx.x, lds);
 }

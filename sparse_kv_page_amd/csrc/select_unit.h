@@ -158,7 +158,7 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   uint32_t* keys = keys_in_lds ? keys_lds : reinterpret_cast<uint32_t*>(sig_row);
   auto is_cand = [&](int j) { return j >= 1 && j < Jc && j != J - 1; };
   for (int x = tid; x < kSelBins; x += kSelThreads) hist[0][x] = 0;
-  if constexpr (NPT > 0) {
+  if constexpr (NPT > 4) {
     static_assert(BITS * 32 >= NT * NPT, "bitmap covers the register pages");
     for (int x = tid; x < BITS; x += kSelThreads) L.bits[x] = 0;
   }
@@ -303,7 +303,7 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     const uint32_t key = float_key(sigma);
     if (keys_in_lds) {
       keys[j] = key;
-      sig_row[j] = sigma;
+      if (a.want_sigma) sig_row[j] = sigma;
     } else {
       sig_row[j] = __uint_as_float(key);  // global scratch holds the key; rewritten below
     }
@@ -349,7 +349,7 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
         }
         const uint32_t key = float_key(sigma);
         kreg[i] = key;
-        sig_row[j] = sigma;
+        if (a.want_sigma) sig_row[j] = sigma;
         if (is_cand(j)) {
           kmax = key > kmax ? key : kmax;
           kmin = key < kmin ? key : kmin;
@@ -458,6 +458,36 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     if (take_all) return true;
     return (key64(j) >> hi) >= (prefix >> hi);
   };
+  static_assert(NPT == 0 || NPT == 4 || NPT == 8, "register pages: 4 or 8 per thread");
+  if constexpr (NPT == 4) {
+    // the thread's register pages are 4 tid .. 4 tid + 3: their chosen flags,
+    // a block scan of the counts, and the writes at ascending positions
+    bool cf[4];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = page_of(i);
+      bool c = false;
+      if (j < J) {
+        c = j == 0 || j == J - 1;
+        if (!c && is_cand(j) && K != 0)
+          c = take_all || ((((uint64_t)kreg[i] << idb) | (idmask - (uint64_t)j)) >> hi) >= (prefix >> hi);
+      }
+      cf[i] = c;
+      cnt += c ? 1 : 0;
+    }
+    int total;
+    int pos = block_excl_scan<kSelWaves>(cnt, wsum, total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (cf[i]) {
+        if (pos < k) put(pos, page_of(i));
+        ++pos;
+      }
+    }
+    for (int t = total + tid; t < k; t += kSelThreads) put(t, -1);
+    return;
+  }
   if constexpr (NPT > 0) {
     // chosen pages set bits of an LDS bitmap; thread t then takes bits
     // NPT t .. NPT t + NPT - 1 (one word holds them) and writes them at the
@@ -524,7 +554,7 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   for (int t = total + tid; t < k; t += kSelThreads) put(t, -1);
 
   // when the keys lived in the global scratch, leave sigma there as documented
-  if (!keys_in_lds) {
+  if (!keys_in_lds && a.want_sigma) {
     __syncthreads();
     for (int j = tid; j < Jc; j += kSelThreads) {
       const uint32_t key = keys[j];
