@@ -210,11 +210,15 @@ def main():
         L.locks_decode_step(cfg, qsets[t % nq], pool, kp_dec, vp_dec, wl.num_blocks, bt, sl, B, maxp,
                             sel, out, lse, ws, ws_bytes)
 
+    # throttle counters: a sampled read over the whole measured part (taken
+    # before the warm-up and after the last timed window, so its ~100 ms of
+    # host time never precede a timed window) and a quick one per window
+    throttle = ThrottleMonitor()
+    region0 = throttle.read_sampled()
     for t in range(args.warmup):
         step(t)
         staged(t)
     torch.cuda.synchronize()
-    throttle = ThrottleMonitor()
 
     def windows(fn, n_steps, n_windows=3):
         """n_steps launches of fn in n_windows timed windows (HIP events on
@@ -269,6 +273,7 @@ def main():
         torch.cuda.synchronize()
         build_ms = b0.elapsed_time(b1) / args.steps
     stage_us["build_step"] = 1e3 * build_ms
+    throttle_region = throttle.delta(region0, throttle.read_sampled())
 
     summary_bytes, kv_bytes = algorithmic_bytes(wl, rec_bytes)
     step_bytes = summary_bytes + kv_bytes
@@ -320,7 +325,8 @@ def main():
         "windows": {"steps_per_window": win_sizes, "us_per_step": us,
                     "median_us": round(statistics.median(us), 3), "mean_us": round(statistics.mean(us), 3),
                     "sd_us": round(statistics.stdev(us), 3) if len(us) > 1 else 0.0,
-                    "throttle": step_thr, "unthrottled_mean_us": round(statistics.mean(ok), 3) if ok else None},
+                    "throttle": step_thr, "unthrottled_mean_us": round(statistics.mean(ok), 3) if ok else None,
+                    "throttle_whole_run": throttle_region},
         "measured_copy_GBps": copy,
         "roofline": roofline("page_score", wl, summary_bytes, stage_us["page_score"]),
         "sparse_decode_roofline": (roofline("sparse_decode", wl, kv_bytes, stage_us["sparse_decode"])
@@ -842,9 +848,17 @@ def selected_kv_footprint(wl, sels, bt):
 
 class ThrottleMonitor:
     """Reads the GPU's accumulated violation counters (thermal, power, VR,
-    HBM thermal) through amdsmi; a window is throttled when any of them grew
-    while it ran. Reports itself unavailable when amdsmi cannot reach the GPU."""
+    HBM thermal residency) from the amdsmi metrics table; a window is
+    throttled when any of them grew while it ran. Reports itself unavailable
+    when amdsmi cannot reach the GPU. The metrics table is read directly
+    (about 0.6 ms) rather than through the violation-status call, which
+    samples for about 100 ms: an idle GPU that long lowers its clocks, and the
+    next timed window started several percent slow."""
     KEYS = ("acc_prochot_thrm", "acc_ppt_pwr", "acc_socket_thrm", "acc_vr_thrm", "acc_hbm_thrm")
+    # metrics-table field of each key
+    FIELDS = {"acc_prochot_thrm": "prochot_residency_acc", "acc_ppt_pwr": "ppt_residency_acc",
+              "acc_socket_thrm": "socket_thm_residency_acc", "acc_vr_thrm": "vr_thm_residency_acc",
+              "acc_hbm_thrm": "hbm_thm_residency_acc", "acc_counter": "accumulation_counter"}
 
     def __init__(self):
         self.h = None
@@ -857,12 +871,27 @@ class ThrottleMonitor:
                 raise RuntimeError("no GPU handle")
             self.h = handles[0]
             self.smi = amdsmi
-            self.smi.amdsmi_get_violation_status(self.h)
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+            missing = [f for f in self.FIELDS.values() if f not in m]
+            if missing:
+                raise RuntimeError(f"metrics table lacks {missing}")
         except Exception as ex:  # noqa: BLE001 - monitoring only
             self.h = None
             self.err = f"{type(ex).__name__}: {ex}"[:200]
 
     def read(self):
+        if self.h is None:
+            return None
+        try:
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+            return {k: m.get(f) for k, f in self.FIELDS.items()}
+        except Exception as ex:  # noqa: BLE001
+            self.err = f"{type(ex).__name__}: {ex}"[:200]
+            return None
+
+    def read_sampled(self):
+        """The same counters through amdsmi's violation-status call (which
+        samples for about 100 ms); only outside timed windows."""
         if self.h is None:
             return None
         try:
