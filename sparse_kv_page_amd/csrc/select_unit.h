@@ -211,22 +211,29 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     }
     __syncthreads();
     static_assert(kSelWaves <= 16, "one row of lanes per wave pair");
+    // straight-line code (every lane loads a row, rows past the waves are
+    // masked), so the heads' dependent DPP chains interleave
     const int wv = lane & 15;
+    const bool wv_ok = wv < kSelWaves;
+    const int wvc = wv_ok ? wv : 0;
+    float m_w[GQ], e_w[GQ];
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
-      lz[g] = -INFINITY;
-      inv_z[g] = 0.f;
-      if (g < G) {
-        const float m_w = wv < kSelWaves ? red_m[wv][g] : -INFINITY;
-        const float s_w = wv < kSelWaves ? red_s[wv][g] : 0.f;
-        const float M = group_max<16>(m_w);
-        const float z = group_sum<16>(m_w > -INFINITY ? s_w * exp2_fast((m_w - M) * kLog2e) : 0.f);
-        mx[g] = M;
-        if (M > -INFINITY) {
-          lz[g] = M + log2_fast(z) * kLn2;
-          inv_z[g] = wm[g] > -INFINITY ? exp2_fast((wm[g] - M) * kLog2e) / z : 0.f;
-        }
-      }
+      const float m0 = red_m[wvc][g], s0 = red_s[wvc][g];
+      m_w[g] = wv_ok ? m0 : -INFINITY;
+      e_w[g] = wv_ok ? s0 : 0.f;
+    }
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) mx[g] = group_max<16>(m_w[g]);
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) e_w[g] = m_w[g] > -INFINITY ? e_w[g] * exp2_fast((m_w[g] - mx[g]) * kLog2e) : 0.f;
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      const float l2z = log2_fast(group_sum<16>(e_w[g]));
+      const bool live = mx[g] > -INFINITY;
+      lz[g] = live ? mx[g] + l2z * kLn2 : -INFINITY;
+      // exp(m_w,g - M) / Z as one exponential, 2^((m_w,g - M) log2 e - log2 Z)
+      inv_z[g] = live && wm[g] > -INFINITY ? exp2_fast((wm[g] - mx[g]) * kLog2e - l2z) : 0.f;
     }
   } else {
     // block max, then block sum of 2^(s - max); each reduction is DPP
@@ -319,42 +326,49 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   // read again. The key stays in a register.
   uint32_t kreg[kRegs];
   if constexpr (NPT > 0) {
+    float sg[kRegs], vs[kRegs];
+    bool low = false;
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int j = page_of(i);
-      kreg[i] = 0u;
-      if (j < Jc) {
-        float v = 0.f;
+      float v = 0.f;
 #pragma unroll
-        for (int g = 0; g < GQ; ++g) v = fmaf(ex[i][g], inv_z[g], v);
-        float sigma;
-        if (v >= 0x1p-60f) {
-          sigma = (log2_fast(v) - log2G) * kLn2;
-        } else {
+      for (int g = 0; g < GQ; ++g) v = fmaf(ex[i][g], inv_z[g], v);
+      vs[i] = v;
+      sg[i] = (log2_fast(v) - log2G) * kLn2;
+      low = low || (page_of(i) < Jc && !(v >= 0x1p-60f));
+    }
+    if (__ballot(low) != 0) {  // rare: some sum below 2^-60 in this wave
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const int j = page_of(i);
+        if (j < Jc && !(vs[i] >= 0x1p-60f)) {
           float tg[GQ];
           float m = -INFINITY;
 #pragma unroll
           for (int g = 0; g < GQ; ++g) {
             tg[g] = -INFINITY;
-            if (g < G && lz[g] > -INFINITY) {
-              tg[g] = (srow[(int64_t)g * a.max_pages + j] - lz[g]) * kLog2e;  // (rare: reread)
+            if (lz[g] > -INFINITY) {
+              tg[g] = (srow[(int64_t)g * a.max_pages + j] - lz[g]) * kLog2e;  // the scores read again
               m = fmaxf(m, tg[g]);
             }
           }
           float su = 0.f;
 #pragma unroll
           for (int g = 0; g < GQ; ++g)
-            if (g < G && m > -INFINITY) su += exp2_fast(tg[g] - m);
-          sigma = m > -INFINITY ? (m + log2_fast(su) - log2G) * kLn2 : -INFINITY;
-        }
-        const uint32_t key = float_key(sigma);
-        kreg[i] = key;
-        if (a.want_sigma) sig_row[j] = sigma;
-        if (is_cand(j)) {
-          kmax = key > kmax ? key : kmax;
-          kmin = key < kmin ? key : kmin;
+            if (m > -INFINITY) su += exp2_fast(tg[g] - m);
+          sg[i] = m > -INFINITY ? (m + log2_fast(su) - log2G) * kLn2 : -INFINITY;
         }
       }
+    }
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int j = page_of(i);
+      const uint32_t key = float_key(sg[i]);
+      kreg[i] = j < Jc ? key : 0u;
+      if (a.want_sigma && j < Jc) sig_row[j] = sg[i];
+      const bool cand = is_cand(j);
+      kmax = cand && key > kmax ? key : kmax;
+      kmin = cand && key < kmin ? key : kmin;
     }
   } else {
     for (int j = tid; j < Jc; j += kSelThreads) {
