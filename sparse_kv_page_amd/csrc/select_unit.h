@@ -156,7 +156,7 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   float* sig_row = a.sigma + ((int64_t)b * a.Hkv + h) * a.max_pages;
   const bool keys_in_lds = Jc <= kSelLdsKeys;
   uint32_t* keys = keys_in_lds ? keys_lds : reinterpret_cast<uint32_t*>(sig_row);
-  auto is_cand = [&](int j) { return j >= 1 && j < Jc && j != J - 1; };
+  auto is_cand = [&](int j) { return (j >= 1) & (j < Jc) & (j != J - 1); };
   for (int x = tid; x < kSelBins; x += kSelThreads) hist[0][x] = 0;
   if constexpr (NPT > 4) {
     static_assert(BITS * 32 >= NT * NPT, "bitmap covers the register pages");
@@ -389,6 +389,9 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
     kmax = redu[w][0] > kmax ? redu[w][0] : kmax;
     kmin = redu[w][1] < kmin ? redu[w][1] : kmin;
   }
+  // uniform (every lane read the same words): the radix bounds live in SGPRs
+  kmax = __builtin_amdgcn_readfirstlane(kmax);
+  kmin = __builtin_amdgcn_readfirstlane(kmin);
 
   // ---- radix select of the K best candidates ----
   int ncand = Jc - 1 - ((J - 1 >= 1 && J - 1 < Jc) ? 1 : 0);
@@ -455,9 +458,9 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
       }
     }
     __syncthreads();
-    const int dsel = pick_s[0];
-    const int need = pick_s[1];
-    const int cnt = pick_s[2];
+    const int dsel = __builtin_amdgcn_readfirstlane(pick_s[0]);
+    const int need = __builtin_amdgcn_readfirstlane(pick_s[1]);
+    const int cnt = __builtin_amdgcn_readfirstlane(pick_s[2]);
     prefix |= (uint64_t)dsel << lo;
     hi = lo;
     kr = need;
@@ -476,17 +479,17 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int b, int h, S
   if constexpr (NPT == 4) {
     // the thread's register pages are 4 tid .. 4 tid + 3: their chosen flags,
     // a block scan of the counts, and the writes at ascending positions
+    // (straight-line flags: every term is evaluated, none behind a branch)
     bool cf[4];
     int cnt = 0;
+    const uint64_t pfx = prefix >> hi;
+    const bool rank_any = K != 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = page_of(i);
-      bool c = false;
-      if (j < J) {
-        c = j == 0 || j == J - 1;
-        if (!c && is_cand(j) && K != 0)
-          c = take_all || ((((uint64_t)kreg[i] << idb) | (idmask - (uint64_t)j)) >> hi) >= (prefix >> hi);
-      }
+      const uint64_t kv = ((uint64_t)kreg[i] << idb) | (idmask - (uint64_t)j);
+      const bool ranked = take_all | ((kv >> hi) >= pfx);
+      const bool c = (j < J) & ((j == 0) | (j == J - 1) | (is_cand(j) & rank_any & ranked));
       cf[i] = c;
       cnt += c ? 1 : 0;
     }
