@@ -149,6 +149,7 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
     for (int s = 0; s < kSteps; ++s) cop[s] = nibbles_to_bf16(0u, nib_m, nib_b);
     a16 = M::product(cop, qb)[0];
   }
+  const f32x4_t a16_init = {-1.5f * a16, -1.5f * a16, -1.5f * a16, -1.5f * a16};
 
   auto bid_ok = [&](int bid) { return bid >= 0 && (int64_t)bid < a.num_blocks; };
   const uint8_t* pool = a.sum_pool + (int64_t)h * R::kBytes;
@@ -314,26 +315,27 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
         for (int s = 0; s < kSteps; ++s) av[p][s] = nibbles_to_bf16(w[s], nib_m, nib_b);
       }
     }
+    // Lane (n, kg) holds rows 4kg .. 4kg+3 of head n. The products start
+    // from -1.5 A16, so a basis row holds A' = A - 1.5 A16 = code . q; the
+    // lane scales its rows where they are (scales s_V[4kg .. 4kg+3], or s_mu
+    // at index RT, in one 8-byte read, issued before the products):
+    //   basis row rho < RT:   A' s_V[rho] * scale * log2(e)
+    //   row RT (centroid):    (16 A'_hi + A'_lo + 0.5 A16) s_mu * scale
+    //                         (= (16 A_hi + A_lo - 25 A16) s_mu * scale)
+    // then the G heads' rows go through LDS to the lanes that own the head.
+    u32x2_t sv[NPG];
+#pragma unroll
+    for (int p = 0; p < NPG; ++p) sv[p] = *reinterpret_cast<const u32x2_t*>(rec[p] + R::kScaleOff + 8 * kg);
     f32x4_t acc[NPG];
 #pragma unroll
-    for (int p = 0; p < NPG; ++p) acc[p] = M::product(av[p], qb);
-    // Lane (n, kg) holds rows 4kg .. 4kg+3 of head n; it scales them where
-    // they are (scales s_V[4kg .. 4kg+3], or s_mu at index RT, in one 8-byte
-    // read):
-    //   basis row rho < RT:   (A - 1.5 A16) s_V[rho] * scale * log2(e)
-    //   row RT (centroid):    (16 A_hi + A_lo - 25 A16) s_mu * scale
-    // then the G heads' rows go through LDS to the lanes that own the head.
+    for (int p = 0; p < NPG; ++p) acc[p] = M::product(av[p], qb, a16_init);
 #pragma unroll
     for (int p = 0; p < NPG; ++p) {
-      const u32x2_t sv = *reinterpret_cast<const u32x2_t*>(rec[p] + R::kScaleOff + 8 * kg);
       f32x4_t o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sz = ((i & 1) ? bf16_hi(sv[i >> 1]) : bf16_lo(sv[i >> 1])) * zscale;
-        o[i] = fmaf(acc[p][i], sz, -1.5f * a16 * sz);
-      }
-      const float smu = (kCi & 1) ? bf16_hi(sv[kCi >> 1]) : bf16_lo(sv[kCi >> 1]);
-      const float cent = (16.f * acc[p][kCi] + acc[p][kCi + 1] - 25.f * a16) * smu * a.scale;
+      for (int i = 0; i < 4; ++i) o[i] = acc[p][i] * (((i & 1) ? bf16_hi(sv[p][i >> 1]) : bf16_lo(sv[p][i >> 1])) * zscale);
+      const float smu = (kCi & 1) ? bf16_hi(sv[p][kCi >> 1]) : bf16_lo(sv[p][kCi >> 1]);
+      const float cent = (16.f * acc[p][kCi] + acc[p][kCi + 1] + 0.5f * a16) * smu * a.scale;
       if (kg == RT / 4) o[kCi] = cent;
       if (n < G) *reinterpret_cast<f32x4_t*>(&wbuf[wave][p][n][kg * 4]) = o;
     }

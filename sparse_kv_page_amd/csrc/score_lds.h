@@ -37,8 +37,7 @@ struct ScoreMfma<bf16_t, D> {
     for (int s = 0; s < kSteps; ++s)
       b[s] = ok ? *reinterpret_cast<const Op*>(qrow + s * 32 + kg * 8) : Op{0, 0, 0, 0, 0, 0, 0, 0};
   }
-  static __device__ __forceinline__ f32x4_t product(const Op* a, const Op* b) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  static __device__ __forceinline__ f32x4_t product(const Op* a, const Op* b, f32x4_t acc = {0.f, 0.f, 0.f, 0.f}) {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
     return acc;
