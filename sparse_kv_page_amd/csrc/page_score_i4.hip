@@ -163,7 +163,17 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   }
   // A operand: lane (n, kg) reads record row n (rows past the centroid's two
   // read row 0; their MFMA output rows are never used) at its k groups
-  const int arow = n < RT + 2 ? n : 0;
+  // Ranks 1, 2 and 4: a page has RT + 2 nibble rows (basis, centroid high
+  // and low), so the 16 rows of one product hold kPack pages (4 at ranks 1
+  // and 2, 2 at rank 4) instead of one, and the nibble decode (the bulk of
+  // the VALU work per record) is shared: lane (n, kg) decodes row n % kRows
+  // of the pack's page n / kRows. Rank 1 pads its 3 rows to 4 so that no
+  // centroid pair straddles two lanes; pad rows and rows past the last whole
+  // page decode row 0 (their output rows are never used).
+  constexpr int kRows = RT == 1 ? 4 : RT + 2;
+  constexpr int kPack = RT <= 4 ? 16 / kRows : 1;
+  const int a_pp = kPack > 1 ? n / kRows : 0;
+  const int arow = kPack > 1 ? (a_pp < kPack && n % kRows < RT + 2 ? n % kRows : 0) : (n < RT + 2 ? n : 0);
   int a_off;
   if constexpr (D == 128) a_off = (arow * R::kRowChunks + (kg ^ (arow % R::kRowChunks))) * 16;
   else a_off = (arow * R::kRowChunks + ((kg >> 1) ^ (arow % R::kRowChunks))) * 16 + (kg & 1) * 8;
@@ -294,6 +304,70 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
     }
   };
 
+  // Phase A with kPack pages per product: the lane's output rows 4 kg + i
+  // (i = 0..3) are row r % kRows of the pack's page r / kRows; basis rows are
+  // scaled as in the one-page form, a centroid pair (always rows i, i + 1 of
+  // one lane) gives the centroid term, and each value goes to its
+  // (page, head, row) slot of the LDS exchange.
+  int o_pr[4], o_lr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o_pr[i] = (4 * kg + i) / kRows;
+    o_lr[i] = (4 * kg + i) % kRows;
+  }
+  auto score_rows_packed = [&](auto npg_tag, const uint8_t* const* rec) {
+    constexpr int NPG = decltype(npg_tag)::value;
+    constexpr int NQ = (NPG + kPack - 1) / kPack;
+    // a centroid pair (rows RT, RT + 1 of a page) never straddles two lanes
+    static_assert(kPack == 1 || (kRows % 4 == 0 && RT % 4 <= 2) || (kRows % 2 == 0 && RT % 2 == 0),
+                  "centroid pairs inside one lane's four rows");
+    typename M::Op av[NQ][kSteps];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const uint8_t* ra = rec[q * kPack];
+#pragma unroll
+      for (int pp = 1; pp < kPack; ++pp)
+        if (q * kPack + pp < NPG && a_pp == pp) ra = rec[q * kPack + pp];
+      if constexpr (D == 128) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(ra + a_off);
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) av[q][st] = nibbles_to_bf16(w[st], nib_m, nib_b);
+      } else {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(ra + a_off);
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) av[q][st] = nibbles_to_bf16(w[st], nib_m, nib_b);
+      }
+    }
+    float sc[NQ][4];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint8_t* rr = rec[q * kPack];
+#pragma unroll
+        for (int pp = 1; pp < kPack; ++pp)
+          if (q * kPack + pp < NPG && o_pr[i] == pp) rr = rec[q * kPack + pp];
+        const int li = o_lr[i] < RT ? o_lr[i] : RT;
+        sc[q][i] = bf16_to_f32(*reinterpret_cast<const bf16_t*>(rr + R::kScaleOff + 2 * li));
+      }
+    f32x4_t acc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = M::product(av[q], qb, a16_init);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int page = q * kPack + o_pr[i];
+        const bool ok = n < G && o_pr[i] < kPack && page < NPG;
+        if (i < 3 && o_lr[i] == RT) {
+          const float cent = (16.f * acc[q][i] + acc[q][(i + 1) & 3] + 0.5f * a16) * sc[q][i] * a.scale;
+          if (ok) wbuf[wave][page][n][RT] = cent;
+        } else if (o_lr[i] < RT) {
+          if (ok) wbuf[wave][page][n][o_lr[i]] = acc[q][i] * (sc[q][i] * zscale);
+        }
+      }
+  };
+
   auto score_pages = [&](auto npg_tag, int t, int s0) {
     constexpr int NPG = decltype(npg_tag)::value;
     const uint8_t* rec[NPG];
@@ -302,6 +376,9 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
     for (int p = 1; p < NPG; ++p) rec[p] = &slots[wave][(s0 + p) % NS][0];
 
     // ---- A: code . q for the basis rows and the centroid's nibble rows ----
+    if constexpr (kPack > 1) {
+      score_rows_packed(std::integral_constant<int, NPG>{}, rec);
+    } else {
     typename M::Op av[NPG][kSteps];
 #pragma unroll
     for (int p = 0; p < NPG; ++p) {
@@ -338,6 +415,7 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
       const float cent = (16.f * acc[p][kCi] + acc[p][kCi + 1] + 0.5f * a16) * smu * a.scale;
       if (kg == RT / 4) o[kCi] = cent;
       if (n < G) *reinterpret_cast<f32x4_t*>(&wbuf[wave][p][n][kg * 4]) = o;
+    }
     }
     wave_lds_sync();
     if constexpr (kMfmaB) {
