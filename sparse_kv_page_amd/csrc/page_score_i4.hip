@@ -132,7 +132,6 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   // below assume only record loads are pending)
   wait_vm_const<0>();
   my_bid = __builtin_amdgcn_mov_dpp(my_bid, 0xE4, 0xf, 0xf, false);  // identity; orders the use after the wait
-  auto bid_at = [&](int t) { return __builtin_amdgcn_readlane(my_bid, t); };  // t wave-uniform, < 64
   const int g = lane / lph;
   const int u = lane - g * lph;
   const float zscale = a.scale * kLog2e;
@@ -154,6 +153,19 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   auto bid_ok = [&](int bid) { return bid >= 0 && (int64_t)bid < a.num_blocks; };
   const uint8_t* pool = a.sum_pool + (int64_t)h * R::kBytes;
   const int64_t blk_stride = (int64_t)a.Hkv * R::kBytes;
+  // per page of the wave (lane t holds page p0 + t): its record's byte offset
+  // (block 0 for an invalid id) and a validity mask, formed once on the VALU
+  // so that a page's load address is two lane reads
+  const bool my_ok = bid_ok(my_bid);
+  const uint64_t ok_mask = __ballot(my_ok);
+  const uint64_t my_off = (uint64_t)(my_ok ? my_bid : 0) * (uint64_t)blk_stride;
+  const uint32_t off_lo = (uint32_t)my_off, off_hi = (uint32_t)(my_off >> 32);
+  auto ok_at = [&](int t) { return ((ok_mask >> t) & 1u) != 0; };  // t wave-uniform, < 64
+  auto rec_at = [&](int t) {
+    const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)off_hi, t) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)off_lo, t);
+    return pool + o;
+  };
 
   int src_off[R::kInstr];
 #pragma unroll
@@ -179,8 +191,7 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   else a_off = (arow * R::kRowChunks + ((kg >> 1) ^ (arow % R::kRowChunks))) * 16 + (kg & 1) * 8;
 
   auto issue = [&](int t, int slot) {
-    const int bid = bid_at(t);
-    const uint8_t* rec = pool + (int64_t)(bid_ok(bid) ? bid : 0) * blk_stride;
+    const uint8_t* rec = rec_at(t);
     const uint32_t dst = lds_addr(&slots[wave][slot][0]);
 #pragma unroll
     for (int j = 0; j < R::kInstr; ++j) {
@@ -214,7 +225,7 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
     for (int p = 0; p < NPG; ++p) {
       if (p > 0 && kg == p) rec_k = rec[p];
       if (p > 0 && cp == p) rec_c = rec[p];
-      ok[p] = bid_ok(bid_at(t + p));
+      ok[p] = ok_at(t + p);
     }
     const bool col_ok = cp < NPG;
     const bool mine = col_ok && kg == cp;
@@ -353,18 +364,26 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
     f32x4_t acc[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) acc[q] = M::product(av[q], qb, a16_init);
+    // every lane stores every row (no branches): rows with no slot (other
+    // heads, centroid low and pad rows, pages past the pack) go to entry 15
+    // of page 0, head 0, which the exchange never reads (it holds at most
+    // RT + 1 <= 9 entries per head)
+    float* const dummy = &wbuf[wave][0][0][15];
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int page = q * kPack + o_pr[i];
-        const bool ok = n < G && o_pr[i] < kPack && page < NPG;
-        if (i < 3 && o_lr[i] == RT) {
-          const float cent = (16.f * acc[q][i] + acc[q][(i + 1) & 3] + 0.5f * a16) * sc[q][i] * a.scale;
-          if (ok) wbuf[wave][page][n][RT] = cent;
-        } else if (o_lr[i] < RT) {
-          if (ok) wbuf[wave][page][n][o_lr[i]] = acc[q][i] * (sc[q][i] * zscale);
-        }
+        const bool live = n < G && o_pr[i] < kPack && page < NPG;
+        const bool is_c = i < 3 && o_lr[i] == RT;
+        const float vb = acc[q][i] * (sc[q][i] * zscale);
+        const float vc = (16.f * acc[q][i] + acc[q][(i + 1) & 3] + 0.5f * a16) * sc[q][i] * a.scale;
+        const bool st = live && (is_c || o_lr[i] < RT);
+        const int pg = page < NPG ? page : 0;
+        const int hd = n < G ? n : 0;
+        const int ix = o_lr[i] < RT ? o_lr[i] : RT;
+        float* const dst = st ? &wbuf[wave][pg][hd][ix] : dummy;
+        *dst = is_c ? vc : vb;
       }
   };
 
@@ -491,9 +510,8 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
     if (u == 0) {
 #pragma unroll
       for (int p = 0; p < NPG; ++p) {
-        const int bid = bid_at(t + p);
         const float s = qmu[p] + (mx[p] + log2_fast(sm[p])) * kLn2;
-        sbuf[wave][t + p][g] = bid_ok(bid) ? s : -INFINITY;
+        sbuf[wave][t + p][g] = ok_at(t + p) ? s : -INFINITY;
       }
     }
     }
