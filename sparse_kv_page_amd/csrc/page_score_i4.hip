@@ -186,9 +186,19 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
   constexpr int kPack = RT <= 4 ? 16 / kRows : 1;
   const int a_pp = kPack > 1 ? n / kRows : 0;
   const int arow = kPack > 1 ? (a_pp < kPack && n % kRows < RT + 2 ? n % kRows : 0) : (n < RT + 2 ? n : 0);
-  int a_off;
-  if constexpr (D == 128) a_off = (arow * R::kRowChunks + (kg ^ (arow % R::kRowChunks))) * 16;
-  else a_off = (arow * R::kRowChunks + ((kg >> 1) ^ (arow % R::kRowChunks))) * 16 + (kg & 1) * 8;
+  auto row_off = [&](int row) {  // the lane's 16 (d = 128) or 8 (d = 64) bytes of nibble row `row`
+    if constexpr (D == 128) return (row * R::kRowChunks + (kg ^ (row % R::kRowChunks))) * 16;
+    else return (row * R::kRowChunks + ((kg >> 1) ^ (row % R::kRowChunks))) * 16 + (kg & 1) * 8;
+  };
+  const int a_off = row_off(arow);
+  // Rank 8 (ten rows a page) splits a page's rows over two products: the
+  // basis rows of two pages fill one product (lane row n: page n / 8, basis
+  // row n % 8) and the centroid rows of up to eight pages another (lane row
+  // n: page n / 2, centroid row RT + n % 2), three products for four pages
+  // instead of four, each row decoded once.
+  constexpr bool kSplit = RT == 8;
+  const int a_off_b = row_off(n & 7);
+  const int a_off_c = row_off(RT + (n & 1));
 
   auto issue = [&](int t, int slot) {
     const uint8_t* rec = rec_at(t);
@@ -387,6 +397,76 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
       }
   };
 
+  // Rank-8 split form. Basis product q: lane (n, kg) holds basis rows
+  // 4 (kg % 2) .. + 3 of page 2 q + kg / 2 for head n (scales in one 8-byte
+  // read); centroid product: rows 4 kg .. 4 kg + 3 are the (high, low) pairs
+  // of pages 2 kg and 2 kg + 1.
+  auto score_rows_split = [&](auto npg_tag, const uint8_t* const* rec) {
+    constexpr int NPG = decltype(npg_tag)::value;
+    constexpr int NB = (NPG + 1) / 2;
+    typename M::Op ab[NB][kSteps], ac[kSteps];
+    auto decode = [&](typename M::Op* dst, const uint8_t* src) {
+      if constexpr (D == 128) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src);
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) dst[st] = nibbles_to_bf16(w[st], nib_m, nib_b);
+      } else {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src);
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) dst[st] = nibbles_to_bf16(w[st], nib_m, nib_b);
+      }
+    };
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const uint8_t* ra = (2 * q + 1 < NPG && n >= 8) ? rec[2 * q + 1] : rec[2 * q];
+      decode(ab[q], ra + a_off_b);
+    }
+    {
+      const uint8_t* ra = rec[0];
+#pragma unroll
+      for (int p = 1; p < NPG; ++p)
+        if ((n >> 1) == p) ra = rec[p];
+      decode(ac, ra + a_off_c);
+    }
+    // scales: the basis product's page for this lane, and the centroid scale
+    // of the two pages whose rows the lane holds in the centroid product
+    u32x2_t sb[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const uint8_t* rs = (2 * q + 1 < NPG && kg >= 2) ? rec[2 * q + 1] : rec[2 * q];
+      sb[q] = *reinterpret_cast<const u32x2_t*>(rs + R::kScaleOff + 8 * (kg & 1));
+    }
+    float smu[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint8_t* rs = rec[0];
+#pragma unroll
+      for (int p = 1; p < NPG; ++p)
+        if (2 * kg + e == p) rs = rec[p];
+      smu[e] = bf16_to_f32(*reinterpret_cast<const bf16_t*>(rs + R::kScaleOff + 2 * RT));
+    }
+    f32x4_t accb[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) accb[q] = M::product(ab[q], qb, a16_init);
+    const f32x4_t accc = M::product(ac, qb, a16_init);
+    float* const dummy = &wbuf[wave][0][0][15];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int page = 2 * q + (kg >> 1);
+      f32x4_t o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = accb[q][i] * (((i & 1) ? bf16_hi(sb[q][i >> 1]) : bf16_lo(sb[q][i >> 1])) * zscale);
+      if (n < G && page < NPG) *reinterpret_cast<f32x4_t*>(&wbuf[wave][page][n][4 * (kg & 1)]) = o;
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int page = 2 * kg + e;
+      const float cent = (16.f * accc[2 * e] + accc[2 * e + 1] + 0.5f * a16) * smu[e] * a.scale;
+      float* const dst = (n < G && page < NPG) ? &wbuf[wave][page < NPG ? page : 0][n < G ? n : 0][RT] : dummy;
+      *dst = cent;
+    }
+  };
+
   auto score_pages = [&](auto npg_tag, int t, int s0) {
     constexpr int NPG = decltype(npg_tag)::value;
     const uint8_t* rec[NPG];
@@ -397,6 +477,8 @@ __device__ __forceinline__ void score_wave_i4(const ScoreArgs& a, int b, int h, 
     // ---- A: code . q for the basis rows and the centroid's nibble rows ----
     if constexpr (kPack > 1) {
       score_rows_packed(std::integral_constant<int, NPG>{}, rec);
+    } else if constexpr (kSplit) {
+      score_rows_split(std::integral_constant<int, NPG>{}, rec);
     } else {
     typename M::Op av[NPG][kSteps];
 #pragma unroll
