@@ -223,6 +223,34 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
   auto bid_ok = [&](int bid) { return bid >= 0 && (int64_t)bid < a.num_blocks; };
   const uint8_t* pool = a.sum_pool + (int64_t)h * R::kBytes;
   const int64_t blk_stride = (int64_t)a.Hkv * R::kBytes;
+  // Short records (small ranks): each page's record offset and validity are
+  // formed once per wave on the VALU (lane l holds pages l and 64 + l), so a
+  // page's load address is two lane reads. Long records keep the per-page
+  // scalar form: the extra registers slowed the rank-8 launch.
+  constexpr bool kLaneOffsets = R::kBytes <= 1024;
+  uint64_t off1 = 0, off2 = 0, okm1 = 0, okm2 = 0;
+  if constexpr (kLaneOffsets) {
+    const bool ok1 = bid_ok(my_bid), ok2 = bid_ok(my_bid2);
+    okm1 = __ballot(ok1);
+    okm2 = __ballot(ok2);
+    off1 = (uint64_t)(ok1 ? my_bid : 0) * (uint64_t)blk_stride;
+    off2 = (uint64_t)(ok2 ? my_bid2 : 0) * (uint64_t)blk_stride;
+  }
+  auto ok_at = [&](int t) {  // t wave-uniform
+    if constexpr (kLaneOffsets) return (((t < 64 ? okm1 : okm2) >> (t & 63)) & 1u) != 0;
+    else return bid_ok(bid_at(t));
+  };
+  auto rec_at = [&](int t) {
+    if constexpr (kLaneOffsets) {
+      const uint64_t o = t < 64 ? off1 : off2;
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)o, t & 63);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(o >> 32), t & 63);
+      return pool + (((uint64_t)hi << 32) | lo);
+    } else {
+      const int bid = bid_at(t);
+      return pool + (int64_t)(bid_ok(bid) ? bid : 0) * blk_stride;
+    }
+  };
 
   // per-lane DMA source offsets (swizzled) for each instruction of a record
   int src_off[R::kInstr];
@@ -241,8 +269,7 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
   }
 
   auto issue = [&](int t, int slot) {
-    const int bid = bid_at(t);
-    const uint8_t* rec = pool + (int64_t)(bid_ok(bid) ? bid : 0) * blk_stride;
+    const uint8_t* rec = rec_at(t);
     const uint32_t dst = lds_addr(&slots[wave][slot][0]);
 #pragma unroll
     for (int j = 0; j < R::kInstr; ++j) {
@@ -276,7 +303,7 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
 #pragma unroll
     for (int p = 0; p < NPG; ++p) {
       if (p > 0 && kg == p) rec_k = rec[p];
-      ok[p] = bid_ok(bid_at(t + p));
+      ok[p] = ok_at(t + p);
     }
     const bool col_ok = cp < NPG;
     const bool mine = col_ok && kg == cp;
@@ -430,9 +457,8 @@ __device__ __forceinline__ void score_wave_lds(const ScoreArgs& a, int b, int h,
     if (u == 0) {
 #pragma unroll
       for (int p = 0; p < NPG; ++p) {
-        const int bid = bid_at(t + p);
         const float sc = qmu[p] * a.scale + (mx[p] + log2_fast(sm[p])) * kLn2;
-        sbuf[wave][t + p][g] = bid_ok(bid) ? sc : -INFINITY;
+        sbuf[wave][t + p][g] = ok_at(t + p) ? sc : -INFINITY;
       }
     }
     }
